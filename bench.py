@@ -1,0 +1,322 @@
+#!/usr/bin/env python3
+"""Throughput of the MI355X scans on one GPU.
+
+A step is one pass of the whole hot path over one batch of synthetic input.
+The default workload is the k = 1 channel scan forward + backward at B=8,
+T=8192, D=4096 with bf16 storage and fp32 arithmetic (workload 3 of
+workloads.py): one linear_scan_fwd followed by one linear_scan_bwd that
+consumes the forward's A and Bc.  Inputs are resident in HBM before the
+timed region starts.
+
+Printed: one JSON line with the whole-job throughput (algorithmic bytes --
+every input read once and every output written once -- per second), the
+roofline of the dominant kernel (HIP events on the stream the kernels run on)
+and the fp64 CPU oracle timed on a bounded sample of the same workload.
+
+  python bench.py [--steps K] [--warmup W] [--workload {1..5}] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth
+METRIC = "scan GB/s and % HBM peak, linear_scan fwd+bwd B=8,T=8192,D=4096"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def source_digest() -> str:
+    """Hash of the kernel sources: stored counter readings are only valid for
+    the exact kernels they were taken on."""
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "linear_recurrence_scans_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode())
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+# ---------------------------------------------------------------------------
+# workloads
+# ---------------------------------------------------------------------------
+
+def build_workload(wid, torch, lrs, workloads):
+    """Returns (description dict, list of (kernel name, fn, algorithmic bytes), step fn)."""
+    w = workloads.WORKLOADS[wid]
+    log("generating inputs for workload", wid, w["name"])
+    t0 = time.time()
+    x = workloads.workload_inputs(wid)
+    dtype = torch.bfloat16 if w["dtype"] == "bf16" else torch.float32
+
+    def dev(a):
+        return torch.from_numpy(a).to(dtype).cuda()
+
+    d = {k: dev(v) for k, v in x.items()}
+    del x
+    log("inputs resident in HBM (%.1fs)" % (time.time() - t0))
+    es = 2 if dtype == torch.bfloat16 else 4
+    kernels = []
+    state = {}
+    if w["op"] == "linear":
+        Bn, T, D = w["B"], w["T"], w["D"]
+        N = Bn * T * D
+        ws = torch.empty(lrs.mi_linear_scan_workspace(Bn, T, D, dtype), dtype=torch.uint8, device="cuda")
+        state["A"] = torch.empty_like(d["a"])
+        state["Bc"] = torch.empty_like(d["a"])
+
+        def fwd():
+            lrs.mi_linear_scan_fwd(d["a"], d["b"], state["A"], state["Bc"], ws=ws)
+        kernels.append(("linear_scan_fwd", fwd, 4 * es * N))
+        if "gA" in d:
+            state["da"] = torch.empty_like(d["a"])
+            state["db"] = torch.empty_like(d["a"])
+
+            def bwd():
+                lrs.mi_linear_scan_bwd(d["a"], state["A"], state["Bc"], d["gA"], d["gBc"],
+                                       state["da"], state["db"], ws=ws)
+            kernels.append(("linear_scan_bwd", bwd, 7 * es * N))
+        desc = {"workload": "linear_scan %s k=1, B=%d, T=%d, D=%d, %s storage / fp32 arithmetic"
+                % ("fwd+bwd" if len(kernels) == 2 else "fwd", Bn, T, D, w["dtype"]),
+                "B": Bn, "T": T, "D": D, "storage": w["dtype"]}
+        units = N
+    elif w["op"] == "log":
+        Bn, T, D = w["B"], w["T"], w["D"]
+        N = Bn * T * D
+        ws = torch.empty(lrs.mi_scan_log_workspace(Bn, T, D, dtype), dtype=torch.uint8, device="cuda")
+        state["h"] = torch.empty_like(d["log_coeffs"])
+
+        def logf():
+            lrs.mi_scan_log_fwd(d["log_coeffs"], d["log_values"], state["h"], ws=ws)
+        kernels.append(("scan_log_fwd", logf, es * (3 * N + Bn * D)))
+        desc = {"workload": "parallel_scan_log_fwd, B=%d, T=%d, D=%d, fp32" % (Bn, T, D),
+                "B": Bn, "T": T, "D": D, "storage": w["dtype"]}
+        units = N
+    else:
+        Bn, T, n, k, v = w["B"], w["T"], w["n"], w["k"], w["v"]
+        S = Bn * T * n
+        ws = torch.empty(lrs.mi_affine_scan_workspace(Bn, T, n, k, v), dtype=torch.uint8, device="cuda")
+        state["Abar"] = torch.empty_like(d["A"])
+        state["Bbar"] = torch.empty_like(d["Bm"])
+
+        def afwd():
+            lrs.mi_affine_scan_fwd(d["A"], d["Bm"], state["Abar"], state["Bbar"], ws=ws)
+        kernels.append(("affine_scan_fwd", afwd, 4 * 2 * (S * k * k + S * k * v)))
+        if "gAbar" in d:
+            state["dA"] = torch.empty_like(d["A"])
+            state["dB"] = torch.empty_like(d["Bm"])
+
+            def abwd():
+                lrs.mi_affine_scan_bwd(d["A"], state["Abar"], state["Bbar"], d["gAbar"], d["gBbar"],
+                                       state["dA"], state["dB"], ws=ws)
+            kernels.append(("affine_scan_bwd", abwd, 4 * (4 * S * k * k + 3 * S * k * v)))
+        desc = {"workload": "affine_scan %s k x k, B=%d, T=%d, n=%d, k=%d, v=%d, fp32"
+                % ("fwd+bwd" if len(kernels) == 2 else "fwd", Bn, T, n, k, v),
+                "B": Bn, "T": T, "n": n, "k": k, "v": v, "storage": w["dtype"]}
+        units = S
+    return desc, kernels, units, d
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline: the fp64 oracle, as it stands, on a bounded sample
+# ---------------------------------------------------------------------------
+
+def cpu_baseline(wid, torch, workloads):
+    import numpy as np
+    import oracle
+    w = workloads.WORKLOADS[wid]
+    dtype = torch.bfloat16 if w["dtype"] == "bf16" else torch.float32
+
+    def q(a):
+        return torch.from_numpy(a).to(dtype).double().numpy()
+
+    if w["op"] == "linear":
+        Bs = max(1, w["B"] // 4) if w["B"] > 1 else 1
+        x = workloads.linear_inputs(Bs, w["T"], w["D"], wid, *((0.9, 0.9999) if wid == 3 else (0.5, 0.999)),
+                                    grads=(wid == 3))
+        x = {k: q(v) for k, v in x.items()}
+        es = 2 if dtype == torch.bfloat16 else 4
+        n = Bs * w["T"] * w["D"]
+        t0 = time.perf_counter()
+        A, Bc = oracle.linear_scan_fwd(x["a"], x["b"])
+        nbytes = 4 * es * n
+        if wid == 3:
+            oracle.linear_scan_bwd(x["a"], A, Bc, x["gA"], x["gBc"])
+            nbytes += 7 * es * n
+        dt = time.perf_counter() - t0
+        sample = "B=%d of %d batch rows (T=%d, D=%d): %d elements, fwd%s" % (
+            Bs, w["B"], w["T"], w["D"], n, "+bwd" if wid == 3 else "")
+    elif w["op"] == "log":
+        Bs = 1
+        x = workloads.log_inputs(Bs, w["T"], w["D"], wid)
+        lc, lv = q(x["log_coeffs"]), q(x["log_values"])
+        n = Bs * w["T"] * w["D"]
+        t0 = time.perf_counter()
+        oracle.scan_log_fwd(lc, lv)
+        dt = time.perf_counter() - t0
+        nbytes = 4 * (3 * n + w["D"])
+        sample = "B=1 of %d batch rows: %d elements" % (w["B"], n)
+    else:
+        Bs = 1
+        gen = workloads.affine_inputs_rotation if wid == 4 else workloads.affine_inputs_diag
+        kw = {} if wid == 4 else {"grads": True}
+        x = gen(Bs, w["T"], w["n"], w["k"], w["v"], wid, **kw)
+        x = {k: q(v) for k, v in x.items()}
+        S = Bs * w["T"] * w["n"]
+        k, v = w["k"], w["v"]
+        t0 = time.perf_counter()
+        Abar, Bbar = oracle.affine_scan_fwd(x["A"], x["Bm"])
+        nbytes = 4 * 2 * (S * k * k + S * k * v)
+        if wid == 5:
+            oracle.affine_scan_bwd(x["A"], Abar, Bbar, x["gAbar"], x["gBbar"])
+            nbytes += 4 * (4 * S * k * k + 3 * S * k * v)
+        dt = time.perf_counter() - t0
+        sample = "B=1 of %d batch rows: %d head-steps" % (w["B"], S)
+    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": oracle.num_threads(),
+            "kind": "oracle", "sample": sample, "seconds": round(dt, 3)}
+
+
+# ---------------------------------------------------------------------------
+
+def stored_traffic(kernel_name, digest):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    e = t.get(kernel_name)
+    if not e or e.get("source_digest") != digest:
+        return None
+    return e.get("hbm_bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", type=int, default=3, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cold", action="store_true",
+                    help="also time each kernel alone after writing 1 GiB to evict the caches")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print("bench.py: this build measures one GPU only (the scan's multi-GPU sharding is "
+              "a design note, not built); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import linear_recurrence_scans_amd as lrs
+    import workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    ok, reason = lrs.mi_device_check(0)
+    if not ok:
+        print("bench.py: " + reason, file=sys.stderr)
+        sys.exit(1)
+
+    desc, kernels, units, _keep = build_workload(args.workload, torch, lrs, workloads)
+    stream = torch.cuda.current_stream()
+
+    log("warmup", args.warmup)
+    for _ in range(args.warmup):
+        for _, fn, _ in kernels:
+            fn()
+    torch.cuda.synchronize()
+
+    # Timed region: K steps; per-kernel HIP events on the stream the kernels run on.
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in kernels] for _ in range(args.steps)]
+    log("timing", args.steps, "steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        for i, (_, fn, _) in enumerate(kernels):
+            ev[s][i][0].record(stream)
+            fn()
+            ev[s][i][1].record(stream)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1e3 / args.steps
+
+    per_kernel = {}
+    for i, (name, _, nbytes) in enumerate(kernels):
+        ms = sum(ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(args.steps)) / args.steps
+        per_kernel[name] = {"avg_ms": round(ms, 4), "bytes": nbytes,
+                            "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1),
+                            "frac_hbm_peak": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+
+    if args.cold:
+        flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        for i, (name, fn, nbytes) in enumerate(kernels):
+            times = []
+            for _ in range(5):
+                flush.fill_(1)
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record(stream)
+                fn()
+                b.record(stream)
+                torch.cuda.synchronize()
+                times.append(a.elapsed_time(b))
+            times.sort()
+            per_kernel[name]["cold_median_ms"] = round(times[len(times) // 2], 4)
+        del flush
+
+    total_bytes = sum(k[2] for k in kernels)
+    value = total_bytes / (ms_per_step * 1e-3) / 1e9
+    dom = max(per_kernel, key=lambda n: per_kernel[n]["avg_ms"])
+    dk = per_kernel[dom]
+    digest = source_digest()
+    achieved = dk["GB/s"]
+    roofline = {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": stored_traffic(dom, digest),
+                "algorithmic_bytes_per_launch": dk["bytes"], "avg_launch_ms": dk["avg_ms"]}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle on a sample)")
+        cpu = cpu_baseline(args.workload, torch, workloads)
+
+    out = {
+        "metric": METRIC if args.workload == 3 else "scan GB/s and % HBM peak, " + desc["workload"],
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "elements_per_s": round(units / (ms_per_step * 1e-3), 1),
+        "config": desc,
+        "kernels": per_kernel,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "source_digest": digest,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,148 @@
+/*
+ * miscan.h -- C ABI of libmiscan.so: parallel prefix scans of the first-order
+ * affine recurrence h_t = a_t * h_{t-1} + b_t and its k x k matrix form, as
+ * hand-written HIP kernels for gfx950 (MI355X, CDNA4), one GPU.
+ *
+ * The operations are those of the minGRU documentation page "Triton kernels"
+ * (API reference of mingru.triton_scans), section "Kernel entry points":
+ * linear_scan_fwd/bwd, parallel_scan_log_fwd and affine_scan_fwd/bwd.  Each
+ * entry point below names the entry it implements.
+ *
+ * Common contract
+ * ---------------
+ *  - Tensors are device pointers to contiguous row-major storage.  Time is the
+ *    second axis: (B, T, D) for the channel scans, (B, T, n, r, c) for the k x k
+ *    scan.  Step t = 1..T of the recurrence is row t-1.
+ *  - Outputs have the shape and dtype of the corresponding input.  With bf16
+ *    storage all arithmetic is fp32; results are rounded to bf16 (nearest-even)
+ *    once, on store.  Every output element is written.
+ *  - Ownership: the caller allocates every input, output and the workspace.  The
+ *    library keeps no device memory and no state between calls, and never
+ *    synchronises: a call enqueues its kernels on `stream` and returns.
+ *  - Workspace: at least the bytes reported by the matching *_workspace query,
+ *    256-byte aligned, contents need not be initialised (the call clears what
+ *    it uses, on `stream`, before its scan kernel).  One workspace must not be
+ *    used by two calls that may run concurrently (e.g. on two streams).  Word 1
+ *    (bytes 4..7) counts cross-workgroup waits that hit their spin limit during
+ *    the last call; it is 0 after every correct run.
+ *  - Errors: every check runs before anything is enqueued; on any status other
+ *    than MI_OK nothing was launched, except MI_ERR_LAUNCH, which reports that
+ *    the HIP runtime refused a launch.  A problem with a zero-sized axis returns
+ *    MI_OK without launching.  Inputs and outputs must not overlap.  There is no
+ *    fallback to any other implementation.
+ *  - Sizes are int64.  Element pointers must be aligned to their element size;
+ *    wider alignment (16 bytes) and D (or k, v) divisible by the vector width
+ *    select the vectorised kernels, other layouts run narrower ones.
+ */
+#ifndef MISCAN_H
+#define MISCAN_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MI_OK = 0,
+    MI_ERR_INVALID_ARG = 1, /* null pointer, negative size, byte-size overflow,
+                               misaligned element pointer, overlapping buffers */
+    MI_ERR_UNSUPPORTED = 2, /* outside the envelope: k not in [1,16], v not in
+                               [1,128], or a dtype not built for the op */
+    MI_ERR_WORKSPACE = 3,   /* workspace NULL or smaller than the query says */
+    MI_ERR_LAUNCH = 4,      /* the HIP runtime reported an error at launch */
+    MI_ERR_DEVICE = 5       /* no usable gfx950 device */
+} mi_status;
+
+typedef enum {
+    MI_F32 = 0,  /* IEEE binary32 storage */
+    MI_BF16 = 1  /* bfloat16 storage, fp32 arithmetic */
+} mi_dtype;
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char *mi_status_string(mi_status s);
+
+/* Analogue of the page's available() probe ("Triton kernels", Availability and
+ * registry): MI_OK if `device` is a gfx950 GPU this library can launch on,
+ * otherwise MI_ERR_DEVICE with a reason copied into `reason` (may be NULL). */
+mi_status mi_device_check(int device, char *reason, size_t reason_len);
+
+/* ------------------------------------------------------------------------ */
+/* k = 1 channel scan ("Triton kernels", Kernel entry points:               */
+/* linear_scan_fwd, linear_scan_bwd).  Dtypes: MI_F32, MI_BF16.             */
+/* ------------------------------------------------------------------------ */
+
+/* Workspace bytes for mi_linear_scan_fwd / mi_linear_scan_bwd on (B, T, D). */
+size_t mi_linear_scan_workspace(int64_t B, int64_t T, int64_t D, mi_dtype dt);
+
+/* linear_scan_fwd: a, b (B,T,D) -> A (running product of a) and Bc (the h_0 = 0
+ * solution of h_t = a_t h_{t-1} + b_t), both (B,T,D). */
+mi_status mi_linear_scan_fwd(const void *a, const void *b, void *A, void *Bc,
+                             int64_t B, int64_t T, int64_t D, mi_dtype dt,
+                             void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* linear_scan_bwd: reads the forward input a, the forward outputs A, Bc and the
+ * upstream grads gA, gBc (all (B,T,D)); writes da, db (B,T,D), the grads of
+ * <gA, A> + <gBc, Bc> with respect to a and b.  A and Bc are used as given:
+ * da_t = lam_t Bc_{t-1} + mu_t A_{t-1}, db_t = lam_t, with
+ * lam_t = gBc_t + a_{t+1} lam_{t+1}, mu_t = gA_t + a_{t+1} mu_{t+1},
+ * a_{T+1} = 0, A_0 = 1, Bc_0 = 0. */
+mi_status mi_linear_scan_bwd(const void *a, const void *A, const void *Bc,
+                             const void *gA, const void *gBc, void *da, void *db,
+                             int64_t B, int64_t T, int64_t D, mi_dtype dt,
+                             void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------ */
+/* Log-space scan ("Triton kernels", Kernel entry points:                   */
+/* parallel_scan_log_fwd).  Dtypes: MI_F32, MI_BF16.                        */
+/* ------------------------------------------------------------------------ */
+
+/* Workspace bytes for mi_scan_log_fwd on (B, T, D). */
+size_t mi_scan_log_workspace(int64_t B, int64_t T, int64_t D, mi_dtype dt);
+
+/* parallel_scan_log_fwd: log_coeffs (B,T,D) holds log a_t; log_values (B,T+1,D)
+ * holds log h_0 in slot 0 and log b_t in slots 1..T.  Writes h_1..h_T as one
+ * (B,T,D) tensor `h`, where h_t = a_t h_{t-1} + b_t.  The scan state is kept in
+ * log space (log-sum-exp combine); only the stored states are exponentiated. */
+mi_status mi_scan_log_fwd(const void *log_coeffs, const void *log_values, void *h,
+                          int64_t B, int64_t T, int64_t D, mi_dtype dt,
+                          void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------ */
+/* k x k matrix-affine scan ("Triton kernels", Kernel entry points:         */
+/* affine_scan_fwd, affine_scan_bwd).  Dtype: MI_F32.  1 <= k <= 16,        */
+/* 1 <= v <= 128.                                                           */
+/* ------------------------------------------------------------------------ */
+
+/* Workspace bytes for mi_affine_scan_fwd / mi_affine_scan_bwd. */
+size_t mi_affine_scan_workspace(int64_t B, int64_t T, int64_t n, int64_t k,
+                                int64_t v, mi_dtype dt);
+
+/* affine_scan_fwd: A (B,T,n,k,k), Bm (B,T,n,k,v) -> Abar (B,T,n,k,k), the
+ * running product A_t @ ... @ A_1 (composition A_current @ A_earlier), and Bbar
+ * (B,T,n,k,v), the H_0 = 0 solution of H_t = A_t @ H_{t-1} + Bm_t. */
+mi_status mi_affine_scan_fwd(const void *A, const void *Bm, void *Abar, void *Bbar,
+                             int64_t B, int64_t T, int64_t n, int64_t k, int64_t v,
+                             mi_dtype dt, void *ws, size_t ws_bytes,
+                             hipStream_t stream);
+
+/* affine_scan_bwd: reads the forward input A, the forward outputs Abar, Bbar and
+ * the upstream grads gAbar (shape of Abar), gBbar (shape of Bbar); writes dA
+ * (shape of A) and dB (shape of Bbar), the grads of <gAbar, Abar> +
+ * <gBbar, Bbar> with respect to A and Bm.  With M_t = gAbar_t + A_{t+1}^T M_{t+1}
+ * and Lam_t = gBbar_t + A_{t+1}^T Lam_{t+1} (nothing after T):
+ * dB_t = Lam_t, dA_t = M_t Abar_{t-1}^T + Lam_t Bbar_{t-1}^T, Abar_0 = I,
+ * Bbar_0 = 0.  Abar and Bbar are used as given. */
+mi_status mi_affine_scan_bwd(const void *A, const void *Abar, const void *Bbar,
+                             const void *gAbar, const void *gBbar, void *dA, void *dB,
+                             int64_t B, int64_t T, int64_t n, int64_t k, int64_t v,
+                             mi_dtype dt, void *ws, size_t ws_bytes,
+                             hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MISCAN_H */

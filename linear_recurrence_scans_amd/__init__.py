@@ -1,0 +1,305 @@
+"""linear_recurrence_scans_amd -- MI355X (gfx950) scans of h_t = a_t h_{t-1} + b_t.
+
+Thin ctypes binding over ``libmiscan.so`` (C ABI in ``include/miscan.h``).  This
+module only marshals arguments: it checks tensor shapes, makes inputs
+contiguous, allocates outputs and the workspace with torch, and passes raw
+device pointers plus torch's current HIP stream.  Every step of every scan runs
+in the library's HIP kernels; there is no CPU or eager fallback, and a missing
+library raises at first use.
+
+Names follow the C ABI (``mi_linear_scan_fwd`` ...); the minGRU "Triton
+kernels" page's op names (``linear_scan_fwd(a, b) -> (A, Bc)`` ...) are
+provided as aliases with the same argument order and returns.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "MiscanError", "available", "library_path",
+    "mi_status_string", "mi_device_check",
+    "mi_linear_scan_workspace", "mi_linear_scan_fwd", "mi_linear_scan_bwd",
+    "mi_scan_log_workspace", "mi_scan_log_fwd",
+    "mi_affine_scan_workspace", "mi_affine_scan_fwd", "mi_affine_scan_bwd",
+    "linear_scan_fwd", "linear_scan_bwd", "parallel_scan_log_fwd",
+    "affine_scan_fwd", "affine_scan_bwd",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libmiscan.so")
+
+MI_F32, MI_BF16 = 0, 1
+_DTYPES = {torch.float32: MI_F32, torch.bfloat16: MI_BF16}
+
+# C ABI entry points and their argument types.
+_V, _I64, _SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t
+_I = ctypes.c_int
+_SIGS = {
+    "mi_status_string": ([_I], ctypes.c_char_p),
+    "mi_device_check": ([_I, ctypes.c_char_p, _SZ], _I),
+    "mi_linear_scan_workspace": ([_I64, _I64, _I64, _I], _SZ),
+    "mi_linear_scan_fwd": ([_V] * 4 + [_I64] * 3 + [_I, _V, _SZ, _V], _I),
+    "mi_linear_scan_bwd": ([_V] * 7 + [_I64] * 3 + [_I, _V, _SZ, _V], _I),
+    "mi_scan_log_workspace": ([_I64, _I64, _I64, _I], _SZ),
+    "mi_scan_log_fwd": ([_V] * 3 + [_I64] * 3 + [_I, _V, _SZ, _V], _I),
+    "mi_affine_scan_workspace": ([_I64] * 5 + [_I], _SZ),
+    "mi_affine_scan_fwd": ([_V] * 4 + [_I64] * 5 + [_I, _V, _SZ, _V], _I),
+    "mi_affine_scan_bwd": ([_V] * 7 + [_I64] * 5 + [_I, _V, _SZ, _V], _I),
+}
+
+_lib = None
+
+
+class MiscanError(RuntimeError):
+    """A libmiscan call returned a status other than MI_OK."""
+
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__("%s: %s" % (where, mi_status_string(status)))
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            raise ImportError(
+                "libmiscan.so is not built at %s; build it with "
+                "`python -m linear_recurrence_scans_amd.build` (hipcc, gfx950)" % _LIB_PATH)
+        lib = ctypes.CDLL(_LIB_PATH)
+        for name, (argtypes, restype) in _SIGS.items():
+            f = getattr(lib, name)
+            f.argtypes = argtypes
+            f.restype = restype
+        _lib = lib
+    return _lib
+
+
+def mi_status_string(status: int) -> str:
+    return _load().mi_status_string(int(status)).decode()
+
+
+def mi_device_check(device: int = 0):
+    """(ok, reason): whether `device` is a gfx950 GPU the library can launch on."""
+    buf = ctypes.create_string_buffer(256)
+    st = _load().mi_device_check(int(device), buf, 256)
+    return st == 0, buf.value.decode()
+
+
+def available():
+    """True if the HIP scans can run here, else a reason string (the page's
+    available() contract)."""
+    try:
+        _load()
+    except (ImportError, OSError) as e:
+        return "libmiscan not loadable: %s" % e
+    if not torch.cuda.is_available():
+        return "no GPU visible to torch"
+    ok, reason = mi_device_check(torch.cuda.current_device())
+    return True if ok else reason
+
+
+# ---------------------------------------------------------------------------
+# marshalling helpers
+# ---------------------------------------------------------------------------
+
+def _dt(t: torch.Tensor) -> int:
+    try:
+        return _DTYPES[t.dtype]
+    except KeyError:
+        raise TypeError("unsupported dtype %s (float32 or bfloat16)" % t.dtype) from None
+
+
+def _dev_tensor(t: torch.Tensor, name: str) -> torch.Tensor:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if not t.is_cuda:
+        raise ValueError("%s must be a GPU tensor (the scans run only on the GPU)" % name)
+    return t.contiguous()
+
+
+def _out(t, like: torch.Tensor, name: str) -> torch.Tensor:
+    if t is None:
+        return torch.empty_like(like)
+    if t.shape != like.shape or t.dtype != like.dtype or t.device != like.device or not t.is_contiguous():
+        raise ValueError("%s must be a contiguous %s tensor of shape %s on %s"
+                         % (name, like.dtype, tuple(like.shape), like.device))
+    return t
+
+
+def _stream(stream, device) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return stream.cuda_stream
+
+
+def _workspace(ws, nbytes: int, device):
+    if ws is None:
+        return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+    if ws.device != device or ws.numel() * ws.element_size() < nbytes:
+        raise ValueError("workspace too small: %d bytes needed" % nbytes)
+    return ws
+
+
+def _check(st: int, where: str):
+    if st != 0:
+        raise MiscanError(st, where)
+
+
+def _same(ref: torch.Tensor, *ts):
+    for t in ts:
+        if t.device != ref.device or t.dtype != ref.dtype:
+            raise ValueError("all tensors must share device and dtype (%s, %s)" % (ref.device, ref.dtype))
+
+
+# ---------------------------------------------------------------------------
+# k = 1 channel scan
+# ---------------------------------------------------------------------------
+
+def mi_linear_scan_workspace(B: int, T: int, D: int, dtype=torch.float32) -> int:
+    return int(_load().mi_linear_scan_workspace(B, T, D, _DTYPES[dtype]))
+
+
+def mi_linear_scan_fwd(a, b, A=None, Bc=None, *, ws=None, stream=None):
+    """(A, Bc) = linear_scan_fwd(a, b); a, b (B, T, D) float32 or bfloat16."""
+    a, b = _dev_tensor(a, "a"), _dev_tensor(b, "b")
+    if a.dim() != 3 or b.shape != a.shape:
+        raise ValueError("a and b must both be (B, T, D)")
+    _same(a, b)
+    A, Bc = _out(A, a, "A"), _out(Bc, a, "Bc")
+    Bn, T, D = a.shape
+    dt = _dt(a)
+    nbytes = _load().mi_linear_scan_workspace(Bn, T, D, dt)
+    ws = _workspace(ws, nbytes, a.device)
+    st = _load().mi_linear_scan_fwd(a.data_ptr(), b.data_ptr(), A.data_ptr(), Bc.data_ptr(),
+                                    Bn, T, D, dt, ws.data_ptr(), ws.numel() * ws.element_size(),
+                                    _stream(stream, a.device))
+    _check(st, "mi_linear_scan_fwd")
+    return A, Bc
+
+
+def mi_linear_scan_bwd(a, A, Bc, gA, gBc, da=None, db=None, *, ws=None, stream=None):
+    """(da, db) = linear_scan_bwd(a, A, Bc, gA, gBc); all (B, T, D)."""
+    a, A, Bc, gA, gBc = (_dev_tensor(t, n) for t, n in
+                         ((a, "a"), (A, "A"), (Bc, "Bc"), (gA, "gA"), (gBc, "gBc")))
+    if a.dim() != 3 or any(t.shape != a.shape for t in (A, Bc, gA, gBc)):
+        raise ValueError("a, A, Bc, gA, gBc must all be (B, T, D)")
+    _same(a, A, Bc, gA, gBc)
+    da, db = _out(da, a, "da"), _out(db, a, "db")
+    Bn, T, D = a.shape
+    dt = _dt(a)
+    nbytes = _load().mi_linear_scan_workspace(Bn, T, D, dt)
+    ws = _workspace(ws, nbytes, a.device)
+    st = _load().mi_linear_scan_bwd(a.data_ptr(), A.data_ptr(), Bc.data_ptr(), gA.data_ptr(),
+                                    gBc.data_ptr(), da.data_ptr(), db.data_ptr(), Bn, T, D, dt,
+                                    ws.data_ptr(), ws.numel() * ws.element_size(),
+                                    _stream(stream, a.device))
+    _check(st, "mi_linear_scan_bwd")
+    return da, db
+
+
+# ---------------------------------------------------------------------------
+# log-space scan
+# ---------------------------------------------------------------------------
+
+def mi_scan_log_workspace(B: int, T: int, D: int, dtype=torch.float32) -> int:
+    return int(_load().mi_scan_log_workspace(B, T, D, _DTYPES[dtype]))
+
+
+def mi_scan_log_fwd(log_coeffs, log_values, h=None, *, ws=None, stream=None):
+    """h (B, T, D) = parallel_scan_log_fwd(log_coeffs (B,T,D), log_values (B,T+1,D))."""
+    lc, lv = _dev_tensor(log_coeffs, "log_coeffs"), _dev_tensor(log_values, "log_values")
+    if lc.dim() != 3 or lv.dim() != 3 or lv.shape != (lc.shape[0], lc.shape[1] + 1, lc.shape[2]):
+        raise ValueError("log_coeffs must be (B, T, D) and log_values (B, T+1, D)")
+    _same(lc, lv)
+    h = _out(h, lc, "h")
+    Bn, T, D = lc.shape
+    dt = _dt(lc)
+    nbytes = _load().mi_scan_log_workspace(Bn, T, D, dt)
+    ws = _workspace(ws, nbytes, lc.device)
+    st = _load().mi_scan_log_fwd(lc.data_ptr(), lv.data_ptr(), h.data_ptr(), Bn, T, D, dt,
+                                 ws.data_ptr(), ws.numel() * ws.element_size(),
+                                 _stream(stream, lc.device))
+    _check(st, "mi_scan_log_fwd")
+    return h
+
+
+# ---------------------------------------------------------------------------
+# k x k matrix-affine scan
+# ---------------------------------------------------------------------------
+
+def mi_affine_scan_workspace(B: int, T: int, n: int, k: int, v: int, dtype=torch.float32) -> int:
+    return int(_load().mi_affine_scan_workspace(B, T, n, k, v, _DTYPES[dtype]))
+
+
+def _affine_shapes(A, Bm):
+    if A.dim() != 5 or A.shape[3] != A.shape[4]:
+        raise ValueError("A must be (B, T, n, k, k)")
+    if Bm.dim() != 5 or Bm.shape[:4] != A.shape[:4]:
+        raise ValueError("Bm/Bbar must be (B, T, n, k, v) with the B, T, n, k of A")
+    Bn, T, n, k, _ = A.shape
+    return Bn, T, n, k, Bm.shape[4]
+
+
+def mi_affine_scan_fwd(A, Bm, Abar=None, Bbar=None, *, ws=None, stream=None):
+    """(Abar, Bbar) = affine_scan_fwd(A (B,T,n,k,k), Bm (B,T,n,k,v)); float32."""
+    A, Bm = _dev_tensor(A, "A"), _dev_tensor(Bm, "Bm")
+    _same(A, Bm)
+    Bn, T, n, k, v = _affine_shapes(A, Bm)
+    Abar, Bbar = _out(Abar, A, "Abar"), _out(Bbar, Bm, "Bbar")
+    dt = _dt(A)
+    nbytes = _load().mi_affine_scan_workspace(Bn, T, n, k, v, dt)
+    ws = _workspace(ws, nbytes, A.device)
+    st = _load().mi_affine_scan_fwd(A.data_ptr(), Bm.data_ptr(), Abar.data_ptr(), Bbar.data_ptr(),
+                                    Bn, T, n, k, v, dt, ws.data_ptr(),
+                                    ws.numel() * ws.element_size(), _stream(stream, A.device))
+    _check(st, "mi_affine_scan_fwd")
+    return Abar, Bbar
+
+
+def mi_affine_scan_bwd(A, Abar, Bbar, gAbar, gBbar, dA=None, dB=None, *, ws=None, stream=None):
+    """(dA, dB) = affine_scan_bwd(A, Abar, Bbar, gAbar, gBbar); float32."""
+    A, Abar, Bbar, gAbar, gBbar = (_dev_tensor(t, nm) for t, nm in
+                                   ((A, "A"), (Abar, "Abar"), (Bbar, "Bbar"),
+                                    (gAbar, "gAbar"), (gBbar, "gBbar")))
+    _same(A, Abar, Bbar, gAbar, gBbar)
+    Bn, T, n, k, v = _affine_shapes(A, Bbar)
+    if Abar.shape != A.shape or gAbar.shape != A.shape or gBbar.shape != Bbar.shape:
+        raise ValueError("Abar, gAbar must match A; gBbar must match Bbar")
+    dA, dB = _out(dA, A, "dA"), _out(dB, Bbar, "dB")
+    dt = _dt(A)
+    nbytes = _load().mi_affine_scan_workspace(Bn, T, n, k, v, dt)
+    ws = _workspace(ws, nbytes, A.device)
+    st = _load().mi_affine_scan_bwd(A.data_ptr(), Abar.data_ptr(), Bbar.data_ptr(),
+                                    gAbar.data_ptr(), gBbar.data_ptr(), dA.data_ptr(),
+                                    dB.data_ptr(), Bn, T, n, k, v, dt, ws.data_ptr(),
+                                    ws.numel() * ws.element_size(), _stream(stream, A.device))
+    _check(st, "mi_affine_scan_bwd")
+    return dA, dB
+
+
+# Op names of the minGRU "Triton kernels" page (same arguments and returns).
+def linear_scan_fwd(a, b):
+    return mi_linear_scan_fwd(a, b)
+
+
+def linear_scan_bwd(a, A, Bc, gA, gBc):
+    return mi_linear_scan_bwd(a, A, Bc, gA, gBc)
+
+
+def parallel_scan_log_fwd(log_coeffs, log_values):
+    return mi_scan_log_fwd(log_coeffs, log_values)
+
+
+def affine_scan_fwd(A, Bm):
+    return mi_affine_scan_fwd(A, Bm)
+
+
+def affine_scan_bwd(A, Abar, Bbar, gAbar, gBbar):
+    return mi_affine_scan_bwd(A, Abar, Bbar, gAbar, gBbar)

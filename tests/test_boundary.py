@@ -1,0 +1,167 @@
+"""C-ABI boundary checks that need no GPU.
+
+The library must load, export every function include/miscan.h declares, and
+reject bad arguments with the documented status *before* anything is launched.
+Every call below is built to fail validation (or to be a zero-sized no-op), so
+no kernel is ever enqueued and the fake pointers are never dereferenced.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import linear_recurrence_scans_amd as lrs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "miscan.h")
+
+MI_OK, MI_ERR_INVALID_ARG, MI_ERR_UNSUPPORTED, MI_ERR_WORKSPACE, MI_ERR_LAUNCH, MI_ERR_DEVICE = range(6)
+F32, BF16 = 0, 1
+P = 1 << 20        # fake, 256-byte aligned "device" addresses; never dereferenced
+STEP = 1 << 30     # far apart: no overlap unless a test wants one
+
+
+def lib():
+    return lrs._load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(mi_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_symbols_exported():
+    names = declared_functions()
+    assert len(names) >= 10, names
+    so = ctypes.CDLL(lrs.library_path())
+    for n in names:
+        assert hasattr(so, n), "libmiscan.so does not export %s" % n
+    # the binding wraps every declared entry point under the same name
+    for n in names:
+        assert hasattr(lrs, n), "binding lacks %s" % n
+
+
+def test_status_strings():
+    for code in range(6):
+        s = lrs.mi_status_string(code)
+        assert s.startswith("MI_"), s
+    assert "unknown" in lrs.mi_status_string(99)
+
+
+def ptrs(n, base=P):
+    return [base + i * STEP for i in range(n)]
+
+
+def fwd(a, b, A, Bc, Bn, T, D, dt=F32, ws=None, wsb=0):
+    return lib().mi_linear_scan_fwd(a, b, A, Bc, Bn, T, D, dt, ws, wsb, None)
+
+
+def test_linear_fwd_validation():
+    a, b, A, Bc, ws = ptrs(5)
+    big = 1 << 40
+    assert fwd(a, b, A, Bc, -1, 4, 4) == MI_ERR_INVALID_ARG                 # negative size
+    assert fwd(None, b, A, Bc, 1, 4, 4, ws=ws, wsb=big) == MI_ERR_INVALID_ARG  # null pointer
+    assert fwd(a, b, A, Bc, 1, 4, 4, dt=7) == MI_ERR_UNSUPPORTED            # unknown dtype
+    assert fwd(a + 2, b, A, Bc, 1, 4, 4, ws=ws, wsb=big) == MI_ERR_INVALID_ARG  # misaligned f32
+    assert fwd(a + 2, b, A, Bc, 1, 4, 4, dt=BF16, ws=None) == MI_ERR_WORKSPACE  # bf16 aligned ok
+    assert fwd(a, b, a + 8, Bc, 1, 4, 4, ws=ws, wsb=big) == MI_ERR_INVALID_ARG  # output overlaps input
+    assert fwd(a, b, A, A + 4, 1, 4, 4, ws=ws, wsb=big) == MI_ERR_INVALID_ARG  # outputs overlap
+    assert fwd(a, b, A, Bc, 1, 4, 4, ws=None) == MI_ERR_WORKSPACE           # no workspace
+    need = lib().mi_linear_scan_workspace(1, 4, 4, F32)
+    assert need > 0
+    assert fwd(a, b, A, Bc, 1, 4, 4, ws=ws, wsb=need - 1) == MI_ERR_WORKSPACE
+    assert fwd(a, b, A, Bc, 1, 4, 4, ws=ws + 16, wsb=big) == MI_ERR_INVALID_ARG  # ws not 256-aligned
+    assert fwd(a, b, A, Bc, 1, 4, 4, ws=a + 64, wsb=big) == MI_ERR_INVALID_ARG   # ws overlaps a
+    # int64 overflow of the byte size
+    assert fwd(a, b, A, Bc, 1 << 40, 1 << 20, 1 << 10) == MI_ERR_INVALID_ARG
+
+
+def test_zero_sized_problems_launch_nothing():
+    # zero-sized axes: MI_OK with null pointers and no workspace
+    assert fwd(None, None, None, None, 0, 5, 5) == MI_OK
+    assert fwd(None, None, None, None, 2, 0, 5) == MI_OK
+    assert fwd(None, None, None, None, 2, 5, 0) == MI_OK
+    L = lib()
+    assert L.mi_linear_scan_bwd(*([None] * 7), 3, 0, 2, BF16, None, 0, None) == MI_OK
+    assert L.mi_scan_log_fwd(None, None, None, 0, 3, 3, F32, None, 0, None) == MI_OK
+    assert L.mi_affine_scan_fwd(None, None, None, None, 1, 0, 2, 4, 4, F32, None, 0, None) == MI_OK
+    assert L.mi_affine_scan_bwd(*([None] * 7), 1, 2, 0, 4, 4, F32, None, 0, None) == MI_OK
+    assert L.mi_linear_scan_workspace(0, 5, 5, F32) == 0
+
+
+def test_linear_bwd_validation():
+    L = lib()
+    p = ptrs(8)
+    assert L.mi_linear_scan_bwd(*p[:7], 1, 8, 8, F32, None, 0, None) == MI_ERR_WORKSPACE
+    q = list(p[:7])
+    q[6] = q[0]  # db aliases a
+    assert L.mi_linear_scan_bwd(*q, 1, 8, 8, F32, p[7], 1 << 40, None) == MI_ERR_INVALID_ARG
+    q = list(p[:7])
+    q[3] = None
+    assert L.mi_linear_scan_bwd(*q, 1, 8, 8, F32, p[7], 1 << 40, None) == MI_ERR_INVALID_ARG
+
+
+def test_log_validation():
+    L = lib()
+    lc, lv, h, ws = ptrs(4)
+    assert L.mi_scan_log_fwd(lc, lv, h, 2, 8, 8, F32, None, 0, None) == MI_ERR_WORKSPACE
+    # h overlapping log_values' last row (log_values has T+1 rows)
+    assert L.mi_scan_log_fwd(lc, lv, lv + 2 * 8 * 8 * 4, 2, 8, 8, F32, ws, 1 << 40, None) == MI_ERR_INVALID_ARG
+    assert L.mi_scan_log_fwd(lc, lv, h, 2, 8, 8, 5, None, 0, None) == MI_ERR_UNSUPPORTED
+
+
+def test_affine_envelope():
+    L = lib()
+    A, Bm, Ab, Bb, ws = ptrs(5)
+    call = lambda k, v, dt=F32, w=None, wb=0: L.mi_affine_scan_fwd(A, Bm, Ab, Bb, 1, 4, 2, k, v, dt, w, wb, None)
+    assert call(0, 4) == MI_ERR_UNSUPPORTED
+    assert call(17, 4) == MI_ERR_UNSUPPORTED
+    assert call(4, 0) == MI_ERR_UNSUPPORTED
+    assert call(4, 129) == MI_ERR_UNSUPPORTED
+    assert call(4, 4, BF16) == MI_ERR_UNSUPPORTED   # k x k is built for fp32 only
+    assert call(16, 128) == MI_ERR_WORKSPACE        # inside the envelope
+    assert call(1, 1) == MI_ERR_WORKSPACE
+    assert L.mi_affine_scan_workspace(1, 4, 2, 17, 4, F32) == 0
+    assert L.mi_affine_scan_bwd(A, Ab, Bb, Bm, Bm, ws, ws, 1, 4, 2, 4, 4, F32, P, 1 << 40, None) == MI_ERR_INVALID_ARG
+
+
+def test_workspace_sizes_cover_every_shape():
+    L = lib()
+    for Bn, T, D in ((1, 1, 1), (1, 1024, 64), (8, 8192, 4096), (3, 1000, 100)):
+        for dt in (F32, BF16):
+            w = L.mi_linear_scan_workspace(Bn, T, D, dt)
+            assert w >= 256 + 256
+            assert L.mi_scan_log_workspace(Bn, T, D, dt) >= 512
+    for args in ((2, 2048, 64, 4, 16), (4, 4096, 32, 8, 32), (1, 1, 1, 1, 1), (1, 7, 3, 16, 128), (2, 5, 3, 3, 5)):
+        assert L.mi_affine_scan_workspace(*args, F32) > 0
+    # larger problems never need less
+    assert L.mi_linear_scan_workspace(8, 8192, 4096, BF16) > L.mi_linear_scan_workspace(8, 4096, 4096, BF16)
+
+
+def test_binding_refuses_cpu_tensors():
+    torch = pytest.importorskip("torch")
+    a = torch.rand(1, 4, 4)
+    with pytest.raises(ValueError, match="GPU"):
+        lrs.linear_scan_fwd(a, a)
+    with pytest.raises(ValueError, match="GPU"):
+        lrs.parallel_scan_log_fwd(a, torch.rand(1, 5, 4))
+
+
+def test_available_reports_reason_without_gpu():
+    torch = pytest.importorskip("torch")
+    r = lrs.available()
+    if not torch.cuda.is_available():
+        assert isinstance(r, str) and r
+
+
+def test_product_path_does_not_import_oracle():
+    """The HIP binding never imports or links the oracle."""
+    pkg = os.path.join(ROOT, "linear_recurrence_scans_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".hip", ".hpp", ".cpp", ".h")):
+                text = open(os.path.join(dirpath, f)).read()
+                assert "import oracle" not in text and "from oracle" not in text, f
+                assert "lrs_oracle" not in text and "liboracle" not in text, f

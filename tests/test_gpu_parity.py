@@ -1,0 +1,319 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Inputs are seeded and synthetic with the workloads' distributions
+(workloads.py); both sides see the same quantised values.  Error readings and
+tolerances are described in tests/parity.py.  Every case prints what it runs
+before touching the GPU.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import linear_recurrence_scans_amd as lrs
+import oracle
+from parity import TOL, block_err, quantise, scaled_err, timeouts, to_np
+from workloads import (affine_inputs_diag, affine_inputs_rotation, linear_inputs, log_inputs,
+                       workload_inputs)
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*args):
+    print("[case]", *args, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu_ready():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    ok, reason = lrs.mi_device_check(0)
+    assert ok, reason
+
+
+# ---------------------------------------------------------------------------
+# k = 1 channel scan
+# ---------------------------------------------------------------------------
+
+def run_linear(x, dtype, with_bwd=True, check_ws=True):
+    """GPU fwd (+ bwd) on quantised inputs; returns dict of errors vs the oracle."""
+    a_d, a = quantise(x["a"], dtype)
+    b_d, b = quantise(x["b"], dtype)
+    Bn, T, D = a.shape
+    ws = torch.empty(max(lrs.mi_linear_scan_workspace(Bn, T, D, dtype), 8), dtype=torch.uint8,
+                     device="cuda")
+    A_d, Bc_d = lrs.mi_linear_scan_fwd(a_d, b_d, ws=ws)
+    torch.cuda.synchronize()
+    if check_ws and ws.numel() >= 8:
+        assert timeouts(ws) == 0
+    A_r, Bc_r = oracle.linear_scan_fwd(a, b)
+    _, Bc_s = oracle.linear_scan_fwd(np.abs(a), np.abs(b))
+    errs = {"A": scaled_err(to_np(A_d), A_r, A_r), "Bc": scaled_err(to_np(Bc_d), Bc_r, Bc_s)}
+    if with_bwd:
+        # backward inputs: the oracle's forward states, quantised like any input
+        A_in_d, A_in = quantise(A_r, dtype)
+        Bc_in_d, Bc_in = quantise(Bc_r, dtype)
+        gA_d, gA = quantise(x["gA"], dtype)
+        gB_d, gB = quantise(x["gBc"], dtype)
+        da_d, db_d = lrs.mi_linear_scan_bwd(a_d, A_in_d, Bc_in_d, gA_d, gB_d, ws=ws)
+        torch.cuda.synchronize()
+        if check_ws and ws.numel() >= 8:
+            assert timeouts(ws) == 0
+        da_r, db_r = oracle.linear_scan_bwd(a, A_in, Bc_in, gA, gB)
+        da_s, db_s = oracle.linear_scan_bwd(np.abs(a), np.abs(A_in), np.abs(Bc_in), np.abs(gA),
+                                            np.abs(gB))
+        errs["da"] = scaled_err(to_np(da_d), da_r, da_s)
+        errs["db"] = scaled_err(to_np(db_d), db_r, db_s)
+    return errs
+
+
+def lin_case(Bn, T, D, seed, a_lo=0.5, a_hi=0.999):
+    return linear_inputs(Bn, T, D, seed, a_lo, a_hi, grads=True)
+
+
+@pytest.mark.parametrize("seed", [1, 11])
+def test_linear_fwd_workload1(seed):
+    """Workload 1 at its own size: B=1, T=1024, D=64, fp32."""
+    say("linear fwd+bwd fp32 B=1 T=1024 D=64 seed", seed)
+    errs = run_linear(lin_case(1, 1024, 64, seed), torch.float32)
+    assert max(errs.values()) <= TOL[torch.float32], errs
+
+
+@pytest.mark.parametrize("shape", [(1, 1, 1), (2, 2, 3), (1, 63, 100), (3, 65, 1), (2, 1000, 3),
+                                   (1, 4097, 100), (2, 130, 520), (1, 64, 256), (2, 129, 257)])
+def test_linear_edge_shapes_f32(shape):
+    say("linear fwd+bwd fp32 edge shape", shape)
+    errs = run_linear(lin_case(*shape, seed=sum(shape)), torch.float32)
+    assert max(errs.values()) <= TOL[torch.float32], (shape, errs)
+
+
+@pytest.mark.parametrize("shape", [(2, 1000, 4104), (1, 77, 37), (3, 33, 6), (1, 300, 12)])
+def test_linear_bf16_reduced(shape):
+    """bf16 storage / fp32 arithmetic on the workload-3 distribution; D values
+    pick the 8-, 4-, 2- and 1-wide vector kernels and ragged tiles."""
+    say("linear fwd+bwd bf16 shape", shape)
+    errs = run_linear(lin_case(*shape, seed=13, a_lo=0.9, a_hi=0.9999), torch.bfloat16)
+    assert max(errs.values()) <= TOL[torch.bfloat16], (shape, errs)
+
+
+def test_linear_misaligned_views():
+    """A view starting one element into its storage takes the 1-wide kernel."""
+    say("linear fwd fp32 misaligned view B=2 T=300 D=64")
+    x = lin_case(2, 300, 64, seed=21)
+    a_full = torch.from_numpy(np.concatenate([[0.0], x["a"].ravel()])).float().cuda()
+    b_full = torch.from_numpy(np.concatenate([[0.0], x["b"].ravel()])).float().cuda()
+    a_d = a_full[1:].view(2, 300, 64)
+    b_d = b_full[1:].view(2, 300, 64)
+    assert a_d.data_ptr() % 16 != 0
+    A_d, Bc_d = lrs.linear_scan_fwd(a_d, b_d)
+    a = a_d.double().cpu().numpy()
+    b = b_d.double().cpu().numpy()
+    A_r, Bc_r = oracle.linear_scan_fwd(a, b)
+    _, Bc_s = oracle.linear_scan_fwd(np.abs(a), np.abs(b))
+    assert scaled_err(to_np(A_d), A_r, A_r) <= 1e-5
+    assert scaled_err(to_np(Bc_d), Bc_r, Bc_s) <= 1e-5
+
+
+def test_linear_lookback_long_sequence():
+    """Many more workgroups than fit on the GPU along one tile's time axis:
+    B=1, T=2^20, D=64 -- forward progress of the look-back and correctness."""
+    say("linear fwd+bwd fp32 B=1 T=1048576 D=64 (look-back stress)")
+    errs = run_linear(lin_case(1, 1 << 20, 64, seed=8, a_lo=0.9, a_hi=0.9999), torch.float32)
+    assert max(errs.values()) <= TOL[torch.float32], errs
+
+
+def test_linear_repeated_runs():
+    """Race check over ten runs.  The decoupled look-back folds a chunk's
+    predecessors in an order that depends on which of them has published its
+    inclusive prefix, so runs may differ in the last bit of the carry; each
+    run must still match the oracle, and runs must agree to rounding."""
+    say("linear fwd+bwd bf16 ten repeated runs B=2 T=4096 D=1024")
+    dt = torch.bfloat16
+    x = lin_case(2, 4096, 1024, seed=5, a_lo=0.9, a_hi=0.9999)
+    a_d, a = quantise(x["a"], dt)
+    b_d, b = quantise(x["b"], dt)
+    gA_d, gA = quantise(x["gA"], dt)
+    gB_d, gB = quantise(x["gBc"], dt)
+    A_r, Bc_r = oracle.linear_scan_fwd(a, b)
+    _, Bc_s = oracle.linear_scan_fwd(np.abs(a), np.abs(b))
+    A_in_d, A_in = quantise(A_r, dt)
+    Bc_in_d, Bc_in = quantise(Bc_r, dt)
+    da_r, db_r = oracle.linear_scan_bwd(a, A_in, Bc_in, gA, gB)
+    da_s, db_s = oracle.linear_scan_bwd(np.abs(a), np.abs(A_in), np.abs(Bc_in), np.abs(gA), np.abs(gB))
+    first = None
+    for run in range(10):
+        A_d, Bc_d = lrs.linear_scan_fwd(a_d, b_d)
+        da_d, db_d = lrs.linear_scan_bwd(a_d, A_in_d, Bc_in_d, gA_d, gB_d)
+        outs = [to_np(t) for t in (A_d, Bc_d, da_d, db_d)]
+        errs = [scaled_err(outs[0], A_r, A_r), scaled_err(outs[1], Bc_r, Bc_s),
+                scaled_err(outs[2], da_r, da_s), scaled_err(outs[3], db_r, db_s)]
+        assert max(errs) <= TOL[dt], (run, errs)
+        if first is None:
+            first = outs
+        else:
+            scales = (A_r, Bc_s, da_s, db_s)
+            for f, o, s_ in zip(first, outs, scales):
+                assert scaled_err(o, f, s_) <= 2 * TOL[dt], run
+
+
+def test_linear_workload3_full():
+    """Workload 3 at its full size (B=8, T=8192, D=4096, bf16), the launch
+    configuration the benchmark times; every output element is compared."""
+    say("linear fwd+bwd bf16 B=8 T=8192 D=4096 seed 3 (full size)")
+    errs = run_linear(workload_inputs(3), torch.bfloat16)
+    print("errors", errs, flush=True)
+    assert max(errs.values()) <= TOL[torch.bfloat16], errs
+
+
+# ---------------------------------------------------------------------------
+# log-space scan
+# ---------------------------------------------------------------------------
+
+def run_log(x, dtype):
+    lc_d, lc = quantise(x["log_coeffs"], dtype)
+    lv_d, lv = quantise(x["log_values"], dtype)
+    Bn, T, D = lc.shape
+    ws = torch.empty(max(lrs.mi_scan_log_workspace(Bn, T, D, dtype), 8), dtype=torch.uint8,
+                     device="cuda")
+    h_d = lrs.mi_scan_log_fwd(lc_d, lv_d, ws=ws)
+    torch.cuda.synchronize()
+    assert timeouts(ws) == 0
+    h_r = oracle.scan_log_fwd_logspace(lc, lv)
+    return scaled_err(to_np(h_d), h_r, h_r)
+
+
+@pytest.mark.parametrize("seed", [2, 12])
+def test_log_workload2_full(seed):
+    say("log fwd fp32 B=4 T=4096 D=512 seed", seed)
+    e = run_log(workload_inputs(2, seed=seed), torch.float32)
+    print("error", e, flush=True)
+    assert e <= TOL[torch.float32], e
+
+
+@pytest.mark.parametrize("shape", [(1, 1, 1), (2, 63, 3), (1, 65, 100), (2, 1000, 5), (1, 4097, 64),
+                                   (3, 200, 260)])
+def test_log_edge_shapes(shape):
+    say("log fwd fp32 edge shape", shape)
+    e = run_log(log_inputs(*shape, seed=sum(shape)), torch.float32)
+    assert e <= TOL[torch.float32], (shape, e)
+
+
+def test_log_bf16():
+    say("log fwd bf16 B=2 T=500 D=136")
+    e = run_log(log_inputs(2, 500, 136, seed=7), torch.bfloat16)
+    assert e <= TOL[torch.bfloat16], e
+
+
+def test_log_extreme_range():
+    """Magnitudes whose linear form would underflow fp32: a = e^-120 on some
+    steps, b = e^-90; the log-space result is still exact to fp32."""
+    say("log fwd fp32 extreme range B=1 T=256 D=64")
+    r = np.random.Generator(np.random.PCG64(99))
+    lc = np.where(r.random((1, 256, 64)) < 0.1, -120.0, -0.01)
+    lv = np.full((1, 257, 64), -90.0) + r.normal(0, 1, (1, 257, 64))
+    e = run_log({"log_coeffs": lc, "log_values": lv}, torch.float32)
+    assert e <= TOL[torch.float32], e
+
+
+# ---------------------------------------------------------------------------
+# k x k scan
+# ---------------------------------------------------------------------------
+
+def run_affine(x, with_bwd, metric):
+    """metric "block": per (b, t, head) block relative to the block's largest
+    entry -- for rotation inputs, whose elementwise-absolute products grow
+    geometrically.  metric "abs": the condition-normalised reading of the k = 1
+    scan (oracle on absolute values as the scale) -- for diagonally dominant
+    inputs, whose absolute products stay bounded."""
+    A_d, A = quantise(x["A"], torch.float32)
+    B_d, Bm = quantise(x["Bm"], torch.float32)
+    Bn, T, n, k, _ = A.shape
+    v = Bm.shape[4]
+    ws = torch.empty(max(lrs.mi_affine_scan_workspace(Bn, T, n, k, v), 8), dtype=torch.uint8,
+                     device="cuda")
+    Abar_d, Bbar_d = lrs.mi_affine_scan_fwd(A_d, B_d, ws=ws)
+    torch.cuda.synchronize()
+    assert timeouts(ws) == 0
+    Abar_r, Bbar_r = oracle.affine_scan_fwd(A, Bm)
+    if metric == "block":
+        errs = {"Abar": block_err(to_np(Abar_d), Abar_r), "Bbar": block_err(to_np(Bbar_d), Bbar_r)}
+    else:
+        Abar_s, Bbar_s = oracle.affine_scan_fwd(np.abs(A), np.abs(Bm))
+        assert np.all(np.isfinite(Abar_s)) and np.all(np.isfinite(Bbar_s))
+        errs = {"Abar": scaled_err(to_np(Abar_d), Abar_r, Abar_s),
+                "Bbar": scaled_err(to_np(Bbar_d), Bbar_r, Bbar_s)}
+    if with_bwd:
+        assert metric == "abs"
+        Ab_in_d, Ab_in = quantise(Abar_r, torch.float32)
+        Bb_in_d, Bb_in = quantise(Bbar_r, torch.float32)
+        gA_d, gA = quantise(x["gAbar"], torch.float32)
+        gB_d, gB = quantise(x["gBbar"], torch.float32)
+        dA_d, dB_d = lrs.mi_affine_scan_bwd(A_d, Ab_in_d, Bb_in_d, gA_d, gB_d, ws=ws)
+        torch.cuda.synchronize()
+        assert timeouts(ws) == 0
+        dA_r, dB_r = oracle.affine_scan_bwd(A, Ab_in, Bb_in, gA, gB)
+        dA_s, dB_s = oracle.affine_scan_bwd(np.abs(A), np.abs(Ab_in), np.abs(Bb_in), np.abs(gA),
+                                            np.abs(gB))
+        assert np.all(np.isfinite(dA_s)) and np.all(np.isfinite(dB_s))
+        errs["dA"] = scaled_err(to_np(dA_d), dA_r, dA_s)
+        errs["dB"] = scaled_err(to_np(dB_d), dB_r, dB_s)
+    return errs
+
+
+@pytest.mark.parametrize("seed", [4, 14])
+def test_affine_workload4_full(seed):
+    say("affine fwd fp32 B=2 T=2048 n=64 k=4 v=16 seed", seed)
+    errs = run_affine(workload_inputs(4, seed=seed), with_bwd=False, metric="block")
+    print("errors", errs, flush=True)
+    assert max(errs.values()) <= TOL[torch.float32], errs
+
+
+@pytest.mark.parametrize("seed", [5, 15])
+def test_affine_workload5_full(seed):
+    say("affine fwd+bwd fp32 B=4 T=4096 n=32 k=8 v=32 seed", seed)
+    errs = run_affine(workload_inputs(5, seed=seed), with_bwd=True, metric="abs")
+    print("errors", errs, flush=True)
+    assert max(errs.values()) <= TOL[torch.float32], errs
+
+
+@pytest.mark.parametrize("kv", [(1, 1), (2, 2), (3, 5), (4, 16), (8, 32), (16, 1), (2, 128),
+                                (16, 128), (5, 3), (4, 6)])
+def test_affine_edge_shapes(kv):
+    k, v = kv
+    for (Bn, T, n) in ((1, 1, 1), (2, 33, 3), (1, 130, 5)):
+        say("affine fwd+bwd fp32 edge B,T,n,k,v =", (Bn, T, n, k, v))
+        x = affine_inputs_diag(Bn, T, n, k, v, seed=k * 100 + v + T, grads=True)
+        errs = run_affine(x, with_bwd=True, metric="abs")
+        assert max(errs.values()) <= TOL[torch.float32], ((Bn, T, n, k, v), errs)
+
+
+def test_affine_rotation_long():
+    """Rotations (non-commuting products) over a long sequence."""
+    say("affine fwd fp32 rotation B=1 T=5000 n=3 k=4 v=3")
+    x = affine_inputs_rotation(1, 5000, 3, 4, 3, seed=31, rho=0.999)
+    errs = run_affine(x, with_bwd=False, metric="block")
+    assert max(errs.values()) <= TOL[torch.float32], errs
+
+
+def test_affine_repeated_runs():
+    """Race check over ten runs (see test_linear_repeated_runs)."""
+    say("affine fwd+bwd ten repeated runs B=2 T=1024 n=16 k=8 v=32")
+    x = affine_inputs_diag(2, 1024, 16, 8, 32, seed=3, grads=True)
+    A_d, A = quantise(x["A"], torch.float32)
+    B_d, Bm = quantise(x["Bm"], torch.float32)
+    gA_d, gA = quantise(x["gAbar"], torch.float32)
+    gB_d, gB = quantise(x["gBbar"], torch.float32)
+    Abar_r, Bbar_r = oracle.affine_scan_fwd(A, Bm)
+    Abar_s, Bbar_s = oracle.affine_scan_fwd(np.abs(A), np.abs(Bm))
+    Ab_in_d, Ab_in = quantise(Abar_r, torch.float32)
+    Bb_in_d, Bb_in = quantise(Bbar_r, torch.float32)
+    dA_r, dB_r = oracle.affine_scan_bwd(A, Ab_in, Bb_in, gA, gB)
+    dA_s, dB_s = oracle.affine_scan_bwd(np.abs(A), np.abs(Ab_in), np.abs(Bb_in), np.abs(gA), np.abs(gB))
+    for run in range(10):
+        Abar_d, Bbar_d = lrs.affine_scan_fwd(A_d, B_d)
+        dA_d, dB_d = lrs.affine_scan_bwd(A_d, Ab_in_d, Bb_in_d, gA_d, gB_d)
+        errs = [scaled_err(to_np(Abar_d), Abar_r, Abar_s), scaled_err(to_np(Bbar_d), Bbar_r, Bbar_s),
+                scaled_err(to_np(dA_d), dA_r, dA_s), scaled_err(to_np(dB_d), dB_r, dB_s)]
+        assert max(errs) <= TOL[torch.float32], (run, errs)
