@@ -206,40 +206,40 @@ __device__ __forceinline__ void fwd_step(float (&x)[KP][CPL], const FwdArgs &p, 
     }
 }
 
-// Own columns of one head's payload block, row-major (KP rows of NCP floats).
-template <int KP, int CPL, bool VIO>
+// Own columns of one head's payload block, row-major (KP rows of NCP floats),
+// moved with device-coherent word accesses (see common.hpp).
+template <int KP, int CPL>
 __device__ __forceinline__ void payload_store(float *blk, int NCP, int c0, const float (&x)[KP][CPL]) {
 #pragma unroll
-    for (int i = 0; i < KP; ++i) {
-        if constexpr (VIO) stv<CPL, false>(blk + i * NCP + c0, x[i]);
-        else {
+    for (int i = 0; i < KP; ++i)
 #pragma unroll
-            for (int cc = 0; cc < CPL; ++cc) blk[i * NCP + c0 + cc] = x[i][cc];
-        }
-    }
+        for (int cc = 0; cc < CPL; ++cc) carry_store(blk + i * NCP + c0 + cc, x[i][cc]);
 }
-template <int KP, int CPL, bool VIO>
+template <int KP, int CPL>
 __device__ __forceinline__ void payload_load(float (&x)[KP][CPL], const float *blk, int NCP, int c0) {
 #pragma unroll
-    for (int i = 0; i < KP; ++i) {
-        if constexpr (VIO) ldv<CPL>(x[i], blk + i * NCP + c0);
-        else {
+    for (int i = 0; i < KP; ++i)
 #pragma unroll
-            for (int cc = 0; cc < CPL; ++cc) x[i][cc] = blk[i * NCP + c0 + cc];
-        }
-    }
+        for (int cc = 0; cc < CPL; ++cc) x[i][cc] = carry_load(blk + i * NCP + c0 + cc);
 }
 
-// S <- M S (+ add where addmask), column by column, M a KP x KP block whose
-// rows are read one at a time from `Msrc` (row stride `ld`).
-template <int KP, int CPL, bool VIO>
+// S <- M S (+ add where addmask), column by column.  M is the leading k x k
+// block (zero padded to KP) of a row-major matrix with row stride `ld`, read
+// either from a published payload (PAYLOAD: device-coherent word loads) or
+// from LDS.
+template <int KP, int CPL, bool PAYLOAD>
 __device__ __forceinline__ void mat_apply(float (&S)[KP][CPL], const float *Msrc, int64_t ld, int k,
                                           const float (&add)[KP][CPL], const bool (&addmask)[CPL]) {
     float ns[KP][CPL];
 #pragma unroll
     for (int i = 0; i < KP; ++i) {
         float mrow[KP];
-        load_row<KP, VIO>(mrow, Msrc + i * ld, i < k, k);
+#pragma unroll
+        for (int j = 0; j < KP; ++j) {
+            const bool in = i < k && j < k;
+            if constexpr (PAYLOAD) mrow[j] = in ? carry_load(Msrc + i * ld + j) : 0.f;
+            else mrow[j] = in ? Msrc[i * ld + j] : 0.f;
+        }
 #pragma unroll
         for (int cc = 0; cc < CPL; ++cc) {
             float s = addmask[cc] ? add[i][cc] : 0.f;
@@ -326,22 +326,17 @@ __global__ __launch_bounds__(64) void affine_fwd_kernel(FwdArgs p) {
         for (int cc = 0; cc < CPL; ++cc)
             S[i][cc] = (cl.kind[cc] == C_ABAR && i == cl.col[cc]) ? 1.f : 0.f;
     if (chunk > 0) {
-        if (slot_lane) payload_store<KP, CPL, VIO>(p.ws.agg + slot * slot_sz + hoff, p.NCP, c0, x);
-        publish_flag(p.ws.flags + slot, FLAG_AGG);
-        int j0 = chunk - 1;
-        for (; j0 > 0; --j0) {
-            const uint32_t f = wait_flag(p.ws.flags + (int64_t)grp * p.n_chunks + j0, p.ws.hdr + 1);
-            if (f == FLAG_INC) break;
-        }
-        if (j0 == 0) (void)wait_flag(p.ws.flags + (int64_t)grp * p.n_chunks, p.ws.hdr + 1);
+        if (slot_lane) payload_store<KP, CPL>(p.ws.agg + slot * slot_sz + hoff, p.NCP, c0, x);
+        const int dist = wait_ready(p.ws.flags, slot - 1, -1, chunk, p.ws.hdr + 1, p.ws.flags + slot, FLAG_AGG);
+        const int j0 = chunk - 1 - dist;
         // slot j0 holds an inclusive state; chunks j0+1 .. chunk-1 hold transforms
-        payload_load<KP, CPL, VIO>(S, p.ws.inc + ((int64_t)grp * p.n_chunks + j0) * slot_sz + hoff,
+        payload_load<KP, CPL>(S, p.ws.inc + ((int64_t)grp * p.n_chunks + j0) * slot_sz + hoff,
                                    p.NCP, c0);
         for (int jj = j0 + 1; jj < chunk; ++jj) {
             const float *blk = p.ws.agg + ((int64_t)grp * p.n_chunks + jj) * slot_sz + hoff;
             float Hx[KP][CPL];
-            payload_load<KP, CPL, VIO>(Hx, blk, p.NCP, c0);
-            mat_apply<KP, CPL, VIO>(S, blk, p.NCP, k, Hx, is_h);
+            payload_load<KP, CPL>(Hx, blk, p.NCP, c0);
+            mat_apply<KP, CPL, true>(S, blk, p.NCP, k, Hx, is_h);
         }
     }
     // Inclusive state after this chunk: [Abar_c | H_c] applied to S.
@@ -352,7 +347,7 @@ __global__ __launch_bounds__(64) void affine_fwd_kernel(FwdArgs p) {
 #pragma unroll
             for (int cc = 0; cc < CPL; ++cc) inc[i][cc] = S[i][cc];
         mat_apply<KP, CPL, false>(inc, s_abar + hsc * KP * KP, KP, KP, x, is_h);
-        if (slot_lane) payload_store<KP, CPL, VIO>(p.ws.inc + slot * slot_sz + hoff, p.NCP, c0, inc);
+        if (slot_lane) payload_store<KP, CPL>(p.ws.inc + slot * slot_sz + hoff, p.NCP, c0, inc);
         publish_flag(p.ws.flags + slot, FLAG_INC);
     }
 
@@ -492,15 +487,11 @@ __global__ __launch_bounds__(64) void affine_bwd_kernel(BwdArgs p) {
 #pragma unroll
         for (int cc = 0; cc < CPL; ++cc) S[i][cc] = 0.f;
     if (chunk < last) {
-        if (slot_lane) payload_store<KP, CPL, VIO>(p.ws.agg + slot * slot_sz + hoff, p.NCP, c0, z);
-        publish_flag(p.ws.flags + slot, FLAG_AGG);
-        int j0 = chunk + 1;
-        for (; j0 < last; ++j0) {
-            const uint32_t f = wait_flag(p.ws.flags + (int64_t)grp * p.n_chunks + j0, p.ws.hdr + 1);
-            if (f == FLAG_INC) break;
-        }
-        if (j0 == last) (void)wait_flag(p.ws.flags + (int64_t)grp * p.n_chunks + last, p.ws.hdr + 1);
-        payload_load<KP, CPL, VIO>(S, p.ws.inc + ((int64_t)grp * p.n_chunks + j0) * slot_sz + hoff,
+        if (slot_lane) payload_store<KP, CPL>(p.ws.agg + slot * slot_sz + hoff, p.NCP, c0, z);
+        const int dist = wait_ready(p.ws.flags, slot + 1, +1, last - chunk, p.ws.hdr + 1, p.ws.flags + slot,
+                                    FLAG_AGG);
+        const int j0 = chunk + 1 + dist;
+        payload_load<KP, CPL>(S, p.ws.inc + ((int64_t)grp * p.n_chunks + j0) * slot_sz + hoff,
                                    p.NCP, c0);
 #pragma unroll
         for (int i = 0; i < KP; ++i)
@@ -509,8 +500,8 @@ __global__ __launch_bounds__(64) void affine_bwd_kernel(BwdArgs p) {
         for (int jj = j0 - 1; jj > chunk; --jj) {
             const float *blk = p.ws.agg + ((int64_t)grp * p.n_chunks + jj) * slot_sz + hoff;
             float Yl[KP][CPL];
-            payload_load<KP, CPL, VIO>(Yl, blk, p.NCP, c0);
-            mat_apply<KP, CPL, VIO>(S, blk, p.NCP, k, Yl, is_y);
+            payload_load<KP, CPL>(Yl, blk, p.NCP, c0);
+            mat_apply<KP, CPL, true>(S, blk, p.NCP, k, Yl, is_y);
         }
     }
     {
@@ -520,7 +511,7 @@ __global__ __launch_bounds__(64) void affine_bwd_kernel(BwdArgs p) {
 #pragma unroll
             for (int cc = 0; cc < CPL; ++cc) inc[i][cc] = S[i][cc];
         mat_apply<KP, CPL, false>(inc, s_P + hsc * KP * KP, KP, KP, z, is_y);
-        if (slot_lane) payload_store<KP, CPL, VIO>(p.ws.inc + slot * slot_sz + hoff, p.NCP, c0, inc);
+        if (slot_lane) payload_store<KP, CPL>(p.ws.inc + slot * slot_sz + hoff, p.NCP, c0, inc);
         publish_flag(p.ws.flags + slot, FLAG_INC);
     }
 
@@ -632,7 +623,10 @@ __global__ __launch_bounds__(64) void affine_bwd_kernel(BwdArgs p) {
 // ---------------------------------------------------------------------------
 // Host side: tile selection and launch.
 // ---------------------------------------------------------------------------
-constexpr int LC_STEPS = 32;  // time steps per work item
+#ifndef MISCAN_AFF_LC
+#define MISCAN_AFF_LC 32
+#endif
+constexpr int LC_STEPS = MISCAN_AFF_LC;  // time steps per work item
 
 struct AffPlan {
     int KP, CPL;

@@ -98,6 +98,25 @@ __device__ __forceinline__ void store_vec(T *p, typename Pack<T, VEC>::raw_t r) 
     __builtin_nontemporal_store(r, reinterpret_cast<typename Pack<T, VEC>::raw_t *>(p));
 }
 
+// Workgroup barrier for LDS traffic only.  __syncthreads() also waits for
+// every outstanding global load of the calling wave (vmcnt(0)), which would
+// drain rows prefetched for the next work item; the kernels exchange only LDS
+// data across their barriers, so waiting for this wave's LDS operations
+// (lgkmcnt(0)) is enough.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// Makes the compiler treat a held raw row as freshly produced, so a second
+// pass over rows kept in registers re-widens them from the packed storage
+// instead of keeping a widened fp32 copy of every row alive in between.
+template <typename R>
+__device__ __forceinline__ void opaque(R &r) {
+    asm volatile("" : "+v"(r));
+}
+
 template <typename T, int VEC>
 __device__ __forceinline__ typename Pack<T, VEC>::raw_t splat(float x) {
     float f[VEC];
@@ -118,9 +137,18 @@ __device__ __forceinline__ typename Pack<T, VEC>::raw_t splat(float x) {
 // Each item publishes, per channel, first its local aggregate (flag AGG),
 // then its inclusive prefix (flag INC).  A successor walks back over its
 // predecessors' slots, folding aggregates until it meets an inclusive prefix
-// (decoupled look-back).  Payload stores are ordered before the flag store by
-// an agent-scope release; payload loads after the flag load by an agent-scope
-// acquire (both span the separate L2s of the XCDs).
+// (decoupled look-back).
+//
+// Visibility across the XCDs (each has its own L2) uses device-scope memory
+// operations only, never cache maintenance: payload words and flags are
+// written and read with agent-scope relaxed atomics, which gfx950 performs at
+// the device coherence point (the sc1 bit).  The writer waits until its
+// payload stores are acknowledged (s_waitcnt vmcnt(0)) before it stores the
+// flag; the reader's payload loads are issued only after its flag load has
+// returned a non-empty value (the branch on that value waits for it).  An
+// agent-scope release/acquire pair would add an L2 writeback on every publish
+// and an L2 invalidate on every poll, which the streaming kernels around it
+// cannot afford.
 // ---------------------------------------------------------------------------
 enum : uint32_t { FLAG_EMPTY = 0, FLAG_AGG = 1, FLAG_INC = 2 };
 
@@ -134,22 +162,78 @@ __device__ __forceinline__ uint32_t take_ticket(uint32_t *ctr) {
     return __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-__device__ __forceinline__ void publish_flag(uint32_t *flag, uint32_t v) {
-    __hip_atomic_store(flag, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+// Payload words: device-coherent stores and loads.
+__device__ __forceinline__ void carry_store(float *p, float v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float carry_load(const float *p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Spin until the slot's flag is non-empty; returns FLAG_AGG or FLAG_INC.
-__device__ __forceinline__ uint32_t wait_flag(const uint32_t *flag, uint32_t *timeouts) {
+template <int N>
+__device__ __forceinline__ void carry_store_n(float *dst, const float *src) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) carry_store(dst + i, src[i]);
+}
+template <int N>
+__device__ __forceinline__ void carry_load_n(float *dst, const float *src) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) dst[i] = carry_load(src + i);
+}
+
+// Store the flag once this lane's earlier payload stores are acknowledged.
+__device__ __forceinline__ void publish_flag(uint32_t *flag, uint32_t v) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __hip_atomic_store(flag, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Wave-cooperative look-back wait.  Predecessor d (d = 0 is the nearest) owns
+// slot slot0 + dir*d, for d < n_pred; the farthest predecessor always
+// publishes an inclusive prefix without waiting on anyone.  Lane l polls
+// predecessor base + l, so one coalesced load reads 64 flags.  Returns the
+// distance k of the nearest predecessor whose inclusive prefix is published
+// with every nearer one at least aggregate-ready: the caller then folds
+// aggregates 0..k-1 and the inclusive prefix k.
+//
+// If `pending` is non-null the caller's own flag is stored (value
+// `pending_val`) right after the first poll returns: the wait for the
+// caller's payload acknowledgements then overlaps that first round trip.
+// Every lane of the wave must call this.
+__device__ __forceinline__ int wait_ready(const uint32_t *flags, int64_t slot0, int dir, int n_pred,
+                                          uint32_t *timeouts, uint32_t *pending = nullptr,
+                                          uint32_t pending_val = 0) {
+    const int lane = threadIdx.x & 63;
+    int base = 0;
     uint32_t spins = 0;
-    uint32_t f;
-    while ((f = __hip_atomic_load(flag, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT)) == FLAG_EMPTY) {
+    while (true) {
+        const int d = base + lane;
+        const bool valid = d < n_pred;
+        uint32_t f = FLAG_EMPTY;
+        if (valid)
+            f = __hip_atomic_load(flags + slot0 + (int64_t)dir * d, __ATOMIC_RELAXED,
+                                  __HIP_MEMORY_SCOPE_AGENT);
+        const uint64_t incm = __ballot(valid && f == FLAG_INC);
+        const uint64_t empm = __ballot(valid && f == FLAG_EMPTY);
+        if (pending) {
+            publish_flag(pending, pending_val);
+            pending = nullptr;
+        }
+        const int first_inc = incm ? __builtin_ctzll(incm) : 64;
+        const int first_emp = empm ? __builtin_ctzll(empm) : 64;
+        if (first_inc < first_emp) {
+            asm volatile("" ::: "memory");  // payload loads stay after the flag loads
+            return base + first_inc;
+        }
+        if (first_emp == 64 && base + 64 < n_pred) {  // whole window ready, none inclusive
+            base += 64;
+            continue;
+        }
         __builtin_amdgcn_s_sleep(1);
         if (++spins >= SPIN_LIMIT) {
-            __hip_atomic_fetch_add(timeouts, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            return FLAG_INC;
+            if (lane == 0) __hip_atomic_fetch_add(timeouts, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            return n_pred - 1;
         }
     }
-    return f;
 }
 
 // ---------------------------------------------------------------------------
@@ -195,9 +279,119 @@ inline WsPtrs ws_ptrs(void *ws, const WsLayout &l) {
 // (a plain kernel rather than a memset node, so the pair stays capturable).
 mi_status clear_workspace(const WsPtrs &w, size_t n_slots, hipStream_t stream);
 
+// Workgroups of a persistent kernel: as many as can be resident on the
+// current device at once (they loop over tickets), never more than the work
+// items.  Residency changes nothing for correctness -- a workgroup that is not
+// yet running holds no ticket -- it only sizes the loop.
+inline size_t persistent_grid(const void *kernel, int block, size_t n_items) {
+    int dev = 0, n_cu = 0, per_cu = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, block, 0) != hipSuccess ||
+        n_cu <= 0 || per_cu <= 0) {
+        n_cu = 256;
+        per_cu = 1;
+    }
+    const size_t cap = (size_t)n_cu * (size_t)per_cu;
+    return n_items < cap ? n_items : cap;
+}
+
 inline mi_status launch_status() {
     hipError_t e = hipGetLastError();
     return e == hipSuccess ? MI_OK : MI_ERR_LAUNCH;
+}
+
+// ---------------------------------------------------------------------------
+// Workgroup-wide look-back for the channel scans.  A work item is a tile of
+// TILE channels x one time chunk, run by NT threads.  Thread t owns channels
+// t, t + NT, ... (< TILE); `c` holds this chunk's aggregate for them and `in`
+// enters as the state before the first chunk (the identity unless the scan
+// starts from a given state) and leaves as the carry-in of this chunk.
+//
+//  1. every thread stores its channels' aggregate (component-major payload,
+//     so the stores and the loads below coalesce);
+//  2. wave 0 finds the nearest predecessor with a published inclusive prefix
+//     (wait_ready), publishing this chunk's aggregate flag on the way;
+//  3. every thread folds the k aggregates and the inclusive prefix of its
+//     channels, issuing up to 8 predecessors' loads at a time -- so the walk
+//     costs one round trip rather than one per predecessor;
+//  4. every thread stores its channels' inclusive prefix in (+) c.
+// The caller then stages `in` in LDS and calls wg_publish_inc.
+//
+// Op describes the carry algebra: NC floats per channel, and
+// then(r, x, y): r = x followed by y (x is applied to the state first).
+// ---------------------------------------------------------------------------
+template <class Op, int TILE, int NT>
+__device__ __forceinline__ void wg_lookback(const WsPtrs &ws, int64_t slot, int dir, int n_pred,
+                                            const float (&c)[(TILE + NT - 1) / NT][Op::NC],
+                                            float (&in)[(TILE + NT - 1) / NT][Op::NC], int *s_k) {
+    constexpr int NC = Op::NC, CPT = (TILE + NT - 1) / NT, BATCH = 8;
+    const int tid = threadIdx.x;
+    const int64_t pay = (int64_t)NC * TILE;  // payload floats per slot
+    if (n_pred > 0) {
+#pragma unroll
+        for (int q = 0; q < CPT; ++q) {
+            const int ch = tid + q * NT;
+            if (ch < TILE)
+#pragma unroll
+                for (int m = 0; m < NC; ++m) carry_store(ws.agg + slot * pay + m * TILE + ch, c[q][m]);
+        }
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // every wave's aggregate is acknowledged
+        lds_barrier();
+        if (tid < 64) {
+            const int k = wait_ready(ws.flags, slot + dir, dir, n_pred, ws.hdr + 1, ws.flags + slot, FLAG_AGG);
+            if (tid == 0) *s_k = k;
+        }
+        lds_barrier();
+        const int k = *s_k;
+        for (int j0 = 0; j0 <= k; j0 += BATCH) {
+            float x[BATCH][CPT][NC];
+#pragma unroll
+            for (int u = 0; u < BATCH; ++u) {
+                const int j = j0 + u;
+                if (j <= k) {
+                    const float *src = (j == k ? ws.inc : ws.agg) + (slot + (int64_t)dir * (j + 1)) * pay;
+#pragma unroll
+                    for (int q = 0; q < CPT; ++q) {
+                        const int ch = tid + q * NT;
+#pragma unroll
+                        for (int m = 0; m < NC; ++m) x[u][q][m] = ch < TILE ? carry_load(src + m * TILE + ch) : 0.f;
+                    }
+                }
+            }
+#pragma unroll
+            for (int u = 0; u < BATCH; ++u) {
+                if (j0 + u <= k) {
+#pragma unroll
+                    for (int q = 0; q < CPT; ++q) {
+                        float r[NC];
+                        Op::then(r, x[u][q], in[q]);  // predecessor j comes before all folded so far
+#pragma unroll
+                        for (int m = 0; m < NC; ++m) in[q][m] = r[m];
+                    }
+                }
+            }
+        }
+    }
+#pragma unroll
+    for (int q = 0; q < CPT; ++q) {
+        const int ch = tid + q * NT;
+        if (ch < TILE) {
+            float r[NC];
+            Op::then(r, in[q], c[q]);
+#pragma unroll
+            for (int m = 0; m < NC; ++m) carry_store(ws.inc + slot * pay + m * TILE + ch, r[m]);
+        }
+    }
+}
+
+// Publish the chunk's inclusive prefix once every wave's payload stores are
+// acknowledged; the barrier also makes the caller's staged LDS carry visible.
+__device__ __forceinline__ void wg_publish_inc(const WsPtrs &ws, int64_t slot) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    lds_barrier();
+    if (threadIdx.x < 64)
+        __hip_atomic_store(ws.flags + slot, (uint32_t)FLAG_INC, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 }  // namespace miscan

@@ -41,92 +41,101 @@ struct BwdArgs {
     WsPtrs ws;
 };
 
-template <int N>
-__device__ __forceinline__ void store_floats(float *dst, const float *src) {
-    if constexpr (N % 4 == 0) {
-#pragma unroll
-        for (int i = 0; i < N; i += 4) {
-            f32x4 v = {src[i], src[i + 1], src[i + 2], src[i + 3]};
-            *reinterpret_cast<f32x4 *>(dst + i) = v;
-        }
-    } else if constexpr (N % 2 == 0) {
-#pragma unroll
-        for (int i = 0; i < N; i += 2) {
-            f32x2 v = {src[i], src[i + 1]};
-            *reinterpret_cast<f32x2 *>(dst + i) = v;
-        }
-    } else {
-#pragma unroll
-        for (int i = 0; i < N; ++i) dst[i] = src[i];
+// Carry algebra of the forward scan per channel: (A, h) maps a state h_in to
+// A*h_in + h.  then(x, y) = x followed by y = (y.A*x.A, y.A*x.h + y.h).
+struct FwdOp {
+    static constexpr int NC = 2;
+    static __device__ __forceinline__ void then(float (&r)[2], const float (&x)[2], const float (&y)[2]) {
+        r[0] = y[0] * x[0];
+        r[1] = fmaf(y[0], x[1], y[1]);
     }
+};
+
+// Carry algebra of the reverse scan per channel: (P, l, m) maps the adjoint
+// state (lam, mu) entering from later time to (P*lam + l, P*mu + m).
+// then(x, y) = x (later in time, applied first) followed by y.
+struct BwdOp {
+    static constexpr int NC = 3;
+    static __device__ __forceinline__ void then(float (&r)[3], const float (&x)[3], const float (&y)[3]) {
+        r[0] = y[0] * x[0];
+        r[1] = fmaf(y[0], x[1], y[1]);
+        r[2] = fmaf(y[0], x[2], y[2]);
+    }
+};
+
+struct Item {
+    int chunk, tile;
+    int64_t t0;    // first row of this wave
+    int64_t base;  // element offset of (b, t0, d) for this lane
+    bool lane_ok;  // this lane's channels exist
+};
+
+// Work item of a ticket.  Tickets run chunk-major in scan order: every tile's
+// first chunk (in time for the forward, the last one for the reverse scan)
+// before any tile's second.
+template <int VEC, int L, int NW>
+__device__ __forceinline__ Item decode_item(uint32_t ticket, int n_tiles, int n_dtiles, int64_t T,
+                                            int64_t D, int lane, int wave, bool reverse, int n_chunks) {
+    constexpr int TILE = 64 * VEC;
+    Item it;
+    const int ord = (int)ticket / n_tiles;
+    it.tile = (int)ticket - ord * n_tiles;
+    it.chunk = reverse ? n_chunks - 1 - ord : ord;
+    const int bidx = it.tile / n_dtiles;
+    const int dtile = it.tile - bidx * n_dtiles;
+    const int64_t d = (int64_t)dtile * TILE + (int64_t)lane * VEC;
+    it.lane_ok = d < D;
+    it.t0 = (int64_t)it.chunk * (NW * L) + (int64_t)wave * L;
+    it.base = ((int64_t)bidx * T + it.t0) * D + d;
+    return it;
 }
 
-template <int N>
-__device__ __forceinline__ void load_floats(float *dst, const float *src) {
-    if constexpr (N % 4 == 0) {
-#pragma unroll
-        for (int i = 0; i < N; i += 4) {
-            f32x4 v = *reinterpret_cast<const f32x4 *>(src + i);
-            dst[i] = v.x; dst[i + 1] = v.y; dst[i + 2] = v.z; dst[i + 3] = v.w;
-        }
-    } else if constexpr (N % 2 == 0) {
-#pragma unroll
-        for (int i = 0; i < N; i += 2) {
-            f32x2 v = *reinterpret_cast<const f32x2 *>(src + i);
-            dst[i] = v.x; dst[i + 1] = v.y;
-        }
-    } else {
-#pragma unroll
-        for (int i = 0; i < N; ++i) dst[i] = src[i];
-    }
+// Row r of a tensor at element offset base + shift*D, or `fill` when the row
+// is outside [0, T) or the lane is past D.  Branch-free: an invalid row is
+// loaded from the tensor's first vector and then replaced, so a wave's loads
+// form one straight run.
+template <typename T, int VEC>
+__device__ __forceinline__ typename Pack<T, VEC>::raw_t row_or(const void *base_ptr, bool ok, int64_t off,
+                                                             typename Pack<T, VEC>::raw_t fill) {
+    const typename Pack<T, VEC>::raw_t x = load_vec<T, VEC>(static_cast<const T *>(base_ptr) + (ok ? off : 0));
+    return ok ? x : fill;
 }
 
 // ---------------------------------------------------------------------------
-// Forward.  Per channel the segment transform is (A, h): h_out = A*h_in + h.
-// Composition, earlier segment 1 then later segment 2:
-//     (A1, h1) then (A2, h2) = (A2*A1, A2*h1 + h2).
+// Forward.  One workgroup = one work item (a tile x a time chunk): each wave
+// scans its L rows in registers, the wave aggregates meet in LDS, the whole
+// workgroup runs the look-back (wg_lookback), and each wave rescans its rows
+// from its carry-in and stores A_t, Bc_t.
 // ---------------------------------------------------------------------------
 template <typename T, int VEC, int L, int NW>
 __global__ __launch_bounds__(NW * 64) void linear_fwd_kernel(FwdArgs p) {
     using PK = Pack<T, VEC>;
     using raw_t = typename PK::raw_t;
-    constexpr int TILE = 64 * VEC;
-    constexpr int CHUNK = NW * L;
-    constexpr int NV = 2 * VEC;  // payload floats per lane: A[VEC], h[VEC]
+    constexpr int TILE = 64 * VEC, NT = NW * 64, CPT = (TILE + NT - 1) / NT;
 
-    __shared__ float s_A[NW][TILE];
+    __shared__ float s_A[NW][TILE];  // wave aggregates
     __shared__ float s_H[NW][TILE];
-    __shared__ float s_cA[TILE];
+    __shared__ float s_cA[TILE];     // chunk carry-in
     __shared__ float s_cH[TILE];
     __shared__ uint32_t s_ticket;
+    __shared__ int s_k;
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     if (threadIdx.x == 0) s_ticket = take_ticket(p.ws.hdr);
     __syncthreads();
-    const int ticket = (int)s_ticket;
-    const int chunk = ticket / p.n_tiles;
-    const int tile = ticket - chunk * p.n_tiles;
-    const int bidx = tile / p.n_dtiles;
-    const int dtile = tile - bidx * p.n_dtiles;
+    const Item it = decode_item<VEC, L, NW>(s_ticket, p.n_tiles, p.n_dtiles, p.T, p.D, lane, wave, false,
+                                            p.n_chunks);
 
-    const int64_t d = (int64_t)dtile * TILE + (int64_t)lane * VEC;
-    const bool lane_ok = d < p.D;
-    const int64_t t0 = (int64_t)chunk * CHUNK + (int64_t)wave * L;
-    const int64_t base = ((int64_t)bidx * p.T + t0) * p.D + d;
-    const T *a = static_cast<const T *>(p.a) + base;
-    const T *b = static_cast<const T *>(p.b) + base;
-
-    // 1. Load this wave's L rows (identity step (1, 0) past T or past D).
+    // 1. Load this wave's rows (identity step (1, 0) past T or D).
     raw_t ra[L], rb[L];
+    {
+        const raw_t one = splat<T, VEC>(1.f), zero = splat<T, VEC>(0.f);
 #pragma unroll
-    for (int r = 0; r < L; ++r) {
-        if (lane_ok && t0 + r < p.T) {
-            ra[r] = load_vec<T, VEC>(a + r * p.D);
-            rb[r] = load_vec<T, VEC>(b + r * p.D);
-        } else {
-            ra[r] = splat<T, VEC>(1.f);
-            rb[r] = splat<T, VEC>(0.f);
+        for (int r = 0; r < L; ++r) {
+            const bool ok = it.lane_ok && it.t0 + r < p.T;
+            ra[r] = row_or<T, VEC>(p.a, ok, it.base + r * p.D, one);
+            rb[r] = row_or<T, VEC>(p.b, ok, it.base + r * p.D, zero);
         }
     }
 
@@ -150,59 +159,33 @@ __global__ __launch_bounds__(NW * 64) void linear_fwd_kernel(FwdArgs p) {
         s_A[wave][lane * VEC + v] = gA[v];
         s_H[wave][lane * VEC + v] = gH[v];
     }
-    __syncthreads();
+    lds_barrier();
 
-    // 3. Wave 0: chunk aggregate, publish, look back, publish inclusive prefix.
-    if (wave == 0) {
-        float c[NV];  // chunk aggregate: c[0..VEC) = A, c[VEC..2VEC) = h
+    // 3. Chunk aggregate per channel (waves in time order), look-back, carry.
+    const int64_t slot = (int64_t)it.tile * p.n_chunks + it.chunk;
+    {
+        float c[CPT][2], in[CPT][2];
 #pragma unroll
-        for (int v = 0; v < VEC; ++v) { c[v] = 1.f; c[VEC + v] = 0.f; }
-        for (int w = 0; w < NW; ++w) {
-#pragma unroll
-            for (int v = 0; v < VEC; ++v) {
-                const float xA = s_A[w][lane * VEC + v], xH = s_H[w][lane * VEC + v];
-                c[VEC + v] = fmaf(xA, c[VEC + v], xH);
-                c[v] = xA * c[v];
-            }
-        }
-        float in[NV];  // carry-in = inclusive prefix of all earlier chunks
-#pragma unroll
-        for (int v = 0; v < VEC; ++v) { in[v] = 1.f; in[VEC + v] = 0.f; }
-        const int64_t slot = (int64_t)tile * p.n_chunks + chunk;
-        const int64_t lane_off = (int64_t)lane * NV;
-        if (chunk > 0) {
-            store_floats<NV>(p.ws.agg + slot * (64 * NV) + lane_off, c);
-            publish_flag(p.ws.flags + slot, FLAG_AGG);
-            for (int j = chunk - 1; j >= 0; --j) {
-                const int64_t sj = (int64_t)tile * p.n_chunks + j;
-                const uint32_t f = wait_flag(p.ws.flags + sj, p.ws.hdr + 1);
-                const float *src = (f == FLAG_INC ? p.ws.inc : p.ws.agg) + sj * (64 * NV) + lane_off;
-                float x[NV];
-                load_floats<NV>(x, src);
-                // slot j comes before everything folded so far
-#pragma unroll
-                for (int v = 0; v < VEC; ++v) {
-                    in[VEC + v] = fmaf(in[v], x[VEC + v], in[VEC + v]);
-                    in[v] = in[v] * x[v];
+        for (int q = 0; q < CPT; ++q) {
+            const int ch = threadIdx.x + q * NT;
+            c[q][0] = 1.f; c[q][1] = 0.f;
+            in[q][0] = 1.f; in[q][1] = 0.f;
+            if (ch < TILE)
+                for (int w = 0; w < NW; ++w) {
+                    const float x[2] = {s_A[w][ch], s_H[w][ch]};
+                    float r[2];
+                    FwdOp::then(r, c[q], x);
+                    c[q][0] = r[0]; c[q][1] = r[1];
                 }
-                if (f == FLAG_INC) break;
-            }
         }
-        float inc[NV];
+        wg_lookback<FwdOp, TILE, NT>(p.ws, slot, -1, it.chunk, c, in, &s_k);
 #pragma unroll
-        for (int v = 0; v < VEC; ++v) {
-            inc[v] = c[v] * in[v];
-            inc[VEC + v] = fmaf(c[v], in[VEC + v], c[VEC + v]);
+        for (int q = 0; q < CPT; ++q) {
+            const int ch = threadIdx.x + q * NT;
+            if (ch < TILE) { s_cA[ch] = in[q][0]; s_cH[ch] = in[q][1]; }
         }
-        store_floats<NV>(p.ws.inc + slot * (64 * NV) + lane_off, inc);
-        publish_flag(p.ws.flags + slot, FLAG_INC);
-#pragma unroll
-        for (int v = 0; v < VEC; ++v) {
-            s_cA[lane * VEC + v] = in[v];
-            s_cH[lane * VEC + v] = in[VEC + v];
-        }
+        wg_publish_inc(p.ws, slot);
     }
-    __syncthreads();
 
     // 4. Carry into this wave: chunk carry-in, then waves 0..wave-1.
     float hA[VEC], hH[VEC];
@@ -218,12 +201,14 @@ __global__ __launch_bounds__(NW * 64) void linear_fwd_kernel(FwdArgs p) {
     }
 
     // 5. Rescan the rows from registers and store A_t, Bc_t.
-    if (!lane_ok) return;
-    T *Ao = static_cast<T *>(p.A) + base;
-    T *Bo = static_cast<T *>(p.Bc) + base;
+    if (!it.lane_ok) return;
+#pragma unroll
+    for (int r = 0; r < L; ++r) { opaque(ra[r]); opaque(rb[r]); }
+    T *Ao = static_cast<T *>(p.A) + it.base;
+    T *Bo = static_cast<T *>(p.Bc) + it.base;
 #pragma unroll
     for (int r = 0; r < L; ++r) {
-        if (t0 + r < p.T) {
+        if (it.t0 + r < p.T) {
             float fa[VEC], fb[VEC];
             PK::unpack(ra[r], fa);
             PK::unpack(rb[r], fb);
@@ -242,59 +227,45 @@ __global__ __launch_bounds__(NW * 64) void linear_fwd_kernel(FwdArgs p) {
 // Backward.  Reverse time with c_t = a_{t+1} (c_T = 0):
 //     lam_t = gBc_t + c_t lam_{t+1},  mu_t = gA_t + c_t mu_{t+1},
 //     db_t = lam_t,  da_t = lam_t Bc_{t-1} + mu_t A_{t-1}  (A_0 = 1, Bc_0 = 0).
-// A reverse segment is (P, l, m): lam_out = P*lam_in + l, mu_out = P*mu_in + m.
-// Applying later segment 2 first, then earlier segment 1:
-//     (P1*P2, P1*l2 + l1, P1*m2 + m1).
+// Same work-item structure as the forward, with chunks taken from the end of
+// time backwards and each wave scanning its rows from the last one.
 // ---------------------------------------------------------------------------
 template <typename T, int VEC, int L, int NW>
 __global__ __launch_bounds__(NW * 64) void linear_bwd_kernel(BwdArgs p) {
     using PK = Pack<T, VEC>;
     using raw_t = typename PK::raw_t;
-    constexpr int TILE = 64 * VEC;
-    constexpr int CHUNK = NW * L;
-    constexpr int NV = 3 * VEC;  // payload floats per lane: P[VEC], lam[VEC], mu[VEC]
+    constexpr int TILE = 64 * VEC, NT = NW * 64, CPT = (TILE + NT - 1) / NT;
 
     __shared__ float s_P[NW][TILE];
     __shared__ float s_L[NW][TILE];
     __shared__ float s_M[NW][TILE];
-    __shared__ float s_cP[TILE];
     __shared__ float s_cL[TILE];
     __shared__ float s_cM[TILE];
     __shared__ uint32_t s_ticket;
+    __shared__ int s_k;
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
     if (threadIdx.x == 0) s_ticket = take_ticket(p.ws.hdr);
     __syncthreads();
-    const int ticket = (int)s_ticket;
-    const int rchunk = ticket / p.n_tiles;  // 0 = last chunk in time
-    const int tile = ticket - rchunk * p.n_tiles;
-    const int chunk = p.n_chunks - 1 - rchunk;
-    const int bidx = tile / p.n_dtiles;
-    const int dtile = tile - bidx * p.n_dtiles;
-
-    const int64_t d = (int64_t)dtile * TILE + (int64_t)lane * VEC;
-    const bool lane_ok = d < p.D;
-    const int64_t t0 = (int64_t)chunk * CHUNK + (int64_t)wave * L;
-    const int64_t base = ((int64_t)bidx * p.T + t0) * p.D + d;
-    const T *a = static_cast<const T *>(p.a) + base;
-    const T *Ai = static_cast<const T *>(p.A) + base;
-    const T *Bci = static_cast<const T *>(p.Bc) + base;
-    const T *gA = static_cast<const T *>(p.gA) + base;
-    const T *gB = static_cast<const T *>(p.gBc) + base;
+    const Item it = decode_item<VEC, L, NW>(s_ticket, p.n_tiles, p.n_dtiles, p.T, p.D, lane, wave, true,
+                                            p.n_chunks);
 
     // 1. Loads.  Row r is time t = t0 + r.  c = a_{t+1}; Ap = A_{t-1}; Bp = Bc_{t-1}.
     raw_t rc[L], rgA[L], rgB[L], rAp[L], rBp[L];
+    {
+        const raw_t one = splat<T, VEC>(1.f), zero = splat<T, VEC>(0.f);
 #pragma unroll
-    for (int r = 0; r < L; ++r) {
-        const int64_t t = t0 + r;
-        const bool ok = lane_ok && t < p.T;
-        rc[r] = (ok && t + 1 < p.T) ? load_vec<T, VEC>(a + (r + 1) * p.D)
-                                    : splat<T, VEC>(ok ? 0.f : 1.f);
-        rgA[r] = ok ? load_vec<T, VEC>(gA + r * p.D) : splat<T, VEC>(0.f);
-        rgB[r] = ok ? load_vec<T, VEC>(gB + r * p.D) : splat<T, VEC>(0.f);
-        rAp[r] = (ok && t > 0) ? load_vec<T, VEC>(Ai + (r - 1) * p.D) : splat<T, VEC>(1.f);
-        rBp[r] = (ok && t > 0) ? load_vec<T, VEC>(Bci + (r - 1) * p.D) : splat<T, VEC>(0.f);
+        for (int r = 0; r < L; ++r) {
+            const int64_t t = it.t0 + r;
+            const bool ok = it.lane_ok && t < p.T;
+            const int64_t off = it.base + r * p.D;
+            rc[r] = row_or<T, VEC>(p.a, ok && t + 1 < p.T, off + p.D, ok ? zero : one);
+            rgA[r] = row_or<T, VEC>(p.gA, ok, off, zero);
+            rgB[r] = row_or<T, VEC>(p.gBc, ok, off, zero);
+            rAp[r] = row_or<T, VEC>(p.A, ok && t > 0, off - p.D, one);
+            rBp[r] = row_or<T, VEC>(p.Bc, ok && t > 0, off - p.D, zero);
+        }
     }
 
     // 2. Reverse serial scan of the wave's rows: the wave aggregate.
@@ -320,92 +291,55 @@ __global__ __launch_bounds__(NW * 64) void linear_bwd_kernel(BwdArgs p) {
         s_L[wave][lane * VEC + v] = gL[v];
         s_M[wave][lane * VEC + v] = gM[v];
     }
-    __syncthreads();
+    lds_barrier();
 
-    // 3. Wave 0: chunk aggregate (waves NW-1 .. 0), publish, look back over
-    //    later chunks, publish the inclusive suffix.
-    if (wave == 0) {
-        float c[NV];
-#pragma unroll
-        for (int v = 0; v < VEC; ++v) { c[v] = 1.f; c[VEC + v] = 0.f; c[2 * VEC + v] = 0.f; }
-        for (int w = NW - 1; w >= 0; --w) {
-#pragma unroll
-            for (int v = 0; v < VEC; ++v) {
-                const int i = lane * VEC + v;
-                const float xP = s_P[w][i], xL = s_L[w][i], xM = s_M[w][i];
-                c[VEC + v] = fmaf(xP, c[VEC + v], xL);
-                c[2 * VEC + v] = fmaf(xP, c[2 * VEC + v], xM);
-                c[v] = xP * c[v];
-            }
-        }
-        float in[NV];
-#pragma unroll
-        for (int v = 0; v < VEC; ++v) { in[v] = 1.f; in[VEC + v] = 0.f; in[2 * VEC + v] = 0.f; }
-        const int64_t slot = (int64_t)tile * p.n_chunks + chunk;
-        const int64_t lane_off = (int64_t)lane * NV;
-        if (chunk < p.n_chunks - 1) {
-            store_floats<NV>(p.ws.agg + slot * (64 * NV) + lane_off, c);
-            publish_flag(p.ws.flags + slot, FLAG_AGG);
-            for (int j = chunk + 1; j < p.n_chunks; ++j) {
-                const int64_t sj = (int64_t)tile * p.n_chunks + j;
-                const uint32_t f = wait_flag(p.ws.flags + sj, p.ws.hdr + 1);
-                const float *src = (f == FLAG_INC ? p.ws.inc : p.ws.agg) + sj * (64 * NV) + lane_off;
-                float x[NV];
-                load_floats<NV>(x, src);
-                // slot j is applied before everything folded so far
-#pragma unroll
-                for (int v = 0; v < VEC; ++v) {
-                    in[VEC + v] = fmaf(in[v], x[VEC + v], in[VEC + v]);
-                    in[2 * VEC + v] = fmaf(in[v], x[2 * VEC + v], in[2 * VEC + v]);
-                    in[v] = in[v] * x[v];
-                }
-                if (f == FLAG_INC) break;
-            }
-        }
-        float inc[NV];
-#pragma unroll
-        for (int v = 0; v < VEC; ++v) {
-            inc[v] = c[v] * in[v];
-            inc[VEC + v] = fmaf(c[v], in[VEC + v], c[VEC + v]);
-            inc[2 * VEC + v] = fmaf(c[v], in[2 * VEC + v], c[2 * VEC + v]);
-        }
-        store_floats<NV>(p.ws.inc + slot * (64 * NV) + lane_off, inc);
-        publish_flag(p.ws.flags + slot, FLAG_INC);
-#pragma unroll
-        for (int v = 0; v < VEC; ++v) {
-            s_cP[lane * VEC + v] = in[v];
-            s_cL[lane * VEC + v] = in[VEC + v];
-            s_cM[lane * VEC + v] = in[2 * VEC + v];
-        }
-    }
-    __syncthreads();
-
-    // 4. Carry into this wave: chunk carry-in, then waves NW-1 .. wave+1.
-    float lam[VEC], mu[VEC];
+    // 3. Chunk aggregate per channel (waves NW-1 .. 0), look-back over later
+    //    chunks, carry.
+    const int64_t slot = (int64_t)it.tile * p.n_chunks + it.chunk;
     {
-        float cP[VEC];
+        float c[CPT][3], in[CPT][3];
+#pragma unroll
+        for (int q = 0; q < CPT; ++q) {
+            const int ch = threadIdx.x + q * NT;
+            c[q][0] = 1.f; c[q][1] = 0.f; c[q][2] = 0.f;
+            in[q][0] = 1.f; in[q][1] = 0.f; in[q][2] = 0.f;
+            if (ch < TILE)
+                for (int w = NW - 1; w >= 0; --w) {
+                    const float x[3] = {s_P[w][ch], s_L[w][ch], s_M[w][ch]};
+                    float r[3];
+                    BwdOp::then(r, c[q], x);
+                    c[q][0] = r[0]; c[q][1] = r[1]; c[q][2] = r[2];
+                }
+        }
+        wg_lookback<BwdOp, TILE, NT>(p.ws, slot, +1, p.n_chunks - 1 - it.chunk, c, in, &s_k);
+#pragma unroll
+        for (int q = 0; q < CPT; ++q) {
+            const int ch = threadIdx.x + q * NT;
+            if (ch < TILE) { s_cL[ch] = in[q][1]; s_cM[ch] = in[q][2]; }
+        }
+        wg_publish_inc(p.ws, slot);
+    }
+
+    // 4. Adjoint state entering this wave: chunk carry-in, then waves NW-1 .. wave+1.
+    float lam[VEC], mu[VEC];
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) { lam[v] = s_cL[lane * VEC + v]; mu[v] = s_cM[lane * VEC + v]; }
+    for (int w = NW - 1; w > wave; --w) {
 #pragma unroll
         for (int v = 0; v < VEC; ++v) {
-            cP[v] = s_cP[lane * VEC + v];
-            lam[v] = s_cL[lane * VEC + v];
-            mu[v] = s_cM[lane * VEC + v];
-        }
-        for (int w = NW - 1; w > wave; --w) {
-#pragma unroll
-            for (int v = 0; v < VEC; ++v) {
-                const int i = lane * VEC + v;
-                const float xP = s_P[w][i];
-                lam[v] = fmaf(xP, lam[v], s_L[w][i]);
-                mu[v] = fmaf(xP, mu[v], s_M[w][i]);
-                cP[v] = xP * cP[v];
-            }
+            const int i = lane * VEC + v;
+            const float xP = s_P[w][i];
+            lam[v] = fmaf(xP, lam[v], s_L[w][i]);
+            mu[v] = fmaf(xP, mu[v], s_M[w][i]);
         }
     }
 
     // 5. Reverse rescan from registers; store da_t, db_t.
-    if (!lane_ok) return;
-    T *dao = static_cast<T *>(p.da) + base;
-    T *dbo = static_cast<T *>(p.db) + base;
+    if (!it.lane_ok) return;
+#pragma unroll
+    for (int r = 0; r < L; ++r) { opaque(rc[r]); opaque(rgA[r]); opaque(rgB[r]); }
+    T *dao = static_cast<T *>(p.da) + it.base;
+    T *dbo = static_cast<T *>(p.db) + it.base;
 #pragma unroll
     for (int r = L - 1; r >= 0; --r) {
         float fc[VEC], fgA[VEC], fgB[VEC];
@@ -417,7 +351,7 @@ __global__ __launch_bounds__(NW * 64) void linear_bwd_kernel(BwdArgs p) {
             lam[v] = fmaf(fc[v], lam[v], fgB[v]);
             mu[v] = fmaf(fc[v], mu[v], fgA[v]);
         }
-        if (t0 + r < p.T) {
+        if (it.t0 + r < p.T) {
             float fAp[VEC], fBp[VEC], da[VEC];
             PK::unpack(rAp[r], fAp);
             PK::unpack(rBp[r], fBp);
@@ -433,8 +367,24 @@ __global__ __launch_bounds__(NW * 64) void linear_bwd_kernel(BwdArgs p) {
 // Tile shapes.  VEC elements per lane (16-byte accesses when VEC*sizeof(T) is
 // 16), L rows per wave held in registers, NW waves per workgroup.
 // ---------------------------------------------------------------------------
-template <typename T, int VEC> struct FwdShape { static constexpr int L = 8, NW = 8; };
-template <typename T, int VEC> struct BwdShape { static constexpr int L = 4, NW = 8; };
+#ifndef MISCAN_LIN_FWD_L
+#define MISCAN_LIN_FWD_L 8
+#endif
+#ifndef MISCAN_LIN_FWD_NW
+#define MISCAN_LIN_FWD_NW 8
+#endif
+#ifndef MISCAN_LIN_BWD_L
+#define MISCAN_LIN_BWD_L 8
+#endif
+#ifndef MISCAN_LIN_BWD_NW
+#define MISCAN_LIN_BWD_NW 8
+#endif
+template <typename T, int VEC> struct FwdShape {
+    static constexpr int L = MISCAN_LIN_FWD_L, NW = MISCAN_LIN_FWD_NW;
+};
+template <typename T, int VEC> struct BwdShape {
+    static constexpr int L = MISCAN_LIN_BWD_L, NW = MISCAN_LIN_BWD_NW;
+};
 
 struct Grid {
     int n_dtiles, n_tiles, n_chunks;
@@ -481,8 +431,7 @@ mi_status run_fwd(const void *a, const void *b, void *A, void *Bc, int64_t B, in
     p.ws = ws_ptrs(ws, lay);
     mi_status st = clear_workspace(p.ws, g.n_slots, s);
     if (st != MI_OK) return st;
-    hipLaunchKernelGGL((linear_fwd_kernel<E, VEC, L, NW>), dim3((unsigned)g.n_slots),
-                       dim3(NW * 64), 0, s, p);
+    hipLaunchKernelGGL((linear_fwd_kernel<E, VEC, L, NW>), dim3((unsigned)g.n_slots), dim3(NW * 64), 0, s, p);
     return launch_status();
 }
 

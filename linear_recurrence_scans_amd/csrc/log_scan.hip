@@ -46,30 +46,29 @@ struct LogArgs {
     WsPtrs ws;
 };
 
-template <int N>
-__device__ __forceinline__ void st_f(float *dst, const float *src) {
-#pragma unroll
-    for (int i = 0; i < N; ++i) dst[i] = src[i];
-}
-template <int N>
-__device__ __forceinline__ void ld_f(float *dst, const float *src) {
-#pragma unroll
-    for (int i = 0; i < N; ++i) dst[i] = src[i];
-}
+// Carry algebra per channel: (la, lh) maps a log-state x to lae(la + x, lh).
+// then(x, y) = x followed by y = (x.la + y.la, lae(y.la + x.lh, y.lh)).
+struct LogOp {
+    static constexpr int NC = 2;
+    static __device__ __forceinline__ void then(float (&r)[2], const float (&x)[2], const float (&y)[2]) {
+        r[0] = x[0] + y[0];
+        r[1] = lae2(y[0] + x[1], y[1]);
+    }
+};
 
 template <typename T, int VEC, int L, int NW>
 __global__ __launch_bounds__(NW * 64) void log_fwd_kernel(LogArgs p) {
     using PK = Pack<T, VEC>;
     using raw_t = typename PK::raw_t;
-    constexpr int TILE = 64 * VEC;
+    constexpr int TILE = 64 * VEC, NT = NW * 64, CPT = (TILE + NT - 1) / NT;
     constexpr int CHUNK = NW * L;
-    constexpr int NV = 2 * VEC;  // payload per lane: la[VEC], lh[VEC]
     const float NEG_INF = -__builtin_inff();
 
     __shared__ float s_la[NW][TILE];
     __shared__ float s_lh[NW][TILE];
     __shared__ float s_c[TILE];
     __shared__ uint32_t s_ticket;
+    __shared__ int s_k;
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -85,19 +84,22 @@ __global__ __launch_bounds__(NW * 64) void log_fwd_kernel(LogArgs p) {
     const bool lane_ok = d < p.D;
     const int64_t t0 = (int64_t)chunk * CHUNK + (int64_t)wave * L;
     // log_coeffs row t pairs with log_values row t + 1.
-    const T *lc = static_cast<const T *>(p.lc) + ((int64_t)bidx * p.T + t0) * p.D + d;
-    const T *lv = static_cast<const T *>(p.lv) + ((int64_t)bidx * (p.T + 1) + t0 + 1) * p.D + d;
+    const int64_t lc_base = ((int64_t)bidx * p.T + t0) * p.D + d;
+    const int64_t lv_base = ((int64_t)bidx * (p.T + 1) + t0 + 1) * p.D + d;
 
-    // 1. Loads; identity step past T or D is (lc, lv) = (0, -inf).
+    // 1. Loads; identity step past T or D is (lc, lv) = (0, -inf).  Branch
+    //    free: invalid rows read the tensor's first vector and are replaced.
     raw_t rlc[L], rlv[L];
+    {
+        const raw_t zero = splat<T, VEC>(0.f), ninf = splat<T, VEC>(NEG_INF);
+        const T *lc0 = static_cast<const T *>(p.lc), *lv0 = static_cast<const T *>(p.lv);
 #pragma unroll
-    for (int r = 0; r < L; ++r) {
-        if (lane_ok && t0 + r < p.T) {
-            rlc[r] = load_vec<T, VEC>(lc + r * p.D);
-            rlv[r] = load_vec<T, VEC>(lv + r * p.D);
-        } else {
-            rlc[r] = splat<T, VEC>(0.f);
-            rlv[r] = splat<T, VEC>(NEG_INF);
+        for (int r = 0; r < L; ++r) {
+            const bool ok = lane_ok && t0 + r < p.T;
+            const raw_t xc = load_vec<T, VEC>(lc0 + (ok ? lc_base + r * p.D : 0));
+            const raw_t xv = load_vec<T, VEC>(lv0 + (ok ? lv_base + r * p.D : 0));
+            rlc[r] = ok ? xc : zero;
+            rlv[r] = ok ? xv : ninf;
         }
     }
 
@@ -122,68 +124,42 @@ __global__ __launch_bounds__(NW * 64) void log_fwd_kernel(LogArgs p) {
         s_la[wave][lane * VEC + v] = ga[v];
         s_lh[wave][lane * VEC + v] = gh[v];
     }
-    __syncthreads();
+    lds_barrier();
 
-    // 3. Wave 0: chunk aggregate, publish, look back, publish inclusive state.
-    if (wave == 0) {
-        float c[NV];
+    // 3. Chunk aggregate per channel, look-back, carry.  Before the first
+    //    chunk the state is log h_0 (log_values slot 0).
+    const int64_t slot = (int64_t)tile * p.n_chunks + chunk;
+    {
+        float c[CPT][2], in[CPT][2];
+        const int64_t d_tile = (int64_t)dtile * TILE;
 #pragma unroll
-        for (int v = 0; v < VEC; ++v) { c[v] = 0.f; c[VEC + v] = NEG_INF; }
-        for (int w = 0; w < NW; ++w) {
-#pragma unroll
-            for (int v = 0; v < VEC; ++v) {
-                const float xa = s_la[w][lane * VEC + v], xh = s_lh[w][lane * VEC + v];
-                c[VEC + v] = lae2(xa + c[VEC + v], xh);
-                c[v] += xa;
-            }
-        }
-        float in[NV];
-        const int64_t slot = (int64_t)tile * p.n_chunks + chunk;
-        const int64_t lane_off = (int64_t)lane * NV;
-        if (chunk == 0) {
-            // The state before step 1 is log h_0 (log_values slot 0).
-            float f0[VEC];
-            if (lane_ok) {
-                PK::unpack(load_vec<T, VEC>(static_cast<const T *>(p.lv) +
-                                            (int64_t)bidx * (p.T + 1) * p.D + d), f0);
-            } else {
-#pragma unroll
-                for (int v = 0; v < VEC; ++v) f0[v] = NEG_INF;
-            }
-#pragma unroll
-            for (int v = 0; v < VEC; ++v) { in[v] = 0.f; in[VEC + v] = f0[v] * LOG2E; }
-        } else {
-#pragma unroll
-            for (int v = 0; v < VEC; ++v) { in[v] = 0.f; in[VEC + v] = NEG_INF; }
-            st_f<NV>(p.ws.agg + slot * (64 * NV) + lane_off, c);
-            publish_flag(p.ws.flags + slot, FLAG_AGG);
-            for (int j = chunk - 1; j >= 0; --j) {
-                const int64_t sj = (int64_t)tile * p.n_chunks + j;
-                const uint32_t f = wait_flag(p.ws.flags + sj, p.ws.hdr + 1);
-                const float *src = (f == FLAG_INC ? p.ws.inc : p.ws.agg) + sj * (64 * NV) + lane_off;
-                float x[NV];
-                ld_f<NV>(x, src);
-                // slot j comes before everything folded so far
-#pragma unroll
-                for (int v = 0; v < VEC; ++v) {
-                    in[VEC + v] = lae2(in[v] + x[VEC + v], in[VEC + v]);
-                    in[v] += x[v];
+        for (int q = 0; q < CPT; ++q) {
+            const int ch = threadIdx.x + q * NT;
+            c[q][0] = 0.f; c[q][1] = NEG_INF;
+            in[q][0] = 0.f; in[q][1] = NEG_INF;
+            if (ch < TILE) {
+                for (int w = 0; w < NW; ++w) {
+                    const float x[2] = {s_la[w][ch], s_lh[w][ch]};
+                    float r[2];
+                    LogOp::then(r, c[q], x);
+                    c[q][0] = r[0]; c[q][1] = r[1];
                 }
-                if (f == FLAG_INC) break;
+                if (chunk == 0 && d_tile + ch < p.D) {
+                    const T *lv0 = static_cast<const T *>(p.lv) + (int64_t)bidx * (p.T + 1) * p.D + d_tile + ch;
+                    float f0[1];
+                    Pack<T, 1>::unpack(load_vec<T, 1>(lv0), f0);
+                    in[q][1] = f0[0] * LOG2E;
+                }
             }
         }
-        float inc[NV];
+        wg_lookback<LogOp, TILE, NT>(p.ws, slot, -1, chunk, c, in, &s_k);
 #pragma unroll
-        for (int v = 0; v < VEC; ++v) {
-            inc[v] = in[v] + c[v];
-            inc[VEC + v] = lae2(c[v] + in[VEC + v], c[VEC + v]);
+        for (int q = 0; q < CPT; ++q) {
+            const int ch = threadIdx.x + q * NT;
+            if (ch < TILE) s_c[ch] = in[q][1];
         }
-        st_f<NV>(p.ws.inc + slot * (64 * NV) + lane_off, inc);
-        publish_flag(p.ws.flags + slot, FLAG_INC);
-#pragma unroll
-        for (int v = 0; v < VEC; ++v) s_c[lane * VEC + v] = in[VEC + v];
+        wg_publish_inc(p.ws, slot);
     }
-    __syncthreads();
 
     // 4. State entering this wave: chunk carry-in, then waves 0..wave-1.
     float lh[VEC];
@@ -197,7 +173,9 @@ __global__ __launch_bounds__(NW * 64) void log_fwd_kernel(LogArgs p) {
 
     // 5. Rescan and store h_t = 2^lh_t.
     if (!lane_ok) return;
-    T *ho = static_cast<T *>(p.h) + ((int64_t)bidx * p.T + t0) * p.D + d;
+#pragma unroll
+    for (int r = 0; r < L; ++r) { opaque(rlc[r]); opaque(rlv[r]); }
+    T *ho = static_cast<T *>(p.h) + lc_base;
 #pragma unroll
     for (int r = 0; r < L; ++r) {
         if (t0 + r < p.T) {
@@ -214,7 +192,15 @@ __global__ __launch_bounds__(NW * 64) void log_fwd_kernel(LogArgs p) {
     }
 }
 
-template <typename T, int VEC> struct LogShape { static constexpr int L = 8, NW = 8; };
+#ifndef MISCAN_LOG_L
+#define MISCAN_LOG_L 8
+#endif
+#ifndef MISCAN_LOG_NW
+#define MISCAN_LOG_NW 8
+#endif
+template <typename T, int VEC> struct LogShape {
+    static constexpr int L = MISCAN_LOG_L, NW = MISCAN_LOG_NW;
+};
 
 template <typename E, int VEC>
 size_t log_ws(int64_t B, int64_t T, int64_t D) {
