@@ -52,19 +52,38 @@ def source_digest() -> str:
 # workloads
 # ---------------------------------------------------------------------------
 
-def build_workload(wid, torch, lrs, workloads):
-    """Returns (description dict, list of (kernel name, fn, algorithmic bytes), step fn)."""
+def device_inputs(wid, torch, workloads):
+    """Workload-3 inputs drawn on the GPU with a seeded torch generator (same
+    distributions, other draws): a fast path for short profiler runs."""
+    w = workloads.WORKLOADS[wid]
+    if wid != 3:
+        raise SystemExit("--device-inputs is implemented for workload 3 only")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(wid)
+    shp = (w["B"], w["T"], w["D"])
+    a = 0.9 + (0.9999 - 0.9) * torch.rand(shp, device="cuda", generator=g)
+    out = {"a": a}
+    for k in ("b", "gA", "gBc"):
+        out[k] = torch.randn(shp, device="cuda", generator=g)
+    return {k: v.to(torch.bfloat16) for k, v in out.items()}
+
+
+def build_workload(wid, torch, lrs, workloads, on_device=False):
+    """Returns (description dict, list of (kernel name, fn, algorithmic bytes), units, inputs)."""
     w = workloads.WORKLOADS[wid]
     log("generating inputs for workload", wid, w["name"])
     t0 = time.time()
-    x = workloads.workload_inputs(wid)
     dtype = torch.bfloat16 if w["dtype"] == "bf16" else torch.float32
+    if on_device:
+        d = device_inputs(wid, torch, workloads)
+    else:
+        x = workloads.workload_inputs(wid)
 
-    def dev(a):
-        return torch.from_numpy(a).to(dtype).cuda()
+        def dev(a):
+            return torch.from_numpy(a).to(dtype).cuda()
 
-    d = {k: dev(v) for k, v in x.items()}
-    del x
+        d = {k: dev(v) for k, v in x.items()}
+        del x
     log("inputs resident in HBM (%.1fs)" % (time.time() - t0))
     es = 2 if dtype == torch.bfloat16 else 4
     kernels = []
@@ -212,6 +231,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cold", action="store_true",
                     help="also time each kernel alone after writing 1 GiB to evict the caches")
+    ap.add_argument("--device-inputs", action="store_true",
+                    help="draw workload-3 inputs on the GPU (seeded torch generator) instead of numpy")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run 3 device-to-device copies of MIB MiB (counter calibration) and exit")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -226,12 +249,22 @@ def main():
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         sys.exit(1)
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "copies": 3}), flush=True)
+        return
     ok, reason = lrs.mi_device_check(0)
     if not ok:
         print("bench.py: " + reason, file=sys.stderr)
         sys.exit(1)
 
-    desc, kernels, units, _keep = build_workload(args.workload, torch, lrs, workloads)
+    desc, kernels, units, _keep = build_workload(args.workload, torch, lrs, workloads,
+                                                 on_device=args.device_inputs)
     stream = torch.cuda.current_stream()
 
     log("warmup", args.warmup)
