@@ -30,6 +30,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth
 METRIC = "scan GB/s and % HBM peak, linear_scan fwd+bwd B=8,T=8192,D=4096"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+CPU_SECONDS = 10.0  # CPU work spent on the oracle baseline
 
 
 def log(*a):
@@ -167,13 +168,13 @@ def cpu_baseline(wid, torch, workloads):
         x = {k: q(v) for k, v in x.items()}
         es = 2 if dtype == torch.bfloat16 else 4
         n = Bs * w["T"] * w["D"]
-        t0 = time.perf_counter()
-        A, Bc = oracle.linear_scan_fwd(x["a"], x["b"])
-        nbytes = 4 * es * n
-        if wid == 3:
-            oracle.linear_scan_bwd(x["a"], A, Bc, x["gA"], x["gBc"])
-            nbytes += 7 * es * n
-        dt = time.perf_counter() - t0
+
+        def run():
+            A, Bc = oracle.linear_scan_fwd(x["a"], x["b"])
+            if wid == 3:
+                oracle.linear_scan_bwd(x["a"], A, Bc, x["gA"], x["gBc"])
+
+        nbytes = (11 if wid == 3 else 4) * es * n
         sample = "B=%d of %d batch rows (T=%d, D=%d): %d elements, fwd%s" % (
             Bs, w["B"], w["T"], w["D"], n, "+bwd" if wid == 3 else "")
     elif w["op"] == "log":
@@ -181,9 +182,10 @@ def cpu_baseline(wid, torch, workloads):
         x = workloads.log_inputs(Bs, w["T"], w["D"], wid)
         lc, lv = q(x["log_coeffs"]), q(x["log_values"])
         n = Bs * w["T"] * w["D"]
-        t0 = time.perf_counter()
-        oracle.scan_log_fwd(lc, lv)
-        dt = time.perf_counter() - t0
+
+        def run():
+            oracle.scan_log_fwd(lc, lv)
+
         nbytes = 4 * (3 * n + w["D"])
         sample = "B=1 of %d batch rows: %d elements" % (w["B"], n)
     else:
@@ -194,16 +196,26 @@ def cpu_baseline(wid, torch, workloads):
         x = {k: q(v) for k, v in x.items()}
         S = Bs * w["T"] * w["n"]
         k, v = w["k"], w["v"]
-        t0 = time.perf_counter()
-        Abar, Bbar = oracle.affine_scan_fwd(x["A"], x["Bm"])
+
+        def run():
+            Abar, Bbar = oracle.affine_scan_fwd(x["A"], x["Bm"])
+            if wid == 5:
+                oracle.affine_scan_bwd(x["A"], Abar, Bbar, x["gAbar"], x["gBbar"])
+
         nbytes = 4 * 2 * (S * k * k + S * k * v)
         if wid == 5:
-            oracle.affine_scan_bwd(x["A"], Abar, Bbar, x["gAbar"], x["gBbar"])
             nbytes += 4 * (4 * S * k * k + 3 * S * k * v)
-        dt = time.perf_counter() - t0
         sample = "B=1 of %d batch rows: %d head-steps" % (w["B"], S)
-    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": oracle.num_threads(),
-            "kind": "oracle", "sample": sample, "seconds": round(dt, 3)}
+    # The sample is run repeatedly until about CPU_SECONDS of work is done.
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        run()
+        reps += 1
+        dt = time.perf_counter() - t0
+        if dt >= CPU_SECONDS or reps >= 10000:
+            break
+    return {"value": round(reps * nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": oracle.num_threads(),
+            "kind": "oracle", "sample": "%s; run %d times" % (sample, reps), "seconds": round(dt, 3)}
 
 
 # ---------------------------------------------------------------------------

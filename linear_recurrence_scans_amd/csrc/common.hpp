@@ -98,6 +98,66 @@ __device__ __forceinline__ void store_vec(T *p, typename Pack<T, VEC>::raw_t r) 
     __builtin_nontemporal_store(r, reinterpret_cast<typename Pack<T, VEC>::raw_t *>(p));
 }
 
+// ---------------------------------------------------------------------------
+// Row access through buffer resources.  A work item sets up one descriptor
+// per tensor, based at the first row it touches; a lane then needs a single
+// 32-bit byte offset (its channels), and the row offset is a wave-uniform
+// scalar.  No 64-bit address per row lives in vector registers.  Callers
+// keep every offset inside the tensor themselves; the descriptor's size
+// (accesses past it read zeros and are dropped) is a second line of defence.
+// ---------------------------------------------------------------------------
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+// Raw-buffer descriptor word 3 for gfx9-class GPUs (32-bit data format; the
+// raw loads and stores used here ignore the format).
+constexpr int RSRC_WORD3 = 0x00020000;
+
+__device__ __forceinline__ rsrc_t make_rows(const void *base, int64_t bytes) {
+    const uint32_t n = bytes <= 0 ? 0u : bytes >= (int64_t)0xffffffffll ? 0xffffffffu : (uint32_t)bytes;
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)n, RSRC_WORD3);
+}
+
+template <typename T, int VEC>
+__device__ __forceinline__ typename Pack<T, VEC>::raw_t buf_load(rsrc_t r, uint32_t voff, uint32_t soff) {
+    using raw_t = typename Pack<T, VEC>::raw_t;
+    constexpr int BYTES = (int)sizeof(T) * VEC;
+    if constexpr (BYTES == 16) return __builtin_bit_cast(raw_t, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+    else if constexpr (BYTES == 8) return __builtin_bit_cast(raw_t, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0));
+    else if constexpr (BYTES == 4) return __builtin_bit_cast(raw_t, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+    else return __builtin_bit_cast(raw_t, __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0));
+}
+
+// Descriptor for the rows [first_row, T) of batch row `b` of a (B, T, D)
+// tensor; accesses at or past row T read zeros and are dropped.
+template <typename T>
+__device__ __forceinline__ rsrc_t batch_rows(const void *tensor, int b, int64_t first_row, int64_t Tn,
+                                             int64_t D) {
+    const T *base = static_cast<const T *>(tensor) + ((int64_t)b * Tn + first_row) * D;
+    return make_rows(base, (Tn - first_row) * D * (int64_t)sizeof(T));
+}
+
+// Row base of batch row `b`, time `row` of a (B, T, D) tensor.  With
+// wave-uniform arguments the result is a scalar address.
+template <typename T>
+__device__ __forceinline__ char *row_ptr(void *tensor, int b, int64_t row, int64_t Tn, int64_t D) {
+    return reinterpret_cast<char *>(static_cast<T *>(tensor) + ((int64_t)b * Tn + row) * D);
+}
+
+// Streaming store (nontemporal; outputs are written once, never re-read) of
+// one lane's vector at byte offset `voff` from a wave-uniform row base: a
+// global store with a scalar base and a 32-bit lane offset.
+//
+// Outputs deliberately do not use buffer stores.  On gfx950 a buffer store of
+// more than 8 bytes that takes its row offset from an SGPR can still be
+// reading its data registers when the next VALU instruction overwrites them,
+// and the compiler inserts no wait state for that form; 16-byte bf16 stores
+// were seen to lose their first dword that way.  The compiler does protect
+// wide global stores.
+template <typename T, int VEC>
+__device__ __forceinline__ void row_store(typename Pack<T, VEC>::raw_t v, char *row, uint32_t voff) {
+    __builtin_nontemporal_store(v, reinterpret_cast<typename Pack<T, VEC>::raw_t *>(row + voff));
+}
+
 // Workgroup barrier for LDS traffic only.  __syncthreads() also waits for
 // every outstanding global load of the calling wave (vmcnt(0)), which would
 // drain rows prefetched for the next work item; the kernels exchange only LDS
@@ -313,7 +373,7 @@ inline mi_status launch_status() {
 //  2. wave 0 finds the nearest predecessor with a published inclusive prefix
 //     (wait_ready), publishing this chunk's aggregate flag on the way;
 //  3. every thread folds the k aggregates and the inclusive prefix of its
-//     channels, issuing up to 8 predecessors' loads at a time -- so the walk
+//     channels, issuing up to BATCH predecessors' loads at a time -- so the walk
 //     costs one round trip rather than one per predecessor;
 //  4. every thread stores its channels' inclusive prefix in (+) c.
 // The caller then stages `in` in LDS and calls wg_publish_inc.
@@ -321,11 +381,11 @@ inline mi_status launch_status() {
 // Op describes the carry algebra: NC floats per channel, and
 // then(r, x, y): r = x followed by y (x is applied to the state first).
 // ---------------------------------------------------------------------------
-template <class Op, int TILE, int NT>
+template <class Op, int TILE, int NT, int BATCH = 8>
 __device__ __forceinline__ void wg_lookback(const WsPtrs &ws, int64_t slot, int dir, int n_pred,
                                             const float (&c)[(TILE + NT - 1) / NT][Op::NC],
                                             float (&in)[(TILE + NT - 1) / NT][Op::NC], int *s_k) {
-    constexpr int NC = Op::NC, CPT = (TILE + NT - 1) / NT, BATCH = 8;
+    constexpr int NC = Op::NC, CPT = (TILE + NT - 1) / NT;
     const int tid = threadIdx.x;
     const int64_t pay = (int64_t)NC * TILE;  // payload floats per slot
     if (n_pred > 0) {

@@ -64,9 +64,11 @@ struct BwdOp {
 };
 
 struct Item {
-    int chunk, tile;
+    int chunk, tile, bidx;
+    int64_t row0;  // first row of the workgroup's chunk
+    uint32_t wrow; // first row of this wave, relative to row0 (wave-uniform)
     int64_t t0;    // first row of this wave
-    int64_t base;  // element offset of (b, t0, d) for this lane
+    int64_t d;     // first channel of this lane
     bool lane_ok;  // this lane's channels exist
 };
 
@@ -74,31 +76,21 @@ struct Item {
 // first chunk (in time for the forward, the last one for the reverse scan)
 // before any tile's second.
 template <int VEC, int L, int NW>
-__device__ __forceinline__ Item decode_item(uint32_t ticket, int n_tiles, int n_dtiles, int64_t T,
-                                            int64_t D, int lane, int wave, bool reverse, int n_chunks) {
+__device__ __forceinline__ Item decode_item(uint32_t ticket, int n_tiles, int n_dtiles, int64_t D, int lane,
+                                            int wave, bool reverse, int n_chunks) {
     constexpr int TILE = 64 * VEC;
     Item it;
     const int ord = (int)ticket / n_tiles;
     it.tile = (int)ticket - ord * n_tiles;
     it.chunk = reverse ? n_chunks - 1 - ord : ord;
-    const int bidx = it.tile / n_dtiles;
-    const int dtile = it.tile - bidx * n_dtiles;
-    const int64_t d = (int64_t)dtile * TILE + (int64_t)lane * VEC;
-    it.lane_ok = d < D;
-    it.t0 = (int64_t)it.chunk * (NW * L) + (int64_t)wave * L;
-    it.base = ((int64_t)bidx * T + it.t0) * D + d;
+    it.bidx = it.tile / n_dtiles;
+    const int dtile = it.tile - it.bidx * n_dtiles;
+    it.d = (int64_t)dtile * TILE + (int64_t)lane * VEC;
+    it.lane_ok = it.d < D;
+    it.row0 = (int64_t)it.chunk * (NW * L);
+    it.wrow = (uint32_t)__builtin_amdgcn_readfirstlane(wave) * L;
+    it.t0 = it.row0 + it.wrow;
     return it;
-}
-
-// Row r of a tensor at element offset base + shift*D, or `fill` when the row
-// is outside [0, T) or the lane is past D.  Branch-free: an invalid row is
-// loaded from the tensor's first vector and then replaced, so a wave's loads
-// form one straight run.
-template <typename T, int VEC>
-__device__ __forceinline__ typename Pack<T, VEC>::raw_t row_or(const void *base_ptr, bool ok, int64_t off,
-                                                             typename Pack<T, VEC>::raw_t fill) {
-    const typename Pack<T, VEC>::raw_t x = load_vec<T, VEC>(static_cast<const T *>(base_ptr) + (ok ? off : 0));
-    return ok ? x : fill;
 }
 
 // ---------------------------------------------------------------------------
@@ -124,18 +116,30 @@ __global__ __launch_bounds__(NW * 64) void linear_fwd_kernel(FwdArgs p) {
     const int wave = threadIdx.x >> 6;
     if (threadIdx.x == 0) s_ticket = take_ticket(p.ws.hdr);
     __syncthreads();
-    const Item it = decode_item<VEC, L, NW>(s_ticket, p.n_tiles, p.n_dtiles, p.T, p.D, lane, wave, false,
+    const Item it = decode_item<VEC, L, NW>(__builtin_amdgcn_readfirstlane(s_ticket), p.n_tiles, p.n_dtiles,
+                                            p.D, lane, wave, false,
                                             p.n_chunks);
+    // Offsets of rows or lanes outside the tensor are replaced by 0 (a valid
+    // element) before the access, and the loaded value by the identity after
+    // it, so no access leaves the tensor whatever the descriptor's range.
+    const uint32_t voff = it.lane_ok ? (uint32_t)(it.d * (int64_t)sizeof(T)) : 0u;
+    const uint32_t rowb = (uint32_t)(p.D * (int64_t)sizeof(T));  // bytes per row
 
     // 1. Load this wave's rows (identity step (1, 0) past T or D).
     raw_t ra[L], rb[L];
     {
+        const rsrc_t sa = batch_rows<T>(p.a, it.bidx, it.row0, p.T, p.D);
+        const rsrc_t sb = batch_rows<T>(p.b, it.bidx, it.row0, p.T, p.D);
         const raw_t one = splat<T, VEC>(1.f), zero = splat<T, VEC>(0.f);
 #pragma unroll
         for (int r = 0; r < L; ++r) {
-            const bool ok = it.lane_ok && it.t0 + r < p.T;
-            ra[r] = row_or<T, VEC>(p.a, ok, it.base + r * p.D, one);
-            rb[r] = row_or<T, VEC>(p.b, ok, it.base + r * p.D, zero);
+            const bool row_ok = it.t0 + r < p.T;  // wave-uniform
+            const bool ok = it.lane_ok && row_ok;
+            const uint32_t so = row_ok ? (it.wrow + r) * rowb : 0u;
+            const raw_t xa = buf_load<T, VEC>(sa, voff, so);
+            const raw_t xb = buf_load<T, VEC>(sb, voff, so);
+            ra[r] = ok ? xa : one;
+            rb[r] = ok ? xb : zero;
         }
     }
 
@@ -204,8 +208,8 @@ __global__ __launch_bounds__(NW * 64) void linear_fwd_kernel(FwdArgs p) {
     if (!it.lane_ok) return;
 #pragma unroll
     for (int r = 0; r < L; ++r) { opaque(ra[r]); opaque(rb[r]); }
-    T *Ao = static_cast<T *>(p.A) + it.base;
-    T *Bo = static_cast<T *>(p.Bc) + it.base;
+    char *const Ao = row_ptr<T>(p.A, it.bidx, it.row0, p.T, p.D);
+    char *const Bo = row_ptr<T>(p.Bc, it.bidx, it.row0, p.T, p.D);
 #pragma unroll
     for (int r = 0; r < L; ++r) {
         if (it.t0 + r < p.T) {
@@ -217,8 +221,9 @@ __global__ __launch_bounds__(NW * 64) void linear_fwd_kernel(FwdArgs p) {
                 hA[v] = fa[v] * hA[v];
                 hH[v] = fmaf(fa[v], hH[v], fb[v]);
             }
-            store_vec<T, VEC>(Ao + r * p.D, PK::pack(hA));
-            store_vec<T, VEC>(Bo + r * p.D, PK::pack(hH));
+            const uint32_t so = (it.wrow + r) * rowb;
+            row_store<T, VEC>(PK::pack(hA), Ao + so, voff);
+            row_store<T, VEC>(PK::pack(hH), Bo + so, voff);
         }
     }
 }
@@ -248,23 +253,37 @@ __global__ __launch_bounds__(NW * 64) void linear_bwd_kernel(BwdArgs p) {
     const int wave = threadIdx.x >> 6;
     if (threadIdx.x == 0) s_ticket = take_ticket(p.ws.hdr);
     __syncthreads();
-    const Item it = decode_item<VEC, L, NW>(s_ticket, p.n_tiles, p.n_dtiles, p.T, p.D, lane, wave, true,
+    const Item it = decode_item<VEC, L, NW>(__builtin_amdgcn_readfirstlane(s_ticket), p.n_tiles, p.n_dtiles,
+                                            p.D, lane, wave, true,
                                             p.n_chunks);
+    // Rows or lanes outside the tensor load from offset 0 (a valid element)
+    // and are replaced by the identity; see the forward kernel.
+    const uint32_t voff = it.lane_ok ? (uint32_t)(it.d * (int64_t)sizeof(T)) : 0u;
+    const uint32_t rowb = (uint32_t)(p.D * (int64_t)sizeof(T));
+    // Descriptors start one row before the chunk (the A_{t-1}, Bc_{t-1} halo),
+    // except for the first chunk, which has no row before it.
+    const int64_t first = it.row0 > 0 ? it.row0 - 1 : 0;
+    const uint32_t sh = (uint32_t)(it.row0 - first);  // 1, or 0 for the first chunk
 
     // 1. Loads.  Row r is time t = t0 + r.  c = a_{t+1}; Ap = A_{t-1}; Bp = Bc_{t-1}.
     raw_t rc[L], rgA[L], rgB[L], rAp[L], rBp[L];
     {
+        const rsrc_t sa = batch_rows<T>(p.a, it.bidx, first, p.T, p.D);
+        const rsrc_t sgA = batch_rows<T>(p.gA, it.bidx, first, p.T, p.D);
+        const rsrc_t sgB = batch_rows<T>(p.gBc, it.bidx, first, p.T, p.D);
         const raw_t one = splat<T, VEC>(1.f), zero = splat<T, VEC>(0.f);
 #pragma unroll
         for (int r = 0; r < L; ++r) {
             const int64_t t = it.t0 + r;
             const bool ok = it.lane_ok && t < p.T;
-            const int64_t off = it.base + r * p.D;
-            rc[r] = row_or<T, VEC>(p.a, ok && t + 1 < p.T, off + p.D, ok ? zero : one);
-            rgA[r] = row_or<T, VEC>(p.gA, ok, off, zero);
-            rgB[r] = row_or<T, VEC>(p.gBc, ok, off, zero);
-            rAp[r] = row_or<T, VEC>(p.A, ok && t > 0, off - p.D, one);
-            rBp[r] = row_or<T, VEC>(p.Bc, ok && t > 0, off - p.D, zero);
+            const uint32_t so = t < p.T ? (it.wrow + r + sh) * rowb : 0u;
+            const uint32_t so_next = t + 1 < p.T ? (it.wrow + r + sh + 1) * rowb : 0u;
+            const raw_t xc = buf_load<T, VEC>(sa, voff, so_next);
+            const raw_t xgA = buf_load<T, VEC>(sgA, voff, so);
+            const raw_t xgB = buf_load<T, VEC>(sgB, voff, so);
+            rc[r] = (ok && t + 1 < p.T) ? xc : (ok ? zero : one);
+            rgA[r] = ok ? xgA : zero;
+            rgB[r] = ok ? xgB : zero;
         }
     }
 
@@ -292,6 +311,25 @@ __global__ __launch_bounds__(NW * 64) void linear_bwd_kernel(BwdArgs p) {
         s_M[wave][lane * VEC + v] = gM[v];
     }
     lds_barrier();
+    // A_{t-1}, Bc_{t-1} are needed only by the rescan: loaded after the
+    // barrier (which the compiler cannot hoist them over), they overlap the
+    // look-back instead of occupying registers during the first scan.
+    {
+        const rsrc_t sA = batch_rows<T>(p.A, it.bidx, first, p.T, p.D);
+        const rsrc_t sB = batch_rows<T>(p.Bc, it.bidx, first, p.T, p.D);
+        const raw_t one = splat<T, VEC>(1.f), zero = splat<T, VEC>(0.f);
+#pragma unroll
+        for (int r = 0; r < L; ++r) {
+            const int64_t t = it.t0 + r;
+            const bool row_ok = t < p.T && t > 0;  // wave-uniform
+            const bool ok = it.lane_ok && row_ok;
+            const uint32_t so = row_ok ? (it.wrow + r + sh - 1) * rowb : 0u;
+            const raw_t xA = buf_load<T, VEC>(sA, voff, so);
+            const raw_t xB = buf_load<T, VEC>(sB, voff, so);
+            rAp[r] = ok ? xA : one;
+            rBp[r] = ok ? xB : zero;
+        }
+    }
 
     // 3. Chunk aggregate per channel (waves NW-1 .. 0), look-back over later
     //    chunks, carry.
@@ -311,7 +349,7 @@ __global__ __launch_bounds__(NW * 64) void linear_bwd_kernel(BwdArgs p) {
                     c[q][0] = r[0]; c[q][1] = r[1]; c[q][2] = r[2];
                 }
         }
-        wg_lookback<BwdOp, TILE, NT>(p.ws, slot, +1, p.n_chunks - 1 - it.chunk, c, in, &s_k);
+        wg_lookback<BwdOp, TILE, NT, 4>(p.ws, slot, +1, p.n_chunks - 1 - it.chunk, c, in, &s_k);
 #pragma unroll
         for (int q = 0; q < CPT; ++q) {
             const int ch = threadIdx.x + q * NT;
@@ -338,8 +376,8 @@ __global__ __launch_bounds__(NW * 64) void linear_bwd_kernel(BwdArgs p) {
     if (!it.lane_ok) return;
 #pragma unroll
     for (int r = 0; r < L; ++r) { opaque(rc[r]); opaque(rgA[r]); opaque(rgB[r]); }
-    T *dao = static_cast<T *>(p.da) + it.base;
-    T *dbo = static_cast<T *>(p.db) + it.base;
+    char *const dao = row_ptr<T>(p.da, it.bidx, it.row0, p.T, p.D);
+    char *const dbo = row_ptr<T>(p.db, it.bidx, it.row0, p.T, p.D);
 #pragma unroll
     for (int r = L - 1; r >= 0; --r) {
         float fc[VEC], fgA[VEC], fgB[VEC];
@@ -357,8 +395,9 @@ __global__ __launch_bounds__(NW * 64) void linear_bwd_kernel(BwdArgs p) {
             PK::unpack(rBp[r], fBp);
 #pragma unroll
             for (int v = 0; v < VEC; ++v) da[v] = fmaf(lam[v], fBp[v], mu[v] * fAp[v]);
-            store_vec<T, VEC>(dao + r * p.D, PK::pack(da));
-            store_vec<T, VEC>(dbo + r * p.D, PK::pack(lam));
+            const uint32_t so = (it.wrow + r) * rowb;
+            row_store<T, VEC>(PK::pack(da), dao + so, voff);
+            row_store<T, VEC>(PK::pack(lam), dbo + so, voff);
         }
     }
 }
@@ -392,10 +431,13 @@ struct Grid {
     bool ok;  // the work-item count fits the int32 ticket space
 };
 
-inline Grid make_grid(int64_t B, int64_t T, int64_t D, int tile, int chunk) {
+inline Grid make_grid(int64_t B, int64_t T, int64_t D, int tile, int chunk, int esz) {
     const int64_t nd = (D + tile - 1) / tile, nt = B * nd, nc = (T + chunk - 1) / chunk;
     Grid g;
-    g.ok = nt <= INT32_MAX && nc <= INT32_MAX && nt * nc <= (int64_t)INT32_MAX;
+    // work items fit the int32 ticket space; a chunk's rows (plus the halo)
+    // fit the 32-bit byte offsets of the row descriptors
+    g.ok = nt <= INT32_MAX && nc <= INT32_MAX && nt * nc <= (int64_t)INT32_MAX &&
+           (int64_t)(chunk + 2) * D * esz < ((int64_t)1 << 32);
     g.n_dtiles = (int)nd;
     g.n_tiles = (int)nt;
     g.n_chunks = (int)nc;
@@ -406,14 +448,14 @@ inline Grid make_grid(int64_t B, int64_t T, int64_t D, int tile, int chunk) {
 template <typename E, int VEC>
 size_t fwd_ws(int64_t B, int64_t T, int64_t D) {
     constexpr int L = FwdShape<E, VEC>::L, NW = FwdShape<E, VEC>::NW;
-    Grid g = make_grid(B, T, D, 64 * VEC, L * NW);
+    Grid g = make_grid(B, T, D, 64 * VEC, L * NW, (int)sizeof(E));
     return WsLayout(g.n_slots, 64 * 2 * VEC).total;
 }
 
 template <typename E, int VEC>
 size_t bwd_ws(int64_t B, int64_t T, int64_t D) {
     constexpr int L = BwdShape<E, VEC>::L, NW = BwdShape<E, VEC>::NW;
-    Grid g = make_grid(B, T, D, 64 * VEC, L * NW);
+    Grid g = make_grid(B, T, D, 64 * VEC, L * NW, (int)sizeof(E));
     return WsLayout(g.n_slots, 64 * 3 * VEC).total;
 }
 
@@ -421,7 +463,7 @@ template <typename E, int VEC>
 mi_status run_fwd(const void *a, const void *b, void *A, void *Bc, int64_t B, int64_t T,
                   int64_t D, void *ws, size_t ws_bytes, hipStream_t s) {
     constexpr int L = FwdShape<E, VEC>::L, NW = FwdShape<E, VEC>::NW;
-    Grid g = make_grid(B, T, D, 64 * VEC, L * NW);
+    Grid g = make_grid(B, T, D, 64 * VEC, L * NW, (int)sizeof(E));
     if (!g.ok) return MI_ERR_UNSUPPORTED;
     WsLayout lay(g.n_slots, 64 * 2 * VEC);
     if (ws == nullptr || ws_bytes < lay.total) return MI_ERR_WORKSPACE;
@@ -440,7 +482,7 @@ mi_status run_bwd(const void *a, const void *A, const void *Bc, const void *gA,
                   const void *gBc, void *da, void *db, int64_t B, int64_t T, int64_t D,
                   void *ws, size_t ws_bytes, hipStream_t s) {
     constexpr int L = BwdShape<E, VEC>::L, NW = BwdShape<E, VEC>::NW;
-    Grid g = make_grid(B, T, D, 64 * VEC, L * NW);
+    Grid g = make_grid(B, T, D, 64 * VEC, L * NW, (int)sizeof(E));
     if (!g.ok) return MI_ERR_UNSUPPORTED;
     WsLayout lay(g.n_slots, 64 * 3 * VEC);
     if (ws == nullptr || ws_bytes < lay.total) return MI_ERR_WORKSPACE;

@@ -74,7 +74,7 @@ __global__ __launch_bounds__(NW * 64) void log_fwd_kernel(LogArgs p) {
     const int wave = threadIdx.x >> 6;
     if (threadIdx.x == 0) s_ticket = take_ticket(p.ws.hdr);
     __syncthreads();
-    const int ticket = (int)s_ticket;
+    const int ticket = (int)__builtin_amdgcn_readfirstlane(s_ticket);
     const int chunk = ticket / p.n_tiles;
     const int tile = ticket - chunk * p.n_tiles;
     const int bidx = tile / p.n_dtiles;
@@ -82,22 +82,28 @@ __global__ __launch_bounds__(NW * 64) void log_fwd_kernel(LogArgs p) {
 
     const int64_t d = (int64_t)dtile * TILE + (int64_t)lane * VEC;
     const bool lane_ok = d < p.D;
-    const int64_t t0 = (int64_t)chunk * CHUNK + (int64_t)wave * L;
-    // log_coeffs row t pairs with log_values row t + 1.
-    const int64_t lc_base = ((int64_t)bidx * p.T + t0) * p.D + d;
-    const int64_t lv_base = ((int64_t)bidx * (p.T + 1) + t0 + 1) * p.D + d;
+    const int64_t row0 = (int64_t)chunk * CHUNK;
+    const uint32_t wrow = (uint32_t)__builtin_amdgcn_readfirstlane(wave) * L;
+    const int64_t t0 = row0 + wrow;
+    // Rows or lanes outside the tensor load from offset 0 and are replaced.
+    const uint32_t voff = lane_ok ? (uint32_t)(d * (int64_t)sizeof(T)) : 0u;
+    const uint32_t rowb = (uint32_t)(p.D * (int64_t)sizeof(T));
 
-    // 1. Loads; identity step past T or D is (lc, lv) = (0, -inf).  Branch
-    //    free: invalid rows read the tensor's first vector and are replaced.
+    // 1. Loads; identity step past T or D is (lc, lv) = (0, -inf).
+    //    log_coeffs row t pairs with log_values row t + 1.
     raw_t rlc[L], rlv[L];
     {
+        const rsrc_t slc = batch_rows<T>(p.lc, bidx, row0, p.T, p.D);
+        const rsrc_t slv = make_rows(static_cast<const T *>(p.lv) + ((int64_t)bidx * (p.T + 1) + row0 + 1) * p.D,
+                                     (p.T - row0) * p.D * (int64_t)sizeof(T));
         const raw_t zero = splat<T, VEC>(0.f), ninf = splat<T, VEC>(NEG_INF);
-        const T *lc0 = static_cast<const T *>(p.lc), *lv0 = static_cast<const T *>(p.lv);
 #pragma unroll
         for (int r = 0; r < L; ++r) {
-            const bool ok = lane_ok && t0 + r < p.T;
-            const raw_t xc = load_vec<T, VEC>(lc0 + (ok ? lc_base + r * p.D : 0));
-            const raw_t xv = load_vec<T, VEC>(lv0 + (ok ? lv_base + r * p.D : 0));
+            const bool row_ok = t0 + r < p.T;  // wave-uniform
+            const bool ok = lane_ok && row_ok;
+            const uint32_t so = row_ok ? (wrow + r) * rowb : 0u;
+            const raw_t xc = buf_load<T, VEC>(slc, voff, so);
+            const raw_t xv = buf_load<T, VEC>(slv, voff, so);
             rlc[r] = ok ? xc : zero;
             rlv[r] = ok ? xv : ninf;
         }
@@ -175,7 +181,7 @@ __global__ __launch_bounds__(NW * 64) void log_fwd_kernel(LogArgs p) {
     if (!lane_ok) return;
 #pragma unroll
     for (int r = 0; r < L; ++r) { opaque(rlc[r]); opaque(rlv[r]); }
-    T *ho = static_cast<T *>(p.h) + lc_base;
+    char *const ho = row_ptr<T>(p.h, bidx, row0, p.T, p.D);
 #pragma unroll
     for (int r = 0; r < L; ++r) {
         if (t0 + r < p.T) {
@@ -187,7 +193,7 @@ __global__ __launch_bounds__(NW * 64) void log_fwd_kernel(LogArgs p) {
                 lh[v] = lae2(fc[v] * LOG2E + lh[v], fv[v] * LOG2E);
                 out[v] = exp2f(lh[v]);
             }
-            store_vec<T, VEC>(ho + r * p.D, PK::pack(out));
+            row_store<T, VEC>(PK::pack(out), ho + (wrow + r) * rowb, voff);
         }
     }
 }
@@ -217,6 +223,7 @@ mi_status run_log(const void *lc, const void *lv, void *h, int64_t B, int64_t T,
     const int64_t tile = 64 * VEC, chunk = L * NW;
     const int64_t nd = (D + tile - 1) / tile, nc = (T + chunk - 1) / chunk;
     if (B * nd > INT32_MAX || nc > INT32_MAX || B * nd * nc > (int64_t)INT32_MAX) return MI_ERR_UNSUPPORTED;
+    if ((chunk + 2) * D * (int64_t)sizeof(E) >= ((int64_t)1 << 32)) return MI_ERR_UNSUPPORTED;
     LogArgs p;
     p.n_dtiles = (int)((D + tile - 1) / tile);
     p.n_tiles = (int)(B * p.n_dtiles);
