@@ -84,21 +84,6 @@ __device__ __forceinline__ void stv(float *dst, const float *src) {
     }
 }
 
-// k x k block (row-major, row stride `ld`) into a KP x KP register tile, zero
-// padded.  VIO: k == KP and the rows are vector-aligned.
-template <int KP, bool VIO>
-__device__ __forceinline__ void load_block(float (&m)[KP][KP], const float *src, int k, int64_t ld) {
-    if constexpr (VIO) {
-#pragma unroll
-        for (int i = 0; i < KP; ++i) ldv<KP>(m[i], src + i * ld);
-    } else {
-#pragma unroll
-        for (int i = 0; i < KP; ++i)
-#pragma unroll
-            for (int j = 0; j < KP; ++j) m[i][j] = (i < k && j < k) ? src[i * ld + j] : 0.f;
-    }
-}
-
 // One row of a k x k block into KP registers, zero padded; `ok` false gives zeros.
 template <int KP, bool VIO>
 __device__ __forceinline__ void load_row(float (&r)[KP], const float *src, bool ok, int k) {
@@ -120,7 +105,7 @@ struct FwdArgs {
     float *Abar, *Bbar;
     int64_t T, heads;
     int n, k, v;
-    int G, HPW, NCP, n_groups, n_chunks, LC;
+    int G, HPW, NCP, n_groups, n_chunks, NW;
     WsPtrs ws;
 };
 
@@ -144,66 +129,157 @@ struct Cols {
 // ---------------------------------------------------------------------------
 // Forward
 // ---------------------------------------------------------------------------
+
+// Time steps a wave holds in registers: L steps of the lane's B columns,
+// L * KP * CPL floats, kept near 64.
+#ifndef MISCAN_AFF_BREGS
+#define MISCAN_AFF_BREGS 32
+#endif
+#ifndef MISCAN_AFF_NWMAX
+#define MISCAN_AFF_NWMAX 8
+#endif
+template <int KP, int CPL> struct AffL {
+    static constexpr int raw = MISCAN_AFF_BREGS * (KP >= 8 ? 2 : 1) / (KP * CPL);
+    static constexpr int L = raw < 1 ? 1 : raw > 16 ? 16 : raw;
+};
+
+// The lane's columns of B_t (zero for Abar and padding columns, or when !ok).
 template <int KP, int CPL, bool VIO>
-__device__ __forceinline__ void fwd_step(float (&x)[KP][CPL], const FwdArgs &p, const Cols<CPL> &cl,
-                                         int64_t m, bool active, bool store) {
+__device__ __forceinline__ void load_b(float (&b)[KP][CPL], const FwdArgs &p, const Cols<CPL> &cl, int64_t m,
+                                       bool ok) {
     const int k = p.k, v = p.v;
-    const float *At = p.A + m * k * k;
     const float *Bt = p.Bm + m * k * v;
-    float nx[KP][CPL];
-    // nx = [0 | B_t] for the lane's columns
     if constexpr (VIO) {
-        if (active && cl.kind[0] == C_H) {
+        if (ok && cl.kind[0] == C_H) {
 #pragma unroll
-            for (int i = 0; i < KP; ++i) ldv<CPL>(nx[i], Bt + i * v + cl.col[0]);
+            for (int i = 0; i < KP; ++i) ldv<CPL>(b[i], Bt + i * v + cl.col[0]);
         } else {
 #pragma unroll
             for (int i = 0; i < KP; ++i)
 #pragma unroll
-                for (int cc = 0; cc < CPL; ++cc) nx[i][cc] = 0.f;
+                for (int cc = 0; cc < CPL; ++cc) b[i][cc] = 0.f;
         }
     } else {
 #pragma unroll
         for (int i = 0; i < KP; ++i)
 #pragma unroll
             for (int cc = 0; cc < CPL; ++cc)
-                nx[i][cc] = (active && cl.kind[cc] == C_H && i < k) ? Bt[i * v + cl.col[cc]] : 0.f;
+                b[i][cc] = (ok && cl.kind[cc] == C_H && i < k) ? Bt[i * v + cl.col[cc]] : 0.f;
     }
-    // nx[i] += sum_j A_t[i][j] x[j], one row of A_t at a time
+}
+
+// Store the lane's columns of X_t = [Abar_t | H_t].
+template <int KP, int CPL, bool VIO>
+__device__ __forceinline__ void store_x(const FwdArgs &p, const Cols<CPL> &cl, int64_t m, const float (&x)[KP][CPL]) {
+    const int k = p.k, v = p.v;
+    if constexpr (VIO) {
+        if (cl.kind[0] != C_PAD) {
+            float *dst = (cl.kind[0] == C_ABAR) ? p.Abar + m * k * k + cl.col[0] : p.Bbar + m * k * v + cl.col[0];
+            const int ld = (cl.kind[0] == C_ABAR) ? k : v;
+#pragma unroll
+            for (int i = 0; i < KP; ++i) stv<CPL, true>(dst + i * ld, x[i]);
+        }
+    } else {
+#pragma unroll
+        for (int cc = 0; cc < CPL; ++cc)
+#pragma unroll
+            for (int i = 0; i < KP; ++i) {
+                if (i < k && cl.kind[cc] == C_ABAR) p.Abar[m * k * k + i * k + cl.col[cc]] = x[i][cc];
+                if (i < k && cl.kind[cc] == C_H) p.Bbar[m * k * v + i * v + cl.col[cc]] = x[i][cc];
+            }
+    }
+}
+
+// LDS strides of per-head blocks, padded to 4 (mod 32) floats: the lanes of
+// one head read the same address (a broadcast), and with this padding up to 8
+// heads' blocks start in distinct banks.
+__host__ __device__ constexpr int pad_bank(int f) { return f < 4 ? f : f + ((4 - f % 32) + 32) % 32; }
+
+// A_t of the workgroup's HPW heads for the CH steps of its chunk into LDS,
+// laid out [step][head][AS] with AS = pad_bank(KP * KP) (each block zero
+// padded to KP x KP; identity for steps past T and for heads past the last).
+// Cooperative, coalesced: consecutive threads take consecutive float4s (or
+// floats) of the source.
+template <int KP, bool VIO>
+__device__ __forceinline__ void stage_a(float *s_A, const FwdArgs &p, int grp, int64_t t_c, int CH) {
+    constexpr int KK = KP * KP;
+    constexpr int AS = pad_bank(KK);
+    const int per_step = p.HPW * KK;
+    const int total = CH * per_step;
+    if constexpr (VIO && KK % 4 == 0) {
+        for (int e = (int)threadIdx.x * 4; e < total; e += (int)blockDim.x * 4) {
+            const int s = e / per_step;
+            const int rem = e - s * per_step;
+            const int hs = rem / KK;
+            const int q = rem - hs * KK;
+            const int64_t t = t_c + s;
+            const int64_t gh = (int64_t)grp * p.HPW + hs;
+            f32x4 val;
+            if (t < p.T && gh < p.heads) {
+                const int64_t b = gh / p.n, h = gh - b * p.n;
+                val = *reinterpret_cast<const f32x4 *>(p.A + ((b * p.T + t) * p.n + h) * KK + q);
+            } else {
+                val.x = (q / KP == q % KP) ? 1.f : 0.f;
+                val.y = ((q + 1) / KP == (q + 1) % KP) ? 1.f : 0.f;
+                val.z = ((q + 2) / KP == (q + 2) % KP) ? 1.f : 0.f;
+                val.w = ((q + 3) / KP == (q + 3) % KP) ? 1.f : 0.f;
+            }
+            *reinterpret_cast<f32x4 *>(s_A + (s * p.HPW + hs) * AS + q) = val;
+        }
+    } else {
+        const int k = p.k;
+        for (int e = (int)threadIdx.x; e < total; e += (int)blockDim.x) {
+            const int s = e / per_step;
+            const int rem = e - s * per_step;
+            const int hs = rem / KK;
+            const int q = rem - hs * KK;
+            const int i = q / KP, j = q - (q / KP) * KP;
+            const int64_t t = t_c + s;
+            const int64_t gh = (int64_t)grp * p.HPW + hs;
+            float val = (i == j) ? 1.f : 0.f;
+            if (t < p.T && gh < p.heads && i < k && j < k) {
+                const int64_t b = gh / p.n, h = gh - b * p.n;
+                val = p.A[((b * p.T + t) * p.n + h) * k * k + i * k + j];
+            }
+            s_A[(s * p.HPW + hs) * AS + q] = val;
+        }
+    }
+}
+
+// x <- A x + b for the lane's columns, A a KP x KP block in LDS.  b is zero
+// outside the lane's H columns.
+template <int KP, int CPL>
+__device__ __forceinline__ void step_lds(float (&x)[KP][CPL], const float *Ablk, const float (&b)[KP][CPL]) {
+    float nx[KP][CPL];
 #pragma unroll
     for (int i = 0; i < KP; ++i) {
         float arow[KP];
-        load_row<KP, VIO>(arow, At + i * k, active && i < k, k);
+        ldv<KP>(arow, Ablk + i * KP);
 #pragma unroll
-        for (int j = 0; j < KP; ++j)
+        for (int cc = 0; cc < CPL; ++cc) {
+            float s = b[i][cc];
 #pragma unroll
-            for (int cc = 0; cc < CPL; ++cc) nx[i][cc] = fmaf(arow[j], x[j][cc], nx[i][cc]);
+            for (int j = 0; j < KP; ++j) s = fmaf(arow[j], x[j][cc], s);
+            nx[i][cc] = s;
+        }
     }
 #pragma unroll
     for (int i = 0; i < KP; ++i)
 #pragma unroll
         for (int cc = 0; cc < CPL; ++cc) x[i][cc] = nx[i][cc];
+}
 
-    if (store && active) {
-        if constexpr (VIO) {
-            if (cl.kind[0] != C_PAD) {
-                float *dst = (cl.kind[0] == C_ABAR) ? p.Abar + m * k * k + cl.col[0]
-                                                    : p.Bbar + m * k * v + cl.col[0];
-                const int ld = (cl.kind[0] == C_ABAR) ? k : v;
+// The lane's columns of a [KP][NCP] block in LDS.
+// (Rows start 16-byte aligned and c0 is a multiple of CPL: vector accesses.)
+template <int KP, int CPL>
+__device__ __forceinline__ void put_cols(float *blk, int NCP, int c0, const float (&x)[KP][CPL]) {
 #pragma unroll
-                for (int i = 0; i < KP; ++i) stv<CPL, true>(dst + i * ld, x[i]);
-            }
-        } else {
+    for (int i = 0; i < KP; ++i) stv<CPL, false>(blk + i * NCP + c0, x[i]);
+}
+template <int KP, int CPL>
+__device__ __forceinline__ void get_cols(float (&x)[KP][CPL], const float *blk, int NCP, int c0) {
 #pragma unroll
-            for (int cc = 0; cc < CPL; ++cc) {
-#pragma unroll
-                for (int i = 0; i < KP; ++i) {
-                    if (i < k && cl.kind[cc] == C_ABAR) p.Abar[m * k * k + i * k + cl.col[cc]] = x[i][cc];
-                    if (i < k && cl.kind[cc] == C_H) p.Bbar[m * k * v + i * v + cl.col[cc]] = x[i][cc];
-                }
-            }
-        }
-    }
+    for (int i = 0; i < KP; ++i) ldv<CPL>(x[i], blk + i * NCP + c0);
 }
 
 // Own columns of one head's payload block, row-major (KP rows of NCP floats),
@@ -254,29 +330,125 @@ __device__ __forceinline__ void mat_apply(float (&S)[KP][CPL], const float *Msrc
         for (int cc = 0; cc < CPL; ++cc) S[i][cc] = ns[i][cc];
 }
 
-template <int KP, int CPL, bool VIO>
-__global__ __launch_bounds__(64) void affine_fwd_kernel(FwdArgs p) {
-    extern __shared__ float s_dyn[];
-    float *s_abar = s_dyn;  // [HPW][KP][KP]: this chunk's Abar_c per head, zero padded
+// S <- M S + [0 | H] for a transform block [M | H] (row-major, row stride
+// NCP, the leading k x k block is M): the add term of each of the lane's H
+// columns comes from the same block, so no copy of it is held in registers.
+// `rows(i, m, h)` fetches row i: its first KP entries into m and the lane's
+// CPL columns into h.  Fetches are unconditional (every address is inside
+// the block) and out-of-range entries are zeroed by selects: a load under a
+// per-lane branch costs a wait of its own.
+template <int KP, int CPL, class Rows>
+__device__ __forceinline__ void apply_rows(float (&S)[KP][CPL], Rows rows, int k, const bool (&is_h)[CPL]) {
+    float ns[KP][CPL];
+#pragma unroll
+    for (int i = 0; i < KP; ++i) {
+        float mrow[KP], hrow[CPL];
+        rows(i, mrow, hrow);
+#pragma unroll
+        for (int j = 0; j < KP; ++j) mrow[j] = (i < k && j < k) ? mrow[j] : 0.f;
+#pragma unroll
+        for (int cc = 0; cc < CPL; ++cc) {
+            float s = is_h[cc] ? hrow[cc] : 0.f;
+#pragma unroll
+            for (int j = 0; j < KP; ++j) s = fmaf(mrow[j], S[j][cc], s);
+            ns[i][cc] = s;
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < KP; ++i)
+#pragma unroll
+        for (int cc = 0; cc < CPL; ++cc) S[i][cc] = ns[i][cc];
+}
 
-    const int lane = threadIdx.x;
-    uint32_t tk = 0;
-    if (lane == 0) tk = take_ticket(p.ws.hdr);
-    const int ticket = __shfl((int)tk, 0);
+// The block in LDS (rows and the lane's columns 16-byte aligned).
+template <int KP, int CPL>
+__device__ __forceinline__ void block_apply(float (&S)[KP][CPL], const float *blk, int NCP, int k, int c0,
+                                            const bool (&is_h)[CPL]) {
+    apply_rows<KP, CPL>(S, [&](int i, float (&m)[KP], float (&h)[CPL]) {
+        ldv<KP>(m, blk + i * NCP);
+        ldv<CPL>(h, blk + i * NCP + c0);
+    }, k, is_h);
+}
+
+// N consecutive payload floats at byte offset voff, coherent vector loads.
+template <int N>
+__device__ __forceinline__ void carry_row(float *dst, rsrc_t r, uint32_t voff) {
+    if constexpr (N % 4 == 0) {
+#pragma unroll
+        for (int i = 0; i < N; i += 4) carry_load_vec<4>(dst + i, r, voff + 4u * i);
+    } else if constexpr (N % 2 == 0) {
+#pragma unroll
+        for (int i = 0; i < N; i += 2) carry_load_vec<2>(dst + i, r, voff + 4u * i);
+    } else {
+#pragma unroll
+        for (int i = 0; i < N; ++i) carry_load_vec<1>(dst + i, r, voff + 4u * i);
+    }
+}
+
+// The block of a published payload: slot descriptor r, the head's block at
+// byte offset hb.
+template <int KP, int CPL>
+__device__ __forceinline__ void payload_apply(float (&S)[KP][CPL], rsrc_t r, uint32_t hb, int NCP, int k, int c0,
+                                              const bool (&is_h)[CPL]) {
+    apply_rows<KP, CPL>(S, [&](int i, float (&m)[KP], float (&h)[CPL]) {
+        carry_row<KP>(m, r, hb + 4u * (uint32_t)(i * NCP));
+        carry_row<CPL>(h, r, hb + 4u * (uint32_t)(i * NCP + c0));
+    }, k, is_h);
+}
+
+// The lane's columns of a published payload block.
+template <int KP, int CPL>
+__device__ __forceinline__ void payload_cols(float (&x)[KP][CPL], rsrc_t r, uint32_t hb, int NCP, int c0) {
+#pragma unroll
+    for (int i = 0; i < KP; ++i) carry_row<CPL>(x[i], r, hb + 4u * (uint32_t)(i * NCP + c0));
+}
+
+// One workgroup = NW waves = HPW heads x one chunk of CH = NW * L steps.  Wave
+// w owns steps [w L, (w + 1) L) of the chunk:
+//  1. every wave loads its L steps of B (its columns) into registers, and the
+//     workgroup stages the chunk's A_t blocks in LDS;
+//  2. each wave composes its steps' transform [Abar_w | H_w] from [I | 0];
+//  3. an inclusive prefix over the waves, through LDS, in log2(NW) rounds;
+//  4. wave 0 runs the look-back for the state entering the chunk and
+//     publishes the chunk's inclusive state (the last prefix applied to it);
+//  5. each wave applies the prefix of the waves before it to that state,
+//     rescans its steps from registers and stores Abar_t, Bbar_t.
+// The chunk is read from memory once.
+template <int KP, int CPL, bool VIO>
+__global__ __launch_bounds__(512) void affine_fwd_kernel(FwdArgs p) {
+    constexpr int L = AffL<KP, CPL>::L;
+    extern __shared__ __align__(16) float s_dyn[];
+    __shared__ uint32_t s_ticket;
+    const int NW = p.NW, HPW = p.HPW, NCP = p.NCP;
+    constexpr int AS = pad_bank(KP * KP);  // LDS stride of an A_t block
+    const int CH = NW * L;
+    const int blk = KP * NCP;               // floats of one head's [KP][NCP] payload block
+    const int bs = pad_bank(blk);           // LDS stride of such a block
+    float *s_A = s_dyn;                     // [CH][HPW][AS]
+    float *s_X = s_A + (CH * HPW * AS + 3) / 4 * 4;  // [NW][HPW][bs]: wave transforms (16-byte aligned)
+    float *s_C = s_X + NW * HPW * bs;       // [HPW][bs]: chunk transform
+    float *s_S = s_C + HPW * bs;            // [HPW][bs]: state entering the chunk
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    if (tid == 0) s_ticket = take_ticket(p.ws.hdr);
+    __syncthreads();
+    const int ticket = (int)__builtin_amdgcn_readfirstlane(s_ticket);
     const int chunk = ticket / p.n_groups;
     const int grp = ticket - chunk * p.n_groups;
     const int hs = lane / p.G;
     const int g = lane - hs * p.G;
-    const bool slot_lane = hs < p.HPW;  // lane maps to a head slot of this wave
+    const bool slot_lane = hs < HPW;  // lane maps to a head slot
     const int hsc = slot_lane ? hs : 0;
-    const int64_t gh = (int64_t)grp * p.HPW + hs;
+    const int64_t gh = (int64_t)grp * HPW + hs;
     const bool active = slot_lane && gh < p.heads;
     const int64_t bidx = active ? gh / p.n : 0;
     const int64_t hh = active ? gh % p.n : 0;
-    const int k = p.k;
+    // With vector IO k equals KP: a compile-time k removes every bounds test
+    // (and the branches around the loads) from the block products.
+    const int k = VIO ? KP : p.k;
     const int c0 = g * CPL;
-
-    for (int i = lane; i < p.HPW * KP * KP; i += 64) s_abar[i] = 0.f;
 
     Cols<CPL> cl;
 #pragma unroll
@@ -290,70 +462,100 @@ __global__ __launch_bounds__(64) void affine_fwd_kernel(FwdArgs p) {
 #pragma unroll
     for (int cc = 0; cc < CPL; ++cc) is_h[cc] = cl.kind[cc] == C_H;
 
-    const int64_t t_begin = (int64_t)chunk * p.LC;
-    const int64_t t_end = (t_begin + p.LC < p.T) ? t_begin + p.LC : p.T;
-    const int64_t m0 = bidx * p.T * p.n + hh;  // matrix index of (b, t=0, h); + t*n per step
+    const int64_t t_c = (int64_t)chunk * CH;  // first step of the chunk
+    const int64_t t_w = t_c + (int64_t)wave * L;
+    const int64_t m0 = bidx * p.T * p.n + hh;  // matrix index of (b, t = 0, h); + t n per step
 
-    // Pass 1: the chunk's transform [Abar_c | H_c] from [I | 0].
+    // 1. B of the wave's steps (registers) and the chunk's A (LDS).
+    float rb[L][KP][CPL];
+#pragma unroll
+    for (int r = 0; r < L; ++r) load_b<KP, CPL, VIO>(rb[r], p, cl, m0 + (t_w + r) * p.n, active && t_w + r < p.T);
+    stage_a<KP, VIO>(s_A, p, grp, t_c, CH);
+    lds_barrier();
+
+    // 2. The wave's transform from [I | 0].
     float x[KP][CPL];
 #pragma unroll
     for (int i = 0; i < KP; ++i)
 #pragma unroll
-        for (int cc = 0; cc < CPL; ++cc)
-            x[i][cc] = (cl.kind[cc] == C_ABAR && i == cl.col[cc]) ? 1.f : 0.f;
-    for (int64_t t = t_begin; t < t_end; ++t)
-        fwd_step<KP, CPL, VIO>(x, p, cl, m0 + t * p.n, active, false);
-
-    // Abar_c of each head to LDS, written by the lanes that own its columns.
-    __syncthreads();
-    if (slot_lane) {
+        for (int cc = 0; cc < CPL; ++cc) x[i][cc] = (cl.kind[cc] == C_ABAR && i == cl.col[cc]) ? 1.f : 0.f;
 #pragma unroll
-        for (int cc = 0; cc < CPL; ++cc)
-            if (cl.kind[cc] == C_ABAR)
+    for (int r = 0; r < L; ++r) step_lds<KP, CPL>(x, s_A + ((wave * L + r) * HPW + hsc) * AS, rb[r]);
+    // 3. Inclusive prefix over the waves (Hillis-Steele): after the round
+    //    with offset o, wave w holds T_w o ... o T_{max(0, w - 2o + 1)}.  Each
+    //    round applies the block of wave w - o to the wave's own transform:
+    //    X <- X o P  means  [A_X A_P | A_X H_P + H_X], i.e. the lane's columns
+    //    of P under A_X, plus H_X on the H columns.
+    if (slot_lane) put_cols<KP, CPL>(s_X + (wave * HPW + hs) * bs, NCP, c0, x);
+    lds_barrier();
+    for (int o = 1; o < NW; o *= 2) {
+        if (wave >= o) {
+            float P[KP][CPL];
+            get_cols<KP, CPL>(P, s_X + ((wave - o) * HPW + hsc) * bs, NCP, c0);
+            block_apply<KP, CPL>(P, s_X + (wave * HPW + hsc) * bs, NCP, k, c0, is_h);
 #pragma unroll
-                for (int i = 0; i < KP; ++i) s_abar[(hs * KP + i) * KP + cl.col[cc]] = x[i][cc];
-    }
-    __syncthreads();
-
-    // Look-back: the state S entering the chunk ([I | 0] before chunk 0).
-    const int64_t slot_sz = (int64_t)p.HPW * KP * p.NCP;
-    const int64_t hoff = (int64_t)hsc * KP * p.NCP;
-    const int64_t slot = (int64_t)grp * p.n_chunks + chunk;
-    float S[KP][CPL];
+            for (int i = 0; i < KP; ++i)
 #pragma unroll
-    for (int i = 0; i < KP; ++i)
-#pragma unroll
-        for (int cc = 0; cc < CPL; ++cc)
-            S[i][cc] = (cl.kind[cc] == C_ABAR && i == cl.col[cc]) ? 1.f : 0.f;
-    if (chunk > 0) {
-        if (slot_lane) payload_store<KP, CPL>(p.ws.agg + slot * slot_sz + hoff, p.NCP, c0, x);
-        const int dist = wait_ready(p.ws.flags, slot - 1, -1, chunk, p.ws.hdr + 1, p.ws.flags + slot, FLAG_AGG);
-        const int j0 = chunk - 1 - dist;
-        // slot j0 holds an inclusive state; chunks j0+1 .. chunk-1 hold transforms
-        payload_load<KP, CPL>(S, p.ws.inc + ((int64_t)grp * p.n_chunks + j0) * slot_sz + hoff,
-                                   p.NCP, c0);
-        for (int jj = j0 + 1; jj < chunk; ++jj) {
-            const float *blk = p.ws.agg + ((int64_t)grp * p.n_chunks + jj) * slot_sz + hoff;
-            float Hx[KP][CPL];
-            payload_load<KP, CPL>(Hx, blk, p.NCP, c0);
-            mat_apply<KP, CPL, true>(S, blk, p.NCP, k, Hx, is_h);
+                for (int cc = 0; cc < CPL; ++cc) x[i][cc] = P[i][cc];
         }
+        lds_barrier();  // every read of this round is done
+        if (wave >= o && slot_lane) put_cols<KP, CPL>(s_X + (wave * HPW + hs) * bs, NCP, c0, x);
+        lds_barrier();
     }
-    // Inclusive state after this chunk: [Abar_c | H_c] applied to S.
-    {
-        float inc[KP][CPL];
+
+    // 4. Look-back and publication (wave 0).  The chunk transform is the
+    //    last wave's prefix.
+    if (wave == 0) {
+        {
+            float C[KP][CPL];
+            get_cols<KP, CPL>(C, s_X + ((NW - 1) * HPW + hsc) * bs, NCP, c0);
+            if (slot_lane) put_cols<KP, CPL>(s_C + hs * bs, NCP, c0, C);
+        }
+
+        const int64_t slot_sz = (int64_t)HPW * blk;
+        const int64_t hoff = (int64_t)hsc * blk;
+        const int64_t slot = (int64_t)grp * p.n_chunks + chunk;
+        float S[KP][CPL];
 #pragma unroll
         for (int i = 0; i < KP; ++i)
 #pragma unroll
-            for (int cc = 0; cc < CPL; ++cc) inc[i][cc] = S[i][cc];
-        mat_apply<KP, CPL, false>(inc, s_abar + hsc * KP * KP, KP, KP, x, is_h);
-        if (slot_lane) payload_store<KP, CPL>(p.ws.inc + slot * slot_sz + hoff, p.NCP, c0, inc);
+            for (int cc = 0; cc < CPL; ++cc) S[i][cc] = (cl.kind[cc] == C_ABAR && i == cl.col[cc]) ? 1.f : 0.f;
+        // the wave's own s_C writes are complete before other lanes read them
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+        if (chunk > 0) {
+            if (slot_lane) {
+                float C[KP][CPL];
+                get_cols<KP, CPL>(C, s_C + hs * bs, NCP, c0);
+                payload_store<KP, CPL>(p.ws.agg + slot * slot_sz + hoff, NCP, c0, C);
+            }
+            const int dist = wait_ready(p.ws.flags, slot - 1, -1, chunk, p.ws.hdr + 1, p.ws.flags + slot, FLAG_AGG);
+            const int j0 = chunk - 1 - dist;
+            const uint32_t hb = 4u * (uint32_t)hoff;
+            const int64_t slot_bytes = 4 * slot_sz;
+            // slot j0 holds an inclusive state; chunks j0+1 .. chunk-1 hold transforms
+            payload_cols<KP, CPL>(S, make_rows(p.ws.inc + ((int64_t)grp * p.n_chunks + j0) * slot_sz, slot_bytes), hb,
+                                  NCP, c0);
+            for (int jj = j0 + 1; jj < chunk; ++jj)
+                payload_apply<KP, CPL>(S, make_rows(p.ws.agg + ((int64_t)grp * p.n_chunks + jj) * slot_sz, slot_bytes),
+                                       hb, NCP, k, c0, is_h);
+        }
+        if (slot_lane) put_cols<KP, CPL>(s_S + hs * bs, NCP, c0, S);
+        block_apply<KP, CPL>(S, s_C + hsc * bs, NCP, k, c0, is_h);  // S becomes the inclusive state
+        if (slot_lane) payload_store<KP, CPL>(p.ws.inc + slot * slot_sz + hoff, NCP, c0, S);
         publish_flag(p.ws.flags + slot, FLAG_INC);
     }
+    lds_barrier();
 
-    // Pass 2: rescan the chunk from S and store Abar_t, Bbar_t.
-    for (int64_t t = t_begin; t < t_end; ++t)
-        fwd_step<KP, CPL, VIO>(S, p, cl, m0 + t * p.n, active, true);
+    // 5. State entering this wave (the chunk's, then the prefix of the waves
+    //    before it), rescan, store.
+    float S[KP][CPL];
+    get_cols<KP, CPL>(S, s_S + hsc * bs, NCP, c0);
+    if (wave > 0) block_apply<KP, CPL>(S, s_X + ((wave - 1) * HPW + hsc) * bs, NCP, k, c0, is_h);
+#pragma unroll
+    for (int r = 0; r < L; ++r) {
+        step_lds<KP, CPL>(S, s_A + ((wave * L + r) * HPW + hsc) * AS, rb[r]);
+        if (active && t_w + r < p.T) store_x<KP, CPL, VIO>(p, cl, m0 + (t_w + r) * p.n, S);
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -415,7 +617,7 @@ template <int KP> struct RowBlock { static constexpr int RB = KP < 8 ? KP : 8; }
 template <int KP, int CPL, bool VIO>
 __global__ __launch_bounds__(64) void affine_bwd_kernel(BwdArgs p) {
     constexpr int RB = RowBlock<KP>::RB;
-    extern __shared__ float s_dyn[];
+    extern __shared__ __align__(16) float s_dyn[];
     float *s_P = s_dyn;                        // [HPW][KP][KP]: this chunk's P_c
     float *s_part = s_dyn + p.HPW * KP * KP;   // [HPW][G][RB][KP]: dA partial sums
 
@@ -631,7 +833,7 @@ constexpr int LC_STEPS = MISCAN_AFF_LC;  // time steps per work item
 struct AffPlan {
     int KP, CPL;
     bool VIO;
-    int G, HPW, NCP, n_groups, n_chunks, LC, RB;
+    int G, HPW, NCP, n_groups, n_chunks, LC, RB, NW;
     size_t n_slots, payload, lds_bytes;
     bool ok;  // the work-item count fits the int32 ticket space
 };
@@ -654,11 +856,72 @@ inline AffPlan make_plan(int64_t B, int64_t T, int64_t n, int k, int ncols, bool
     pl.n_groups = (int)ng;
     pl.n_chunks = (int)nc;
     pl.RB = pl.KP < 8 ? pl.KP : 8;
+    pl.NW = 1;
     pl.n_slots = pl.ok ? (size_t)ng * (size_t)nc : 0;
     pl.payload = (size_t)pl.HPW * pl.KP * pl.NCP;
     pl.lds_bytes = sizeof(float) * (size_t)pl.HPW * pl.KP * pl.KP;
     if (bwd) pl.lds_bytes += sizeof(float) * (size_t)pl.HPW * pl.G * pl.RB * pl.KP;
     return pl;
+}
+
+// Forward tiling: L steps per wave (AffL), NW waves per workgroup, chunks of
+// NW * L steps; NW as large as 64 KiB of LDS allows.
+constexpr size_t FWD_LDS_MAX = 65536;
+
+inline int aff_L(int KP, int CPL) {
+    const int raw = MISCAN_AFF_BREGS * (KP >= 8 ? 2 : 1) / (KP * CPL);
+    return raw < 1 ? 1 : raw > 16 ? 16 : raw;
+}
+
+inline AffPlan make_fwd_plan(int64_t B, int64_t T, int64_t n, int k, int v, int CPL, bool VIO) {
+    AffPlan pl;
+    pl.KP = next_pow2_16(k);
+    pl.CPL = CPL;
+    pl.VIO = VIO;
+    pl.G = (k + v + CPL - 1) / CPL;
+    pl.HPW = 64 / pl.G;
+    pl.NCP = (int)round_up((size_t)pl.G * CPL, 4);
+    pl.RB = 0;
+    const int L = aff_L(pl.KP, CPL);
+    const size_t per_head = (size_t)pl.KP * pl.NCP;      // payload block
+    const size_t a_ld = (size_t)pad_bank(pl.KP * pl.KP);  // LDS strides (see pad_bank)
+    const size_t x_ld = (size_t)pad_bank(pl.KP * pl.NCP);
+    pl.NW = 1;
+    for (int nw = MISCAN_AFF_NWMAX; nw >= 1; nw /= 2) {
+        const size_t f = round_up((size_t)nw * L * pl.HPW * a_ld, 4) + (size_t)nw * pl.HPW * x_ld +
+                         2 * (size_t)pl.HPW * x_ld;
+        if (f * sizeof(float) <= FWD_LDS_MAX) { pl.NW = nw; break; }
+    }
+    pl.LC = pl.NW * L;
+    pl.lds_bytes = sizeof(float) * (round_up((size_t)pl.LC * pl.HPW * a_ld, 4) + (size_t)pl.NW * pl.HPW * x_ld +
+                                    2 * (size_t)pl.HPW * x_ld);
+    const int64_t heads = B * n;
+    const int64_t ng = (heads + pl.HPW - 1) / pl.HPW;
+    const int64_t nc = (T + pl.LC - 1) / pl.LC;
+    pl.ok = ng <= INT32_MAX && nc <= INT32_MAX && ng * nc <= (int64_t)INT32_MAX && pl.lds_bytes <= FWD_LDS_MAX;
+    pl.n_groups = (int)ng;
+    pl.n_chunks = (int)nc;
+    pl.n_slots = pl.ok ? (size_t)ng * (size_t)nc : 0;
+    pl.payload = (size_t)pl.HPW * per_head;
+    return pl;
+}
+
+// Forward column tiling: of the vector tilings the alignment allows, the one
+// with the longest chunk (fewer look-back steps and payload bytes per step of
+// data), four columns per lane on a tie.
+inline AffPlan choose_fwd_plan(int64_t B, int64_t T, int64_t n, int k, int v, bool ptrs16) {
+    const bool kpow2 = next_pow2_16(k) == k;
+    AffPlan best;
+    bool have = false;
+    const int cands[2] = {4, 2};
+    for (int cpl : cands) {
+        if (!(ptrs16 && kpow2 && k % cpl == 0 && v % cpl == 0 && (k + v + cpl - 1) / cpl <= 64)) continue;
+        AffPlan pl = make_fwd_plan(B, T, n, k, v, cpl, true);
+        if (!pl.ok) continue;
+        if (!have || pl.LC > best.LC) { best = pl; have = true; }
+    }
+    if (!have) best = make_fwd_plan(B, T, n, k, v, 4, false);
+    return best;
 }
 
 inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) % 16) == 0; }
@@ -677,7 +940,8 @@ inline void choose_cols(int k, int v, int ncols, bool ptrs16, int &CPL, bool &VI
 
 template <int KP, int CPL, bool VIO>
 mi_status fwd_launch(const AffPlan &pl, FwdArgs &a, hipStream_t s) {
-    hipLaunchKernelGGL((affine_fwd_kernel<KP, CPL, VIO>), dim3((unsigned)pl.n_slots), dim3(64),
+    if (pl.LC != pl.NW * AffL<KP, CPL>::L) return MI_ERR_UNSUPPORTED;  // host and kernel tilings agree
+    hipLaunchKernelGGL((affine_fwd_kernel<KP, CPL, VIO>), dim3((unsigned)pl.n_slots), dim3(64 * pl.NW),
                        pl.lds_bytes, s, a);
     return launch_status();
 }
@@ -721,16 +985,17 @@ size_t affine_workspace_bytes(int64_t B, int64_t T, int64_t n, int64_t k, int64_
     // The column tiling depends on pointer alignment, known only at the call:
     // size for the largest of the tilings either alignment can select.
     size_t m = 0;
-    for (int bwd = 0; bwd < 2; ++bwd) {
-        const int nc = (int)(bwd ? 2 * k + v : k + v);
-        for (int a16 = 0; a16 < 2; ++a16) {
-            int CPL;
-            bool VIO;
-            choose_cols((int)k, (int)v, nc, a16 != 0, CPL, VIO);
-            AffPlan pl = make_plan(B, T, n, (int)k, nc, bwd != 0, CPL, VIO);
-            const size_t w = WsLayout(pl.n_slots, pl.payload).total;
-            m = w > m ? w : m;
-        }
+    for (int a16 = 0; a16 < 2; ++a16) {
+        const int nc = (int)(2 * k + v);
+        int CPL;
+        bool VIO;
+        choose_cols((int)k, (int)v, nc, a16 != 0, CPL, VIO);
+        AffPlan pb = make_plan(B, T, n, (int)k, nc, true, CPL, VIO);
+        AffPlan pf = choose_fwd_plan(B, T, n, (int)k, (int)v, a16 != 0);
+        const size_t wb = WsLayout(pb.n_slots, pb.payload).total;
+        const size_t wf = WsLayout(pf.n_slots, pf.payload).total;
+        m = wb > m ? wb : m;
+        m = wf > m ? wf : m;
     }
     return m;
 }
@@ -739,11 +1004,7 @@ mi_status launch_affine_fwd(const void *A, const void *Bm, void *Abar, void *Bba
                             int64_t T, int64_t n, int64_t k, int64_t v, void *ws,
                             size_t ws_bytes, hipStream_t s) {
     const bool p16 = aligned16(A) && aligned16(Bm) && aligned16(Abar) && aligned16(Bbar);
-    const int nc = (int)(k + v);
-    int CPL;
-    bool VIO;
-    choose_cols((int)k, (int)v, nc, p16, CPL, VIO);
-    AffPlan pl = make_plan(B, T, n, (int)k, nc, false, CPL, VIO);
+    AffPlan pl = choose_fwd_plan(B, T, n, (int)k, (int)v, p16);
     if (!pl.ok) return MI_ERR_UNSUPPORTED;
     WsLayout lay(pl.n_slots, pl.payload);
     if (ws == nullptr || ws_bytes < lay.total) return MI_ERR_WORKSPACE;
@@ -752,7 +1013,7 @@ mi_status launch_affine_fwd(const void *A, const void *Bm, void *Abar, void *Bba
     a.Abar = static_cast<float *>(Abar); a.Bbar = static_cast<float *>(Bbar);
     a.T = T; a.heads = B * n; a.n = (int)n; a.k = (int)k; a.v = (int)v;
     a.G = pl.G; a.HPW = pl.HPW; a.NCP = pl.NCP; a.n_groups = pl.n_groups;
-    a.n_chunks = pl.n_chunks; a.LC = pl.LC;
+    a.n_chunks = pl.n_chunks; a.NW = pl.NW;
     a.ws = ws_ptrs(ws, lay);
     mi_status st = clear_workspace(a.ws, pl.n_slots, s);
     if (st != MI_OK) return st;

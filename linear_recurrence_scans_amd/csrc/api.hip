@@ -2,9 +2,10 @@
 // vector-width selection and dispatch to the kernel launchers.
 //
 // Every check runs before anything is enqueued, so a rejected call leaves the
-// stream untouched (the "validate before any launch" rule of the minGRU docs
-// page "Triton kernels", angle_scan_impl entry), and nothing ever falls back to
-// another implementation (ScanFallback entry: never a silent downgrade).
+// stream untouched (the minGRU docs page "Triton kernels", angle_scan_impl
+// entry, checks every shape invariant before it enqueues anything), and nothing
+// ever falls back to another implementation (the page's ScanFallback entry
+// rules that out).
 #include <string.h>
 
 #include <algorithm>

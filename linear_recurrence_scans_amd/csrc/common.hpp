@@ -241,6 +241,25 @@ __device__ __forceinline__ void carry_load_n(float *dst, const float *src) {
     for (int i = 0; i < N; ++i) dst[i] = carry_load(src + i);
 }
 
+// Vector form of carry_load for N = 1, 2 or 4 consecutive floats at byte
+// offset `voff` of a buffer resource: the same cache policy (sc1) as the
+// relaxed device-scope atomic loads, so it observes payload words published
+// under the flag protocol.
+constexpr int CPOL_SC1 = 16;
+template <int N>
+__device__ __forceinline__ void carry_load_vec(float *dst, __amdgpu_buffer_rsrc_t r, uint32_t voff) {
+    if constexpr (N == 4) {
+        const f32x4 q = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, 0, CPOL_SC1));
+        dst[0] = q.x; dst[1] = q.y; dst[2] = q.z; dst[3] = q.w;
+    } else if constexpr (N == 2) {
+        const f32x2 q = __builtin_bit_cast(f32x2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, 0, CPOL_SC1));
+        dst[0] = q.x; dst[1] = q.y;
+    } else {
+        static_assert(N == 1, "N must be 1, 2 or 4");
+        dst[0] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, 0, CPOL_SC1));
+    }
+}
+
 // Store the flag once this lane's earlier payload stores are acknowledged.
 __device__ __forceinline__ void publish_flag(uint32_t *flag, uint32_t v) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -374,7 +393,9 @@ inline mi_status launch_status() {
 //     (wait_ready), publishing this chunk's aggregate flag on the way;
 //  3. every thread folds the k aggregates and the inclusive prefix of its
 //     channels, issuing up to BATCH predecessors' loads at a time -- so the walk
-//     costs one round trip rather than one per predecessor;
+//     costs one round trip per BATCH predecessors rather than one each.  When
+//     the workgroup has G >= 2 threads per channel, G groups fold disjoint
+//     runs of predecessors at once and combine their partials through LDS;
 //  4. every thread stores its channels' inclusive prefix in (+) c.
 // The caller then stages `in` in LDS and calls wg_publish_inc.
 //
@@ -386,6 +407,7 @@ __device__ __forceinline__ void wg_lookback(const WsPtrs &ws, int64_t slot, int 
                                             const float (&c)[(TILE + NT - 1) / NT][Op::NC],
                                             float (&in)[(TILE + NT - 1) / NT][Op::NC], int *s_k) {
     constexpr int NC = Op::NC, CPT = (TILE + NT - 1) / NT;
+    constexpr int G = NT >= 2 * TILE ? NT / TILE : 1;  // predecessor-folding groups
     const int tid = threadIdx.x;
     const int64_t pay = (int64_t)NC * TILE;  // payload floats per slot
     if (n_pred > 0) {
@@ -404,31 +426,95 @@ __device__ __forceinline__ void wg_lookback(const WsPtrs &ws, int64_t slot, int 
         }
         lds_barrier();
         const int k = *s_k;
-        for (int j0 = 0; j0 <= k; j0 += BATCH) {
-            float x[BATCH][CPT][NC];
+        if constexpr (G == 1) {
+            for (int j0 = 0; j0 <= k; j0 += BATCH) {
+                float x[BATCH][CPT][NC];
 #pragma unroll
-            for (int u = 0; u < BATCH; ++u) {
-                const int j = j0 + u;
-                if (j <= k) {
-                    const float *src = (j == k ? ws.inc : ws.agg) + (slot + (int64_t)dir * (j + 1)) * pay;
+                for (int u = 0; u < BATCH; ++u) {
+                    const int j = j0 + u;
+                    if (j <= k) {
+                        const float *src = (j == k ? ws.inc : ws.agg) + (slot + (int64_t)dir * (j + 1)) * pay;
 #pragma unroll
-                    for (int q = 0; q < CPT; ++q) {
-                        const int ch = tid + q * NT;
+                        for (int q = 0; q < CPT; ++q) {
+                            const int ch = tid + q * NT;
 #pragma unroll
-                        for (int m = 0; m < NC; ++m) x[u][q][m] = ch < TILE ? carry_load(src + m * TILE + ch) : 0.f;
+                            for (int m = 0; m < NC; ++m)
+                                x[u][q][m] = ch < TILE ? carry_load(src + m * TILE + ch) : 0.f;
+                        }
+                    }
+                }
+#pragma unroll
+                for (int u = 0; u < BATCH; ++u) {
+                    if (j0 + u <= k) {
+#pragma unroll
+                        for (int q = 0; q < CPT; ++q) {
+                            float r[NC];
+                            Op::then(r, x[u][q], in[q]);  // predecessor j comes before all folded so far
+#pragma unroll
+                            for (int m = 0; m < NC; ++m) in[q][m] = r[m];
+                        }
                     }
                 }
             }
+        } else {
+            // G groups of TILE threads (CPT == 1).  Group g folds predecessors
+            // [g * per, (g + 1) * per) into a partial transform, nearest
+            // first; group 0 then applies the partials of the later groups,
+            // which lie further back in time.
+            __shared__ float s_part[G - 1][NC][TILE];
+            const int grp = tid / TILE, ch = tid - grp * TILE;
+            const int per = (k + 1 + G - 1) / G;
+            const int lo = grp * per;
+            const int hi = lo + per < k + 1 ? lo + per : k + 1;
+            float part[NC];
+            bool have = false;
+            if (grp < G) {
+                for (int j0 = lo; j0 < hi; j0 += BATCH) {
+                    float x[BATCH][NC];
 #pragma unroll
-            for (int u = 0; u < BATCH; ++u) {
-                if (j0 + u <= k) {
+                    for (int u = 0; u < BATCH; ++u) {
+                        const int j = j0 + u;
+                        if (j < hi) {
+                            const float *src = (j == k ? ws.inc : ws.agg) + (slot + (int64_t)dir * (j + 1)) * pay;
 #pragma unroll
-                    for (int q = 0; q < CPT; ++q) {
-                        float r[NC];
-                        Op::then(r, x[u][q], in[q]);  // predecessor j comes before all folded so far
-#pragma unroll
-                        for (int m = 0; m < NC; ++m) in[q][m] = r[m];
+                            for (int m = 0; m < NC; ++m) x[u][m] = carry_load(src + m * TILE + ch);
+                        }
                     }
+#pragma unroll
+                    for (int u = 0; u < BATCH; ++u) {
+                        if (j0 + u < hi) {
+                            if (!have) {
+#pragma unroll
+                                for (int m = 0; m < NC; ++m) part[m] = x[u][m];
+                                have = true;
+                            } else {
+                                float r[NC];
+                                Op::then(r, x[u], part);
+#pragma unroll
+                                for (int m = 0; m < NC; ++m) part[m] = r[m];
+                            }
+                        }
+                    }
+                }
+                if (grp > 0 && have)
+#pragma unroll
+                    for (int m = 0; m < NC; ++m) s_part[grp - 1][m][ch] = part[m];
+            }
+            lds_barrier();
+            if (grp == 0) {
+                if (have) {
+                    float r[NC];
+                    Op::then(r, part, in[0]);
+#pragma unroll
+                    for (int m = 0; m < NC; ++m) in[0][m] = r[m];
+                }
+                for (int g = 1; g < G && g * per < k + 1; ++g) {
+                    float x[NC], r[NC];
+#pragma unroll
+                    for (int m = 0; m < NC; ++m) x[m] = s_part[g - 1][m][ch];
+                    Op::then(r, x, in[0]);
+#pragma unroll
+                    for (int m = 0; m < NC; ++m) in[0][m] = r[m];
                 }
             }
         }

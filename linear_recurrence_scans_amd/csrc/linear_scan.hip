@@ -418,6 +418,13 @@ __global__ __launch_bounds__(NW * 64) void linear_bwd_kernel(BwdArgs p) {
 #ifndef MISCAN_LIN_BWD_NW
 #define MISCAN_LIN_BWD_NW 8
 #endif
+// Widest bf16 vector (elements per lane) each direction uses.
+#ifndef MISCAN_LIN_FWD_BF16_VMAX
+#define MISCAN_LIN_FWD_BF16_VMAX 8
+#endif
+#ifndef MISCAN_LIN_BWD_BF16_VMAX
+#define MISCAN_LIN_BWD_BF16_VMAX 8
+#endif
 template <typename T, int VEC> struct FwdShape {
     static constexpr int L = MISCAN_LIN_FWD_L, NW = MISCAN_LIN_FWD_NW;
 };
@@ -527,6 +534,7 @@ mi_status launch_linear_fwd(const void *a, const void *b, void *A, void *Bc, int
             default: return run_fwd<float, 1>(a, b, A, Bc, B, T, D, ws, ws_bytes, s);
         }
     }
+    if (vec > MISCAN_LIN_FWD_BF16_VMAX) vec = MISCAN_LIN_FWD_BF16_VMAX;
     switch (vec) {
         case 8: return run_fwd<bf16_t, 8>(a, b, A, Bc, B, T, D, ws, ws_bytes, s);
         case 4: return run_fwd<bf16_t, 4>(a, b, A, Bc, B, T, D, ws, ws_bytes, s);
@@ -546,6 +554,7 @@ mi_status launch_linear_bwd(const void *a, const void *A, const void *Bc, const 
             default: return run_bwd<float, 1>(a, A, Bc, gA, gBc, da, db, B, T, D, ws, ws_bytes, s);
         }
     }
+    if (vec > MISCAN_LIN_BWD_BF16_VMAX) vec = MISCAN_LIN_BWD_BF16_VMAX;
     switch (vec) {
         case 8: return run_bwd<bf16_t, 8>(a, A, Bc, gA, gBc, da, db, B, T, D, ws, ws_bytes, s);
         case 4: return run_bwd<bf16_t, 4>(a, A, Bc, gA, gBc, da, db, B, T, D, ws, ws_bytes, s);

@@ -56,6 +56,11 @@ struct LogOp {
     }
 };
 
+// Predecessors whose payload loads one look-back round trip issues.
+#ifndef MISCAN_LOG_BATCH
+#define MISCAN_LOG_BATCH 8
+#endif
+
 template <typename T, int VEC, int L, int NW>
 __global__ __launch_bounds__(NW * 64) void log_fwd_kernel(LogArgs p) {
     using PK = Pack<T, VEC>;
@@ -158,7 +163,7 @@ __global__ __launch_bounds__(NW * 64) void log_fwd_kernel(LogArgs p) {
                 }
             }
         }
-        wg_lookback<LogOp, TILE, NT>(p.ws, slot, -1, chunk, c, in, &s_k);
+        wg_lookback<LogOp, TILE, NT, MISCAN_LOG_BATCH>(p.ws, slot, -1, chunk, c, in, &s_k);
 #pragma unroll
         for (int q = 0; q < CPT; ++q) {
             const int ch = threadIdx.x + q * NT;
@@ -199,10 +204,14 @@ __global__ __launch_bounds__(NW * 64) void log_fwd_kernel(LogArgs p) {
 }
 
 #ifndef MISCAN_LOG_L
-#define MISCAN_LOG_L 8
+#define MISCAN_LOG_L 16
 #endif
 #ifndef MISCAN_LOG_NW
 #define MISCAN_LOG_NW 8
+#endif
+// Widest fp32 vector (elements per lane); narrower tiles mean more work items.
+#ifndef MISCAN_LOG_F32_VMAX
+#define MISCAN_LOG_F32_VMAX 4
 #endif
 template <typename T, int VEC> struct LogShape {
     static constexpr int L = MISCAN_LOG_L, NW = MISCAN_LOG_NW;
@@ -258,6 +267,7 @@ mi_status launch_log_fwd(const void *lc, const void *lv, void *h, int64_t B, int
                          int64_t D, mi_dtype dt, int vec, void *ws, size_t ws_bytes,
                          hipStream_t s) {
     if (dt == MI_F32) {
+        if (vec > MISCAN_LOG_F32_VMAX) vec = MISCAN_LOG_F32_VMAX;
         switch (vec) {
             case 4: return run_log<float, 4>(lc, lv, h, B, T, D, ws, ws_bytes, s);
             case 2: return run_log<float, 2>(lc, lv, h, B, T, D, ws, ws_bytes, s);

@@ -12,7 +12,8 @@
  * which core computes a channel, never the arithmetic inside it.
  *
  * The two backward functions are gradients.  The page fixes only their contract
- * (inputs, outputs, "grads w.r.t. the forward inputs"); the formulas used here
+ * (inputs, outputs, and that the outputs are the gradients with respect to the
+ * forward inputs); the formulas used here
  * are the chain rule applied to the forward definitions, derived step by step in
  * the comments and pinned by finite differences and brute-force Jacobians in
  * tests/test_oracle.py.

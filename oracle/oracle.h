@@ -13,7 +13,7 @@
  *
  * Conventions shared by every function:
  *   - every array is a contiguous, row-major fp64 buffer owned by the caller;
- *   - "time t = 1..T" of the page is row t-1 of the T axis;
+ *   - time step t (counted from 1 to T) is row t-1 of the T axis;
  *   - work is sequential in time; independent channels (or heads) may run on
  *     separate OpenMP threads, which does not change any result;
  *   - no function allocates device memory, none fails: sizes are trusted.
