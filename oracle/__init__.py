@@ -51,10 +51,12 @@ def _load():
         lib.lrs_oracle_linear_bwd.argtypes = [i64, i64, i64] + [p] * 7
         lib.lrs_oracle_scan_log_fwd.argtypes = [i64, i64, i64, p, p, p]
         lib.lrs_oracle_scan_log_fwd_logspace.argtypes = [i64, i64, i64, p, p, p]
+        lib.lrs_oracle_scan_log_bwd.argtypes = [i64, i64, i64] + [p] * 6
         lib.lrs_oracle_affine_fwd.argtypes = [i64] * 5 + [p] * 4
         lib.lrs_oracle_affine_bwd.argtypes = [i64] * 5 + [p] * 7
         for f in ("lrs_oracle_linear_fwd", "lrs_oracle_linear_bwd",
                   "lrs_oracle_scan_log_fwd", "lrs_oracle_scan_log_fwd_logspace",
+                  "lrs_oracle_scan_log_bwd",
                   "lrs_oracle_affine_fwd", "lrs_oracle_affine_bwd"):
             getattr(lib, f).restype = None
         _lib = lib
@@ -125,6 +127,19 @@ def scan_log_fwd_logspace(log_coeffs, log_values):
     h = np.empty_like(lc)
     _load().lrs_oracle_scan_log_fwd_logspace(Bn, T, D, _ptr(lc), _ptr(lv), _ptr(h))
     return h
+
+
+def scan_log_bwd(log_coeffs, log_values, h, g):
+    """(dlog_coeffs (B,T,D), dlog_values (B,T+1,D)): gradient of scan_log_fwd,
+    with the forward output h and the upstream gradient g = dL/dh."""
+    lc, lv, h, g = _f64(log_coeffs), _f64(log_values), _f64(h), _f64(g)
+    Bn, T, D = _log_shapes(lc, lv)
+    if h.shape != lc.shape or g.shape != lc.shape:
+        raise ValueError("h and g must be (B, T, D)")
+    dlc = np.empty_like(lc)
+    dlv = np.empty_like(lv)
+    _load().lrs_oracle_scan_log_bwd(Bn, T, D, _ptr(lc), _ptr(lv), _ptr(h), _ptr(g), _ptr(dlc), _ptr(dlv))
+    return dlc, dlv
 
 
 def affine_scan_fwd(A, Bm):

@@ -165,6 +165,49 @@ void lrs_oracle_scan_log_fwd_logspace(int64_t B, int64_t T, int64_t D,
 }
 
 /* ------------------------------------------------------------------------- */
+/* Gradient of parallel_scan_log_fwd.  The page ships the log-space scan as  */
+/* a forward op only ("Triton kernels" page, Kernel entry points:            */
+/* parallel_scan_log_fwd); this is the adjoint of that forward definition.   */
+/* With a_t = exp(log a_t), b_t = exp(log b_t), h_0 = exp(log h_0) and g_t = */
+/* dL/dh_t the upstream gradient of output t, the total derivative          */
+/*     lam_t = dL/dh_t (through every later state)                           */
+/*           = g_t + a_{t+1} lam_{t+1},   a_{T+1} = 0,                        */
+/* and since h_t = a_t h_{t-1} + b_t:                                         */
+/*     d log a_t = lam_t * dh_t/dlog a_t = lam_t a_t h_{t-1}   (t = 1..T),   */
+/*     d log b_t = lam_t * dh_t/dlog b_t = lam_t b_t           (t = 1..T),   */
+/*     d log h_0 = (dL/dh_0) h_0 = a_1 lam_1 h_0.                             */
+/* h_1..h_T are taken from the given forward output h (not recomputed);     */
+/* h_0 comes from log_values slot 0.  dlog_values has slot 0 and slots 1..T */
+/* like log_values.                                                           */
+/* ------------------------------------------------------------------------- */
+void lrs_oracle_scan_log_bwd(int64_t B, int64_t T, int64_t D,
+                             const double *log_coeffs, const double *log_values,
+                             const double *h, const double *g,
+                             double *dlog_coeffs, double *dlog_values) {
+    int64_t channels = B * D;
+#ifdef _OPENMP
+#pragma omp parallel for schedule(static)
+#endif
+    for (int64_t c = 0; c < channels; ++c) {
+        int64_t bb = c / D, dd = c % D;
+        double h0 = exp(log_values[idx3(bb, 0, dd, T + 1, D)]);
+        double lam = 0.0, a_next = 0.0; /* lam_{T+1} = 0, a_{T+1} = 0 */
+        for (int64_t t = T; t >= 1; --t) {
+            int64_t i = idx3(bb, t - 1, dd, T, D);
+            double a_t = exp(log_coeffs[i]);
+            double b_t = exp(log_values[idx3(bb, t, dd, T + 1, D)]);
+            double h_prev = (t > 1) ? h[idx3(bb, t - 2, dd, T, D)] : h0;
+            lam = g[i] + a_next * lam;
+            dlog_coeffs[i] = lam * a_t * h_prev;
+            dlog_values[idx3(bb, t, dd, T + 1, D)] = lam * b_t;
+            a_next = a_t;
+        }
+        /* lam now holds lam_1 and a_next holds a_1 (0 when T = 0) */
+        dlog_values[idx3(bb, 0, dd, T + 1, D)] = a_next * lam * h0;
+    }
+}
+
+/* ------------------------------------------------------------------------- */
 /* k x k helpers on row-major dense matrices (plain triple loops).            */
 /* ------------------------------------------------------------------------- */
 

@@ -60,6 +60,14 @@ void lrs_oracle_scan_log_fwd_logspace(int64_t B, int64_t T, int64_t D,
                                       const double *log_coeffs,
                                       const double *log_values, double *h);
 
+/* Gradient of the log-space scan: dlog_coeffs (B,T,D) and dlog_values
+ * (B,T+1,D, slot 0 = d log h_0) from log_coeffs, log_values, the forward
+ * output h (B,T,D) and the upstream gradient g = dL/dh (B,T,D). */
+void lrs_oracle_scan_log_bwd(int64_t B, int64_t T, int64_t D,
+                             const double *log_coeffs, const double *log_values,
+                             const double *h, const double *g,
+                             double *dlog_coeffs, double *dlog_values);
+
 /* affine_scan_fwd: A is (B,T,n,k,k), Bm is (B,T,n,k,v).  Abar_t = A_t @ Abar_{t-1}
  * (A_current @ A_earlier) with Abar_0 = I; Bbar_t = A_t @ Bbar_{t-1} + Bm_t with
  * Bbar_0 = 0.  Outputs have the input shapes. */

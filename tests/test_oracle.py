@@ -270,6 +270,99 @@ def test_log_extreme_range():
 
 
 # --------------------------------------------------------------------------
+# log-space backward (the adjoint of parallel_scan_log_fwd)
+# --------------------------------------------------------------------------
+
+def _loss_log(lc, lv, g):
+    return float(np.sum(g * oracle.scan_log_fwd(lc, lv)))
+
+
+def test_log_bwd_finite_differences():
+    """Central differences of L = <g, h(lc, lv)> with respect to every entry of
+    log_coeffs and log_values (slot 0 included), fp64, T <= 8."""
+    from workloads import log_inputs
+    eps = 1e-6
+    for T in (1, 2, 5, 8):
+        x = log_inputs(1, T, 2, seed=120 + T)
+        lc, lv = x["log_coeffs"], x["log_values"]
+        g = rng(130 + T).standard_normal(lc.shape)
+        h = oracle.scan_log_fwd(lc, lv)
+        dlc, dlv = oracle.scan_log_bwd(lc, lv, h, g)
+        for arr, grad in ((lc, dlc), (lv, dlv)):
+            for idx in np.ndindex(arr.shape):
+                xp, xm = arr.copy(), arr.copy()
+                xp[idx] += eps
+                xm[idx] -= eps
+                if arr is lc:
+                    fd = (_loss_log(xp, lv, g) - _loss_log(xm, lv, g)) / (2 * eps)
+                else:
+                    fd = (_loss_log(lc, xp, g) - _loss_log(lc, xm, g)) / (2 * eps)
+                assert abs(fd - grad[idx]) <= 1e-7 * max(1.0, abs(fd)), (T, idx, fd, grad[idx])
+
+
+def test_log_bwd_matches_linear_adjoint():
+    """The log scan is the linear scan with a = e^lc, b = e^lv and h = A h0 + Bc.
+    By the chain rule dlc = a * da and dlv_t = b_t * db_t, where (da, db) is the
+    linear backward with gA = h0 g and gBc = g; and d log h0 = h0 * sum_t g_t A_t
+    (a plain numpy sum, a formula of its own)."""
+    from workloads import log_inputs
+    x = log_inputs(2, 700, 5, seed=131)
+    lc, lv = x["log_coeffs"], x["log_values"]
+    g = rng(132).standard_normal(lc.shape)
+    h = oracle.scan_log_fwd(lc, lv)
+    dlc, dlv = oracle.scan_log_bwd(lc, lv, h, g)
+    a, b, h0 = np.exp(lc), np.exp(lv[:, 1:]), np.exp(lv[:, :1])
+    A, Bc = oracle.linear_scan_fwd(a, b)
+    da, db = oracle.linear_scan_bwd(a, A, Bc, g * h0, g)
+    np.testing.assert_allclose(dlc, a * da, rtol=1e-11, atol=1e-300)
+    np.testing.assert_allclose(dlv[:, 1:], b * db, rtol=1e-11, atol=1e-300)
+    np.testing.assert_allclose(dlv[:, 0], h0[:, 0] * np.sum(g * A, axis=1), rtol=1e-11)
+
+
+def test_log_bwd_autograd_bruteforce():
+    """Jacobian^T g from torch autograd (fp64, CPU) on the explicit unrolled
+    forward h_t = h0 prod_{s<=t} a_s + sum_s b_s prod_{s<r<=t} a_r, T <= 8."""
+    torch = pytest.importorskip("torch")
+    from workloads import log_inputs
+    for T in (1, 3, 8):
+        x = log_inputs(2, T, 3, seed=140 + T)
+        lc, lv = x["log_coeffs"], x["log_values"]
+        g = rng(150 + T).standard_normal(lc.shape)
+        tlc = torch.tensor(lc, requires_grad=True)
+        tlv = torch.tensor(lv, requires_grad=True)
+        a, b, h0 = torch.exp(tlc), torch.exp(tlv[:, 1:]), torch.exp(tlv[:, 0])
+        hs = []
+        for t in range(T):
+            acc = h0 * torch.prod(a[:, :t + 1], dim=1)
+            for s in range(t + 1):
+                acc = acc + torch.prod(a[:, s + 1:t + 1], dim=1) * b[:, s]
+            hs.append(acc)
+        L = (torch.stack(hs, 1) * torch.tensor(g)).sum()
+        L.backward()
+        h = oracle.scan_log_fwd(lc, lv)
+        dlc, dlv = oracle.scan_log_bwd(lc, lv, h, g)
+        np.testing.assert_allclose(dlc, tlc.grad.numpy(), rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(dlv, tlv.grad.numpy(), rtol=1e-12, atol=1e-14)
+
+
+def test_log_bwd_unit_coefficients():
+    """log a = 0 (a = 1): lam is the reverse cumulative sum of g (numpy), so
+    dlc_t = lam_t h_{t-1}, dlv_t = lam_t b_t and d log h0 = lam_1 h0."""
+    r = rng(160)
+    T, D = 50, 4
+    lc = np.zeros((1, T, D))
+    lv = np.log(r.uniform(0.1, 1.0, size=(1, T + 1, D)))
+    g = r.standard_normal((1, T, D))
+    h = oracle.scan_log_fwd(lc, lv)
+    dlc, dlv = oracle.scan_log_bwd(lc, lv, h, g)
+    lam = np.cumsum(g[:, ::-1], axis=1)[:, ::-1]
+    h_prev = np.concatenate([np.exp(lv[:, :1]), h[:, :-1]], axis=1)
+    np.testing.assert_allclose(dlc, lam * h_prev, rtol=1e-12)
+    np.testing.assert_allclose(dlv[:, 1:], lam * np.exp(lv[:, 1:]), rtol=1e-12)
+    np.testing.assert_allclose(dlv[:, 0], lam[:, 0] * np.exp(lv[:, 0]), rtol=1e-12)
+
+
+# --------------------------------------------------------------------------
 # k x k forward
 # --------------------------------------------------------------------------
 
