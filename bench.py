@@ -13,7 +13,7 @@ every input read once and every output written once -- per second), the
 roofline of the dominant kernel (HIP events on the stream the kernels run on)
 and the fp64 CPU oracle timed on a bounded sample of the same workload.
 
-  python bench.py [--steps K] [--warmup W] [--workload {1..5}] [--no-cpu-baseline]
+  python bench.py [--steps K] [--warmup W] [--workload {1..6}] [--no-cpu-baseline]
 """
 from __future__ import annotations
 
@@ -120,7 +120,17 @@ def build_workload(wid, torch, lrs, workloads, on_device=False):
         def logf():
             lrs.mi_scan_log_fwd(d["log_coeffs"], d["log_values"], state["h"], ws=ws)
         kernels.append(("scan_log_fwd", logf, es * (3 * N + Bn * D)))
-        desc = {"workload": "parallel_scan_log_fwd, B=%d, T=%d, D=%d, fp32" % (Bn, T, D),
+        if "g" in d:
+            state["dlc"] = torch.empty_like(d["log_coeffs"])
+            state["dlv"] = torch.empty_like(d["log_values"])
+
+            def logb():
+                lrs.mi_scan_log_bwd(d["log_coeffs"], d["log_values"], state["h"], d["g"], state["dlc"],
+                                    state["dlv"], ws=ws)
+            # reads lc, lv, h, g; writes dlc, dlv (lv and dlv have T + 1 rows)
+            kernels.append(("scan_log_bwd", logb, es * (6 * N + 2 * Bn * D)))
+        desc = {"workload": "parallel_scan_log_%s, B=%d, T=%d, D=%d, fp32"
+                % ("fwd+bwd" if len(kernels) == 2 else "fwd", Bn, T, D),
                 "B": Bn, "T": T, "D": D, "storage": w["dtype"]}
         units = N
     else:
@@ -179,15 +189,18 @@ def cpu_baseline(wid, torch, workloads):
             Bs, w["B"], w["T"], w["D"], n, "+bwd" if wid == 3 else "")
     elif w["op"] == "log":
         Bs = 1
-        x = workloads.log_inputs(Bs, w["T"], w["D"], wid)
-        lc, lv = q(x["log_coeffs"]), q(x["log_values"])
+        x = workloads.log_inputs(Bs, w["T"], w["D"], wid, grads=(wid == 6))
+        x = {k: q(v) for k, v in x.items()}
+        lc, lv = x["log_coeffs"], x["log_values"]
         n = Bs * w["T"] * w["D"]
 
         def run():
-            oracle.scan_log_fwd(lc, lv)
+            h = oracle.scan_log_fwd(lc, lv)
+            if wid == 6:
+                oracle.scan_log_bwd(lc, lv, h, x["g"])
 
-        nbytes = 4 * (3 * n + w["D"])
-        sample = "B=1 of %d batch rows: %d elements" % (w["B"], n)
+        nbytes = 4 * (3 * n + w["D"]) + (4 * (6 * n + 2 * w["D"]) if wid == 6 else 0)
+        sample = "B=1 of %d batch rows: %d elements%s" % (w["B"], n, ", fwd+bwd" if wid == 6 else "")
     else:
         Bs = 1
         gen = workloads.affine_inputs_rotation if wid == 4 else workloads.affine_inputs_diag
@@ -239,7 +252,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", type=int, default=3, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--workload", type=int, default=3, choices=[1, 2, 3, 4, 5, 6])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cold", action="store_true",
                     help="also time each kernel alone after writing 1 GiB to evict the caches")

@@ -99,7 +99,7 @@ mi_status mi_linear_scan_bwd(const void *a, const void *A, const void *Bc,
 /* parallel_scan_log_fwd).  Dtypes: MI_F32, MI_BF16.                        */
 /* ------------------------------------------------------------------------ */
 
-/* Workspace bytes for mi_scan_log_fwd on (B, T, D). */
+/* Workspace bytes for mi_scan_log_fwd and mi_scan_log_bwd on (B, T, D). */
 size_t mi_scan_log_workspace(int64_t B, int64_t T, int64_t D, mi_dtype dt);
 
 /* parallel_scan_log_fwd: log_coeffs (B,T,D) holds log a_t; log_values (B,T+1,D)
@@ -107,6 +107,25 @@ size_t mi_scan_log_workspace(int64_t B, int64_t T, int64_t D, mi_dtype dt);
  * (B,T,D) tensor `h`, where h_t = a_t h_{t-1} + b_t.  The scan state is kept in
  * log space (log-sum-exp combine); only the stored states are exponentiated. */
 mi_status mi_scan_log_fwd(const void *log_coeffs, const void *log_values, void *h,
+                          int64_t B, int64_t T, int64_t D, mi_dtype dt,
+                          void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Gradient of parallel_scan_log_fwd.  The page defines the log-space scan as
+ * a forward op; this is the adjoint of that forward definition, for training
+ * through it.  Inputs: log_coeffs (B,T,D) and log_values (B,T+1,D) as in the
+ * forward, h (B,T,D) the forward output, g (B,T,D) the upstream gradient
+ * dL/dh.  Outputs: dlog_coeffs (B,T,D) and dlog_values (B,T+1,D), slot 0 being
+ * the gradient of log h_0:
+ *     lam_t = g_t + a_{t+1} lam_{t+1} (a_{T+1} = 0),
+ *     dlog_coeffs_t = lam_t a_t h_{t-1},  dlog_values_t = lam_t b_t (t >= 1),
+ *     dlog_values_0 = a_1 lam_1 h_0,
+ * with a = exp(log_coeffs), b and h_0 = exp(log_values), and h_{t-1} taken
+ * from the given h (not recomputed).  lam runs in linear space (g is
+ * signed).  Outputs must not overlap inputs or each other; all arithmetic is
+ * fp32, storage as dt.  With T = 0 (and B, D > 0) the only output is slot 0 of
+ * dlog_values, which is set to zero; the other pointers are not used. */
+mi_status mi_scan_log_bwd(const void *log_coeffs, const void *log_values, const void *h,
+                          const void *g, void *dlog_coeffs, void *dlog_values,
                           int64_t B, int64_t T, int64_t D, mi_dtype dt,
                           void *ws, size_t ws_bytes, hipStream_t stream);
 

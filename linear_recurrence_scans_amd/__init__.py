@@ -22,9 +22,9 @@ __all__ = [
     "MiscanError", "available", "library_path",
     "mi_status_string", "mi_device_check",
     "mi_linear_scan_workspace", "mi_linear_scan_fwd", "mi_linear_scan_bwd",
-    "mi_scan_log_workspace", "mi_scan_log_fwd",
+    "mi_scan_log_workspace", "mi_scan_log_fwd", "mi_scan_log_bwd",
     "mi_affine_scan_workspace", "mi_affine_scan_fwd", "mi_affine_scan_bwd",
-    "linear_scan_fwd", "linear_scan_bwd", "parallel_scan_log_fwd",
+    "linear_scan_fwd", "linear_scan_bwd", "parallel_scan_log_fwd", "parallel_scan_log_bwd",
     "affine_scan_fwd", "affine_scan_bwd",
 ]
 
@@ -45,6 +45,7 @@ _SIGS = {
     "mi_linear_scan_bwd": ([_V] * 7 + [_I64] * 3 + [_I, _V, _SZ, _V], _I),
     "mi_scan_log_workspace": ([_I64, _I64, _I64, _I], _SZ),
     "mi_scan_log_fwd": ([_V] * 3 + [_I64] * 3 + [_I, _V, _SZ, _V], _I),
+    "mi_scan_log_bwd": ([_V] * 6 + [_I64] * 3 + [_I, _V, _SZ, _V], _I),
     "mi_affine_scan_workspace": ([_I64] * 5 + [_I], _SZ),
     "mi_affine_scan_fwd": ([_V] * 4 + [_I64] * 5 + [_I, _V, _SZ, _V], _I),
     "mi_affine_scan_bwd": ([_V] * 7 + [_I64] * 5 + [_I, _V, _SZ, _V], _I),
@@ -230,6 +231,28 @@ def mi_scan_log_fwd(log_coeffs, log_values, h=None, *, ws=None, stream=None):
     return h
 
 
+def mi_scan_log_bwd(log_coeffs, log_values, h, g, dlog_coeffs=None, dlog_values=None, *, ws=None, stream=None):
+    """(dlog_coeffs (B,T,D), dlog_values (B,T+1,D)): gradient of parallel_scan_log_fwd
+    given its output h (B,T,D) and the upstream gradient g = dL/dh (B,T,D)."""
+    lc, lv = _dev_tensor(log_coeffs, "log_coeffs"), _dev_tensor(log_values, "log_values")
+    h, g = _dev_tensor(h, "h"), _dev_tensor(g, "g")
+    if lc.dim() != 3 or lv.dim() != 3 or lv.shape != (lc.shape[0], lc.shape[1] + 1, lc.shape[2]):
+        raise ValueError("log_coeffs must be (B, T, D) and log_values (B, T+1, D)")
+    if h.shape != lc.shape or g.shape != lc.shape:
+        raise ValueError("h and g must be (B, T, D)")
+    _same(lc, lv, h, g)
+    dlc, dlv = _out(dlog_coeffs, lc, "dlog_coeffs"), _out(dlog_values, lv, "dlog_values")
+    Bn, T, D = lc.shape
+    dt = _dt(lc)
+    nbytes = _load().mi_scan_log_workspace(Bn, T, D, dt)
+    ws = _workspace(ws, nbytes, lc.device)
+    st = _load().mi_scan_log_bwd(lc.data_ptr(), lv.data_ptr(), h.data_ptr(), g.data_ptr(), dlc.data_ptr(),
+                                 dlv.data_ptr(), Bn, T, D, dt, ws.data_ptr(), ws.numel() * ws.element_size(),
+                                 _stream(stream, lc.device))
+    _check(st, "mi_scan_log_bwd")
+    return dlc, dlv
+
+
 # ---------------------------------------------------------------------------
 # k x k matrix-affine scan
 # ---------------------------------------------------------------------------
@@ -295,6 +318,11 @@ def linear_scan_bwd(a, A, Bc, gA, gBc):
 
 def parallel_scan_log_fwd(log_coeffs, log_values):
     return mi_scan_log_fwd(log_coeffs, log_values)
+
+
+def parallel_scan_log_bwd(log_coeffs, log_values, h, g):
+    """Adjoint of parallel_scan_log_fwd (not an op of the page: added for training)."""
+    return mi_scan_log_bwd(log_coeffs, log_values, h, g)
 
 
 def affine_scan_fwd(A, Bm):

@@ -28,6 +28,12 @@ mi_status clear_workspace(const WsPtrs &w, size_t n_slots, hipStream_t stream) {
     return launch_status();
 }
 
+// Zero n bytes (a grid-stride byte loop; used only for tiny outputs).
+__global__ void zero_bytes_kernel(uint8_t *p, size_t n) {
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+        p[i] = 0;
+}
+
 namespace {
 
 size_t elem_size(mi_dtype dt) { return dt == MI_BF16 ? 2 : 4; }
@@ -210,6 +216,33 @@ mi_status mi_scan_log_fwd(const void *log_coeffs, const void *log_values, void *
     if ((st = check_ws(ws, ws_bytes, log_workspace_bytes(B, T, D, dt), bufs, 3)) != MI_OK) return st;
     const int vec = pick_vec(D, elem_size(dt), bufs, 3);
     return launch_log_fwd(log_coeffs, log_values, h, B, T, D, dt, vec, ws, ws_bytes, stream);
+}
+
+mi_status mi_scan_log_bwd(const void *log_coeffs, const void *log_values, const void *h, const void *g,
+                          void *dlog_coeffs, void *dlog_values, int64_t B, int64_t T, int64_t D, mi_dtype dt,
+                          void *ws, size_t ws_bytes, hipStream_t stream) {
+    int64_t bytes;
+    bool empty;
+    mi_status st = check_btd(B, T, D, dt, &bytes, &empty);
+    if (st != MI_OK) return st;
+    if (empty && T == 0 && B > 0 && D > 0) {
+        // dlog_values still has its slot 0, d log h_0 = 0 when there is no step
+        const Buf out{dlog_values, B * D * (int64_t)elem_size(dt)};
+        if (out.p == nullptr || reinterpret_cast<uintptr_t>(out.p) % elem_size(dt) != 0) return MI_ERR_INVALID_ARG;
+        const size_t n = (size_t)out.bytes;
+        const unsigned blocks = (unsigned)std::min<size_t>(256, (n + 255) / 256);
+        hipLaunchKernelGGL(zero_bytes_kernel, dim3(blocks), dim3(256), 0, stream, (uint8_t *)dlog_values, n);
+        return launch_status();
+    }
+    if (empty) return st;
+    const int64_t lv_bytes = B * (T + 1) * D * (int64_t)elem_size(dt);
+    const Buf bufs[6] = {{log_coeffs, bytes}, {log_values, lv_bytes}, {h, bytes},
+                         {g, bytes},          {dlog_coeffs, bytes},   {dlog_values, lv_bytes}};
+    if ((st = check_buffers(bufs, 6, 2, elem_size(dt))) != MI_OK) return st;
+    if ((st = check_ws(ws, ws_bytes, log_workspace_bytes(B, T, D, dt), bufs, 6)) != MI_OK) return st;
+    const int vec = pick_vec(D, elem_size(dt), bufs, 6);
+    return launch_log_bwd(log_coeffs, log_values, h, g, dlog_coeffs, dlog_values, B, T, D, dt, vec, ws, ws_bytes,
+                          stream);
 }
 
 }  // extern "C"

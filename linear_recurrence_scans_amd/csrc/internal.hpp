@@ -24,6 +24,9 @@ size_t log_workspace_bytes(int64_t B, int64_t T, int64_t D, mi_dtype dt);
 mi_status launch_log_fwd(const void *lc, const void *lv, void *h,
                          int64_t B, int64_t T, int64_t D, mi_dtype dt, int vec,
                          void *ws, size_t ws_bytes, hipStream_t s);
+mi_status launch_log_bwd(const void *lc, const void *lv, const void *h, const void *g, void *dlc, void *dlv,
+                         int64_t B, int64_t T, int64_t D, mi_dtype dt, int vec, void *ws, size_t ws_bytes,
+                         hipStream_t s);
 
 // k x k scan (B, T, n, k, v).
 size_t affine_workspace_bytes(int64_t B, int64_t T, int64_t n, int64_t k, int64_t v);

@@ -112,6 +112,23 @@ def test_log_validation():
     assert L.mi_scan_log_fwd(lc, lv, h, 2, 8, 8, 5, None, 0, None) == MI_ERR_UNSUPPORTED
 
 
+def test_log_bwd_validation():
+    L = lib()
+    lc, lv, h, g, dlc, dlv, ws = ptrs(7)
+    args = lambda **kw: [kw.get(k, v) for k, v in
+                         (("lc", lc), ("lv", lv), ("h", h), ("g", g), ("dlc", dlc), ("dlv", dlv))]
+    assert L.mi_scan_log_bwd(*args(), 2, 8, 8, F32, None, 0, None) == MI_ERR_WORKSPACE
+    # dlog_values (T+1 rows) overlapping the start of g
+    assert L.mi_scan_log_bwd(*args(dlv=g - 8 * 4), 2, 8, 8, F32, ws, 1 << 40, None) == MI_ERR_INVALID_ARG
+    # dlog_coeffs aliasing h
+    assert L.mi_scan_log_bwd(*args(dlc=h), 2, 8, 8, F32, ws, 1 << 40, None) == MI_ERR_INVALID_ARG
+    assert L.mi_scan_log_bwd(*args(g=None), 2, 8, 8, F32, ws, 1 << 40, None) == MI_ERR_INVALID_ARG
+    assert L.mi_scan_log_bwd(*args(), 2, 8, 8, 5, ws, 1 << 40, None) == MI_ERR_UNSUPPORTED
+    assert L.mi_scan_log_bwd(*args(), 0, 5, 8, F32, None, 0, None) == MI_OK  # B = 0: nothing to do
+    # T = 0 still zeroes dlog_values' slot 0 (a launch), but checks its pointer first
+    assert L.mi_scan_log_bwd(*args(dlv=None), 2, 0, 8, F32, None, 0, None) == MI_ERR_INVALID_ARG
+
+
 def test_affine_envelope():
     L = lib()
     A, Bm, Ab, Bb, ws = ptrs(5)

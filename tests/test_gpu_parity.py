@@ -217,6 +217,70 @@ def test_log_extreme_range():
     assert e <= TOL[torch.float32], e
 
 
+def run_log_bwd(x, dtype, seed=0):
+    """GPU backward of the log scan against the oracle.  Both sides get the
+    same quantised log_coeffs, log_values, forward output h (the oracle's, cast
+    like any input) and upstream gradient g."""
+    lc_d, lc = quantise(x["log_coeffs"], dtype)
+    lv_d, lv = quantise(x["log_values"], dtype)
+    Bn, T, D = lc.shape
+    h_d, h = quantise(oracle.scan_log_fwd(lc, lv), dtype)
+    g_d, g = quantise(np.random.Generator(np.random.PCG64(1000 + seed)).standard_normal(lc.shape), dtype)
+    ws = torch.empty(max(lrs.mi_scan_log_workspace(Bn, T, D, dtype), 8), dtype=torch.uint8, device="cuda")
+    dlc_d, dlv_d = lrs.mi_scan_log_bwd(lc_d, lv_d, h_d, g_d, ws=ws)
+    torch.cuda.synchronize()
+    assert timeouts(ws) == 0
+    dlc_r, dlv_r = oracle.scan_log_bwd(lc, lv, h, g)
+    dlc_s, dlv_s = oracle.scan_log_bwd(lc, lv, h, np.abs(g))  # every other factor is positive
+    return {"dlc": scaled_err(to_np(dlc_d), dlc_r, dlc_s), "dlv": scaled_err(to_np(dlv_d), dlv_r, dlv_s)}
+
+
+@pytest.mark.parametrize("seed", [2, 12])
+def test_log_bwd_workload2_full(seed):
+    """Backward of the log scan at the workload-2 size (B=4, T=4096, D=512, fp32)."""
+    say("log bwd fp32 B=4 T=4096 D=512 seed", seed)
+    errs = run_log_bwd(workload_inputs(2, seed=seed), torch.float32, seed)
+    print("errors", errs, flush=True)
+    assert max(errs.values()) <= TOL[torch.float32], errs
+
+
+@pytest.mark.parametrize("shape", [(1, 1, 1), (2, 63, 3), (1, 65, 100), (2, 1000, 5), (1, 4097, 64),
+                                   (3, 200, 260)])
+def test_log_bwd_edge_shapes(shape):
+    say("log bwd fp32 edge shape", shape)
+    errs = run_log_bwd(log_inputs(*shape, seed=sum(shape)), torch.float32, sum(shape))
+    assert max(errs.values()) <= TOL[torch.float32], (shape, errs)
+
+
+@pytest.mark.parametrize("shape", [(2, 500, 136), (1, 77, 37), (3, 129, 6)])
+def test_log_bwd_bf16(shape):
+    """bf16 storage, fp32 arithmetic; D values pick 8-, 1- and 2-wide vectors."""
+    say("log bwd bf16 shape", shape)
+    errs = run_log_bwd(log_inputs(*shape, seed=7), torch.bfloat16, 7)
+    assert max(errs.values()) <= TOL[torch.bfloat16], (shape, errs)
+
+
+def test_log_bwd_no_steps():
+    """T = 0: the only output is d log h_0, which is zero."""
+    say("log bwd fp32 T=0 B=2 D=8")
+    lc = torch.empty(2, 0, 8, device="cuda")
+    lv = torch.zeros(2, 1, 8, device="cuda")
+    h = torch.empty(2, 0, 8, device="cuda")
+    dlv = torch.full((2, 1, 8), float("nan"), device="cuda")
+    dlc, dlv = lrs.mi_scan_log_bwd(lc, lv, h, h, dlog_values=dlv)
+    torch.cuda.synchronize()
+    assert dlc.numel() == 0 and bool(torch.all(dlv == 0))
+
+
+def test_log_bwd_repeated_runs():
+    """Runs agree to rounding and each matches the oracle (look-back race check)."""
+    say("log bwd fp32 three repeated runs B=2 T=3000 D=256")
+    x = log_inputs(2, 3000, 256, seed=21)
+    outs = [run_log_bwd(x, torch.float32, 21) for _ in range(3)]
+    for errs in outs:
+        assert max(errs.values()) <= TOL[torch.float32], errs
+
+
 # ---------------------------------------------------------------------------
 # k x k scan
 # ---------------------------------------------------------------------------

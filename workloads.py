@@ -34,6 +34,8 @@ WORKLOADS = {
     3: dict(name="linear_fwd_bwd", op="linear", dtype="bf16", B=8, T=8192, D=4096),
     4: dict(name="affine_fwd_k4", op="affine", dtype="f32", B=2, T=2048, n=64, k=4, v=16),
     5: dict(name="affine_fwd_bwd_k8", op="affine", dtype="f32", B=4, T=4096, n=32, k=8, v=32),
+    # the log-space scan's forward and its adjoint at the workload-2 size
+    6: dict(name="log_fwd_bwd", op="log", dtype="f32", B=4, T=4096, D=512),
 }
 
 
@@ -52,10 +54,11 @@ def linear_inputs(B, T, D, seed, a_lo=0.5, a_hi=0.999, grads=False):
     return out
 
 
-def log_inputs(B, T, D, seed):
+def log_inputs(B, T, D, seed, grads=False):
     """log_coeffs (B,T,D) = -softplus(x), x~N(0,1), taken as -logaddexp(0, x);
     log_values (B,T+1,D): slot 0 = log h0 with h0~U(0.1,1) per (b,d);
-    slots 1..T = log(sigmoid(y) * u), y~N(0,1), u~U(0.1,1)."""
+    slots 1..T = log(sigmoid(y) * u), y~N(0,1), u~U(0.1,1).
+    grads: also an upstream gradient g = dL/dh (B,T,D) ~ N(0,1)."""
     g = rng(seed)
     x = g.standard_normal(size=(B, T, D))
     log_coeffs = -np.logaddexp(0.0, x)
@@ -65,7 +68,10 @@ def log_inputs(B, T, D, seed):
     # log(sigmoid(y)) = -logaddexp(0, -y)
     lv_rest = -np.logaddexp(0.0, -y) + np.log(u)
     log_values = np.concatenate([np.log(h0), lv_rest], axis=1)
-    return {"log_coeffs": log_coeffs, "log_values": log_values}
+    out = {"log_coeffs": log_coeffs, "log_values": log_values}
+    if grads:
+        out["g"] = g.standard_normal(size=(B, T, D))
+    return out
 
 
 def haar_orthogonal(g: np.random.Generator, shape, k):
@@ -104,7 +110,7 @@ def affine_inputs_diag(B, T, n, k, v, seed, grads=False):
 
 
 def workload_inputs(wid: int, seed: int | None = None, **shape):
-    """Inputs of workload ``wid`` (1..5) at its own sizes, or at sizes overridden by
+    """Inputs of workload ``wid`` (1..6) at its own sizes, or at sizes overridden by
     keyword (B, T, D or B, T, n, k, v), with the workload's distributions."""
     w = dict(WORKLOADS[wid])
     w.update(shape)
@@ -119,4 +125,6 @@ def workload_inputs(wid: int, seed: int | None = None, **shape):
         return affine_inputs_rotation(w["B"], w["T"], w["n"], w["k"], w["v"], s)
     if wid == 5:
         return affine_inputs_diag(w["B"], w["T"], w["n"], w["k"], w["v"], s, grads=True)
+    if wid == 6:
+        return log_inputs(w["B"], w["T"], w["D"], s, grads=True)
     raise KeyError(wid)
