@@ -84,22 +84,6 @@ __device__ __forceinline__ void stv(float *dst, const float *src) {
     }
 }
 
-// One row of a k x k block into KP registers, zero padded; `ok` false gives zeros.
-template <int KP, bool VIO>
-__device__ __forceinline__ void load_row(float (&r)[KP], const float *src, bool ok, int k) {
-    if (ok) {
-        if constexpr (VIO) {
-            ldv<KP>(r, src);
-        } else {
-#pragma unroll
-            for (int j = 0; j < KP; ++j) r[j] = (j < k) ? src[j] : 0.f;
-        }
-    } else {
-#pragma unroll
-        for (int j = 0; j < KP; ++j) r[j] = 0.f;
-    }
-}
-
 struct FwdArgs {
     const float *A, *Bm;
     float *Abar, *Bbar;
@@ -114,7 +98,7 @@ struct BwdArgs {
     float *dA, *dB;
     int64_t T, heads;
     int n, k, v;
-    int G, HPW, NCP, n_groups, n_chunks, LC;
+    int G, HPW, NCP, n_groups, n_chunks, NW;
     WsPtrs ws;
 };
 
@@ -138,8 +122,16 @@ struct Cols {
 #ifndef MISCAN_AFF_NWMAX
 #define MISCAN_AFF_NWMAX 8
 #endif
-template <int KP, int CPL> struct AffL {
-    static constexpr int raw = MISCAN_AFF_BREGS * (KP >= 8 ? 2 : 1) / (KP * CPL);
+// The backward holds two such sets (G_t and X_{t-1} columns).
+#ifndef MISCAN_AFF_BWD_BREGS
+#define MISCAN_AFF_BWD_BREGS MISCAN_AFF_BREGS
+#endif
+#ifndef MISCAN_AFF_BWD_NWMAX
+#define MISCAN_AFF_BWD_NWMAX 4
+#endif
+template <int KP, int CPL, bool BWD = false> struct AffL {
+    static constexpr int regs = BWD ? MISCAN_AFF_BWD_BREGS : MISCAN_AFF_BREGS;
+    static constexpr int raw = regs * (KP >= 8 ? 2 : 1) / (KP * CPL);
     static constexpr int L = raw < 1 ? 1 : raw > 16 ? 16 : raw;
 };
 
@@ -291,45 +283,6 @@ __device__ __forceinline__ void payload_store(float *blk, int NCP, int c0, const
 #pragma unroll
         for (int cc = 0; cc < CPL; ++cc) carry_store(blk + i * NCP + c0 + cc, x[i][cc]);
 }
-template <int KP, int CPL>
-__device__ __forceinline__ void payload_load(float (&x)[KP][CPL], const float *blk, int NCP, int c0) {
-#pragma unroll
-    for (int i = 0; i < KP; ++i)
-#pragma unroll
-        for (int cc = 0; cc < CPL; ++cc) x[i][cc] = carry_load(blk + i * NCP + c0 + cc);
-}
-
-// S <- M S (+ add where addmask), column by column.  M is the leading k x k
-// block (zero padded to KP) of a row-major matrix with row stride `ld`, read
-// either from a published payload (PAYLOAD: device-coherent word loads) or
-// from LDS.
-template <int KP, int CPL, bool PAYLOAD>
-__device__ __forceinline__ void mat_apply(float (&S)[KP][CPL], const float *Msrc, int64_t ld, int k,
-                                          const float (&add)[KP][CPL], const bool (&addmask)[CPL]) {
-    float ns[KP][CPL];
-#pragma unroll
-    for (int i = 0; i < KP; ++i) {
-        float mrow[KP];
-#pragma unroll
-        for (int j = 0; j < KP; ++j) {
-            const bool in = i < k && j < k;
-            if constexpr (PAYLOAD) mrow[j] = in ? carry_load(Msrc + i * ld + j) : 0.f;
-            else mrow[j] = in ? Msrc[i * ld + j] : 0.f;
-        }
-#pragma unroll
-        for (int cc = 0; cc < CPL; ++cc) {
-            float s = addmask[cc] ? add[i][cc] : 0.f;
-#pragma unroll
-            for (int j = 0; j < KP; ++j) s = fmaf(mrow[j], S[j][cc], s);
-            ns[i][cc] = s;
-        }
-    }
-#pragma unroll
-    for (int i = 0; i < KP; ++i)
-#pragma unroll
-        for (int cc = 0; cc < CPL; ++cc) S[i][cc] = ns[i][cc];
-}
-
 // S <- M S + [0 | H] for a transform block [M | H] (row-major, row stride
 // NCP, the leading k x k block is M): the add term of each of the lane's H
 // columns comes from the same block, so no copy of it is held in registers.
@@ -562,24 +515,41 @@ __global__ __launch_bounds__(512) void affine_fwd_kernel(FwdArgs p) {
 // Backward
 // ---------------------------------------------------------------------------
 
-// z <- G_t + A_{t+1}^T z for the lane's columns; A_{T+1} = 0.
+// Rows of dA partial sums exchanged through LDS per round.
+#ifndef MISCAN_AFF_RBMAX
+#define MISCAN_AFF_RBMAX 8
+#endif
+template <int KP> struct AffRB {
+    static constexpr int RB = KP < MISCAN_AFF_RBMAX ? KP : MISCAN_AFF_RBMAX;
+};
+
+// Source of the lane's columns of one of two (k x k | k x v) tensor pairs at
+// matrix index m: the k x k tensor for Z_M columns, the k x v tensor for Z_L
+// columns.  Lanes of other kinds (and !ok) point at a valid element and are
+// zeroed by the caller: every lane loads, so no branch sits around the loads.
+template <int CPL>
+__device__ __forceinline__ const float *y_src(const float *kk, const float *kv, const Cols<CPL> &cl, int64_t m,
+                                              int k, int v, bool ok, int &ld) {
+    const bool is_m = ok && cl.kind[0] == Z_M, is_l = ok && cl.kind[0] == Z_L;
+    ld = is_l ? v : k;
+    return is_m ? kk + m * k * k + cl.col[0] : is_l ? kv + m * k * v + cl.col[0] : kk;
+}
+
+// The lane's columns of G_t = [gAbar_t | gBbar_t] (zero for P and padding
+// columns, or when !ok).
 template <int KP, int CPL, bool VIO>
-__device__ __forceinline__ void bwd_scan_step(float (&z)[KP][CPL], const BwdArgs &p, const Cols<CPL> &cl,
-                                              int64_t m, int64_t t, bool active) {
+__device__ __forceinline__ void load_g(float (&g)[KP][CPL], const BwdArgs &p, const Cols<CPL> &cl, int64_t m,
+                                       bool ok) {
     const int k = p.k, v = p.v;
-    float nz[KP][CPL];
     if constexpr (VIO) {
-        if (active && cl.kind[0] == Z_M) {
+        int ld;
+        const float *src = y_src<CPL>(p.gAbar, p.gBbar, cl, m, k, v, ok, ld);
+        const bool use = ok && (cl.kind[0] == Z_M || cl.kind[0] == Z_L);
 #pragma unroll
-            for (int i = 0; i < KP; ++i) ldv<CPL>(nz[i], p.gAbar + m * k * k + i * k + cl.col[0]);
-        } else if (active && cl.kind[0] == Z_L) {
+        for (int i = 0; i < KP; ++i) {
+            ldv<CPL>(g[i], src + i * ld);
 #pragma unroll
-            for (int i = 0; i < KP; ++i) ldv<CPL>(nz[i], p.gBbar + m * k * v + i * v + cl.col[0]);
-        } else {
-#pragma unroll
-            for (int i = 0; i < KP; ++i)
-#pragma unroll
-                for (int cc = 0; cc < CPL; ++cc) nz[i][cc] = 0.f;
+            for (int cc = 0; cc < CPL; ++cc) g[i][cc] = use ? g[i][cc] : 0.f;
         }
     } else {
 #pragma unroll
@@ -587,59 +557,159 @@ __device__ __forceinline__ void bwd_scan_step(float (&z)[KP][CPL], const BwdArgs
 #pragma unroll
             for (int cc = 0; cc < CPL; ++cc) {
                 float gv = 0.f;
-                if (active && i < k) {
+                if (ok && i < k) {
                     if (cl.kind[cc] == Z_M) gv = p.gAbar[m * k * k + i * k + cl.col[cc]];
                     else if (cl.kind[cc] == Z_L) gv = p.gBbar[m * k * v + i * v + cl.col[cc]];
                 }
-                nz[i][cc] = gv;
+                g[i][cc] = gv;
             }
     }
-    // nz[i] += sum_j A_{t+1}[j][i] z[j], one row j of A_{t+1} at a time
-    const bool has_next = active && t + 1 < p.T;
-    const float *An = p.A + (m + p.n) * k * k;
+}
+
+// The lane's columns of X_{t-1} = [Abar_{t-1} | Bbar_{t-1}] matching its Y
+// columns ([I | 0] at t = 0; zero when !ok).
+template <int KP, int CPL, bool VIO>
+__device__ __forceinline__ void load_xprev(float (&x)[KP][CPL], const BwdArgs &p, const Cols<CPL> &cl, int64_t m,
+                                           int64_t t, bool ok) {
+    const int k = p.k, v = p.v;
+    if constexpr (VIO) {
+        int ld;
+        const float *src = y_src<CPL>(p.Abar, p.Bbar, cl, m - p.n, k, v, ok && t > 0, ld);
+        const bool use = ok && t > 0 && (cl.kind[0] == Z_M || cl.kind[0] == Z_L);
 #pragma unroll
-    for (int j = 0; j < KP; ++j) {
-        float arow[KP];
-        load_row<KP, VIO>(arow, An + j * k, has_next && j < k, k);
+        for (int i = 0; i < KP; ++i) {
+            ldv<CPL>(x[i], src + i * ld);
+#pragma unroll
+            for (int cc = 0; cc < CPL; ++cc) {
+                const float id = (ok && t == 0 && cl.kind[cc] == Z_M && i == cl.col[cc]) ? 1.f : 0.f;
+                x[i][cc] = use ? x[i][cc] : id;
+            }
+        }
+    } else {
 #pragma unroll
         for (int i = 0; i < KP; ++i)
 #pragma unroll
-            for (int cc = 0; cc < CPL; ++cc) nz[i][cc] = fmaf(arow[i], z[j][cc], nz[i][cc]);
+            for (int cc = 0; cc < CPL; ++cc) {
+                float xv = 0.f;
+                if (ok && i < k) {
+                    if (cl.kind[cc] == Z_M)
+                        xv = (t > 0) ? p.Abar[(m - p.n) * k * k + i * k + cl.col[cc]] : (i == cl.col[cc] ? 1.f : 0.f);
+                    else if (cl.kind[cc] == Z_L && t > 0)
+                        xv = p.Bbar[(m - p.n) * k * v + i * v + cl.col[cc]];
+                }
+                x[i][cc] = xv;
+            }
     }
-#pragma unroll
-    for (int i = 0; i < KP; ++i)
-#pragma unroll
-        for (int cc = 0; cc < CPL; ++cc) z[i][cc] = nz[i][cc];
 }
 
-template <int KP> struct RowBlock { static constexpr int RB = KP < 8 ? KP : 8; };
+// A_{t+1}^T for the CH steps t of the chunk into LDS, [step][head][AS] like
+// stage_a: zero for t = T - 1 (A_{T+1} = 0 in the page's 1-based time) and the
+// identity for steps past T or heads past the last.  Sources are read as
+// float4 rows and written transposed.
+template <int KP, bool VIO>
+__device__ __forceinline__ void stage_at(float *s_A, const BwdArgs &p, int grp, int64_t t_c, int CH) {
+    constexpr int KK = KP * KP;
+    constexpr int AS = pad_bank(KK);
+    const int per_step = p.HPW * KK;
+    const int total = CH * per_step;
+    const int k = VIO ? KP : p.k;
+    if constexpr (VIO && KP % 4 == 0) {
+        for (int e = (int)threadIdx.x * 4; e < total; e += (int)blockDim.x * 4) {
+            const int s = e / per_step;
+            const int rem = e - s * per_step;
+            const int hs = rem / KK;
+            const int q = rem - hs * KK;
+            const int jr = q / KP, i0 = q - jr * KP;  // source row jr, columns i0 .. i0 + 3
+            const int64_t t = t_c + s;
+            const int64_t gh = (int64_t)grp * p.HPW + hs;
+            float val[4];
+            if (t + 1 < p.T && gh < p.heads) {
+                const int64_t b = gh / p.n, h = gh - b * p.n;
+                const f32x4 w = *reinterpret_cast<const f32x4 *>(p.A + ((b * p.T + t + 1) * p.n + h) * KK + q);
+                val[0] = w.x; val[1] = w.y; val[2] = w.z; val[3] = w.w;
+            } else {
+                const float d = (t < p.T && gh < p.heads) ? 0.f : 1.f;  // A_{T+1} = 0, identity elsewhere
+#pragma unroll
+                for (int u = 0; u < 4; ++u) val[u] = (i0 + u == jr) ? d : 0.f;
+            }
+            float *dst = s_A + (s * p.HPW + hs) * AS;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) dst[(i0 + u) * KP + jr] = val[u];
+        }
+    } else {
+        for (int e = (int)threadIdx.x; e < total; e += (int)blockDim.x) {
+            const int s = e / per_step;
+            const int rem = e - s * per_step;
+            const int hs = rem / KK;
+            const int q = rem - hs * KK;
+            const int i = q / KP, j = q - (q / KP) * KP;  // element (i, j) of A^T = A[j][i]
+            const int64_t t = t_c + s;
+            const int64_t gh = (int64_t)grp * p.HPW + hs;
+            float val;
+            if (t + 1 < p.T && gh < p.heads) {
+                const int64_t b = gh / p.n, h = gh - b * p.n;
+                val = (i < k && j < k) ? p.A[((b * p.T + t + 1) * p.n + h) * k * k + j * k + i] : (i == j ? 1.f : 0.f);
+            } else {
+                val = (i == j) ? ((t < p.T && gh < p.heads) ? 0.f : 1.f) : 0.f;
+            }
+            s_A[(s * p.HPW + hs) * AS + q] = val;
+        }
+    }
+}
 
+// Reverse time.  Y_t = [M_t | Lam_t] = G_t + A_{t+1}^T Y_{t+1}; a chunk's
+// reverse transform is Z = [P | Q]: Y at its first step = P Y_in + Q, with
+// P = A_{t0+1}^T ... A_{t1}^T.  The lane's columns of Z are P (k), M (k) and
+// Lam (v); the algebra is the forward's with Z for X and reverse order.
+// One workgroup = NW waves = HPW heads x one chunk of CH = NW * L steps:
+//  1. every wave loads its steps' G columns into registers; the workgroup
+//     stages the chunk's A_{t+1}^T in LDS;
+//  2. each wave composes its steps' reverse transform from [I | 0 | 0];
+//  3. an inclusive suffix over the waves (reverse Hillis-Steele) through LDS;
+//     meanwhile the X_{t-1} columns for dA arrive;
+//  4. wave 0 runs the look-back over later chunks and publishes the state at
+//     the chunk's first step;
+//  5. each wave applies the suffix of the waves after it to the state from
+//     later time, rescans its steps backwards, stores dB_t = Lam_t and forms
+//     dA_t = Y_t X_{t-1}^T: per-lane partial sums over its columns, added
+//     across the head's lanes through a per-wave LDS buffer (RB rows a round).
 template <int KP, int CPL, bool VIO>
-__global__ __launch_bounds__(64) void affine_bwd_kernel(BwdArgs p) {
-    constexpr int RB = RowBlock<KP>::RB;
+__global__ __launch_bounds__(512) void affine_bwd_kernel(BwdArgs p) {
+    constexpr int L = AffL<KP, CPL, true>::L;
+    constexpr int RB = AffRB<KP>::RB;
+    constexpr int AS = pad_bank(KP * KP);
     extern __shared__ __align__(16) float s_dyn[];
-    float *s_P = s_dyn;                        // [HPW][KP][KP]: this chunk's P_c
-    float *s_part = s_dyn + p.HPW * KP * KP;   // [HPW][G][RB][KP]: dA partial sums
+    __shared__ uint32_t s_ticket;
+    const int NW = p.NW, HPW = p.HPW, NCP = p.NCP, G = p.G;
+    const int CH = NW * L;
+    const int blk = KP * NCP;
+    const int bs = pad_bank(blk);
+    const int pw = (HPW * G * RB * KP + 3) / 4 * 4;  // one wave's dA partial-sum buffer
+    float *s_A = s_dyn;                                 // [CH][HPW][AS]: A_{t+1}^T
+    float *s_X = s_A + (CH * HPW * AS + 3) / 4 * 4;     // [NW][HPW][bs]: wave transforms / suffixes
+    float *s_S = s_X + NW * HPW * bs;                   // [HPW][bs]: Y entering the chunk from later
+    float *s_part = s_S + HPW * bs;                     // [NW][pw]
 
-    const int lane = threadIdx.x;
-    uint32_t tk = 0;
-    if (lane == 0) tk = take_ticket(p.ws.hdr);
-    const int ticket = __shfl((int)tk, 0);
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    if (tid == 0) s_ticket = take_ticket(p.ws.hdr);
+    __syncthreads();
+    const int ticket = (int)__builtin_amdgcn_readfirstlane(s_ticket);
     const int rchunk = ticket / p.n_groups;
     const int grp = ticket - rchunk * p.n_groups;
     const int chunk = p.n_chunks - 1 - rchunk;
-    const int hs = lane / p.G;
-    const int g = lane - hs * p.G;
-    const bool slot_lane = hs < p.HPW;
+    const int hs = lane / G;
+    const int g = lane - hs * G;
+    const bool slot_lane = hs < HPW;
     const int hsc = slot_lane ? hs : 0;
-    const int64_t gh = (int64_t)grp * p.HPW + hs;
+    const int64_t gh = (int64_t)grp * HPW + hs;
     const bool active = slot_lane && gh < p.heads;
     const int64_t bidx = active ? gh / p.n : 0;
     const int64_t hh = active ? gh % p.n : 0;
-    const int k = p.k, v = p.v;
+    const int k = VIO ? KP : p.k;
+    const int v = p.v;
     const int c0 = g * CPL;
-
-    for (int i = lane; i < p.HPW * KP * KP; i += 64) s_P[i] = 0.f;
 
     Cols<CPL> cl;
 #pragma unroll
@@ -654,110 +724,102 @@ __global__ __launch_bounds__(64) void affine_bwd_kernel(BwdArgs p) {
 #pragma unroll
     for (int cc = 0; cc < CPL; ++cc) is_y[cc] = cl.kind[cc] == Z_M || cl.kind[cc] == Z_L;
 
-    const int64_t t_begin = (int64_t)chunk * p.LC;
-    const int64_t t_end = (t_begin + p.LC < p.T) ? t_begin + p.LC : p.T;
+    const int64_t t_c = (int64_t)chunk * CH;
+    const int64_t t_w = t_c + (int64_t)wave * L;
     const int64_t m0 = bidx * p.T * p.n + hh;
 
-    // Pass 1 (reverse): Z_c = [P_c | Y_c] from [I | 0 | 0].
-    float z[KP][CPL];
+    // 1. G columns (registers), A_{t+1}^T (LDS).
+    float rg[L][KP][CPL];
 #pragma unroll
-    for (int i = 0; i < KP; ++i)
-#pragma unroll
-        for (int cc = 0; cc < CPL; ++cc) z[i][cc] = (cl.kind[cc] == Z_P && i == cl.col[cc]) ? 1.f : 0.f;
-    for (int64_t t = t_end - 1; t >= t_begin; --t)
-        bwd_scan_step<KP, CPL, VIO>(z, p, cl, m0 + t * p.n, t, active);
+    for (int r = 0; r < L; ++r) load_g<KP, CPL, VIO>(rg[r], p, cl, m0 + (t_w + r) * p.n, active && t_w + r < p.T);
+    stage_at<KP, VIO>(s_A, p, grp, t_c, CH);
+    lds_barrier();
 
-    __syncthreads();
-    if (slot_lane) {
-#pragma unroll
-        for (int cc = 0; cc < CPL; ++cc)
-            if (cl.kind[cc] == Z_P)
-#pragma unroll
-                for (int i = 0; i < KP; ++i) s_P[(hs * KP + i) * KP + cl.col[cc]] = z[i][cc];
-    }
-    __syncthreads();
-
-    // Look-back over later chunks: Y entering this chunk from the future
-    // (zero after the last chunk).
-    const int64_t slot_sz = (int64_t)p.HPW * KP * p.NCP;
-    const int64_t hoff = (int64_t)hsc * KP * p.NCP;
-    const int64_t slot = (int64_t)grp * p.n_chunks + chunk;
-    const int last = p.n_chunks - 1;
-    float S[KP][CPL];
-#pragma unroll
-    for (int i = 0; i < KP; ++i)
-#pragma unroll
-        for (int cc = 0; cc < CPL; ++cc) S[i][cc] = 0.f;
-    if (chunk < last) {
-        if (slot_lane) payload_store<KP, CPL>(p.ws.agg + slot * slot_sz + hoff, p.NCP, c0, z);
-        const int dist = wait_ready(p.ws.flags, slot + 1, +1, last - chunk, p.ws.hdr + 1, p.ws.flags + slot,
-                                    FLAG_AGG);
-        const int j0 = chunk + 1 + dist;
-        payload_load<KP, CPL>(S, p.ws.inc + ((int64_t)grp * p.n_chunks + j0) * slot_sz + hoff,
-                                   p.NCP, c0);
-#pragma unroll
-        for (int i = 0; i < KP; ++i)
-#pragma unroll
-            for (int cc = 0; cc < CPL; ++cc) S[i][cc] = is_y[cc] ? S[i][cc] : 0.f;
-        for (int jj = j0 - 1; jj > chunk; --jj) {
-            const float *blk = p.ws.agg + ((int64_t)grp * p.n_chunks + jj) * slot_sz + hoff;
-            float Yl[KP][CPL];
-            payload_load<KP, CPL>(Yl, blk, p.NCP, c0);
-            mat_apply<KP, CPL, true>(S, blk, p.NCP, k, Yl, is_y);
-        }
-    }
+    // 2. The wave's reverse transform from [I | 0 | 0].
     {
-        float inc[KP][CPL];
+        float z[KP][CPL];
 #pragma unroll
         for (int i = 0; i < KP; ++i)
 #pragma unroll
-            for (int cc = 0; cc < CPL; ++cc) inc[i][cc] = S[i][cc];
-        mat_apply<KP, CPL, false>(inc, s_P + hsc * KP * KP, KP, KP, z, is_y);
-        if (slot_lane) payload_store<KP, CPL>(p.ws.inc + slot * slot_sz + hoff, p.NCP, c0, inc);
-        publish_flag(p.ws.flags + slot, FLAG_INC);
+            for (int cc = 0; cc < CPL; ++cc) z[i][cc] = (cl.kind[cc] == Z_P && i == cl.col[cc]) ? 1.f : 0.f;
+#pragma unroll
+        for (int r = L - 1; r >= 0; --r) step_lds<KP, CPL>(z, s_A + ((wave * L + r) * HPW + hsc) * AS, rg[r]);
+        if (slot_lane) put_cols<KP, CPL>(s_X + (wave * HPW + hs) * bs, NCP, c0, z);
+    }
+    lds_barrier();
+
+    // X_{t-1} columns for dA; loaded here so that they arrive during steps 3-4.
+    float rx[L][KP][CPL];
+#pragma unroll
+    for (int r = 0; r < L; ++r)
+        load_xprev<KP, CPL, VIO>(rx[r], p, cl, m0 + (t_w + r) * p.n, t_w + r, active && t_w + r < p.T);
+
+    // 3. Inclusive suffix: after the round with offset o, wave w holds
+    //    T_w o T_{w+1} o ... (T of later waves applied first).
+    for (int o = 1; o < NW; o *= 2) {
+        float x[KP][CPL];
+        if (wave + o < NW) {
+            get_cols<KP, CPL>(x, s_X + ((wave + o) * HPW + hsc) * bs, NCP, c0);
+            block_apply<KP, CPL>(x, s_X + (wave * HPW + hsc) * bs, NCP, k, c0, is_y);
+        }
+        lds_barrier();
+        if (wave + o < NW && slot_lane) put_cols<KP, CPL>(s_X + (wave * HPW + hs) * bs, NCP, c0, x);
+        lds_barrier();
     }
 
-    // Pass 2 (reverse): true Y_t from S; dB_t = Lam_t; dA_t = Y_t X_{t-1}^T.
-    float *part_mine = s_part + ((int64_t)(hsc * p.G + g) * RB) * KP;
-    const float *part_head = s_part + (int64_t)hsc * p.G * RB * KP;
-    for (int64_t t = t_end - 1; t >= t_begin; --t) {
-        const int64_t m = m0 + t * p.n;
-        bwd_scan_step<KP, CPL, VIO>(S, p, cl, m, t, active);
-
-        // X_{t-1} columns matching the lane's Y columns ([I | 0] at t = 0).
-        float xp[KP][CPL];
-        if constexpr (VIO) {
-            if (active && t > 0 && cl.kind[0] == Z_M) {
+    // 4. Look-back over later chunks (wave 0): Y entering the chunk from later
+    //    time (zero after the last chunk), then Y at the chunk's first step.
+    if (wave == 0) {
+        const int64_t slot_sz = (int64_t)HPW * blk;
+        const int64_t hoff = (int64_t)hsc * blk;
+        const int64_t slot = (int64_t)grp * p.n_chunks + chunk;
+        const int last = p.n_chunks - 1;
+        float S[KP][CPL];
 #pragma unroll
-                for (int i = 0; i < KP; ++i) ldv<CPL>(xp[i], p.Abar + (m - p.n) * k * k + i * k + cl.col[0]);
-            } else if (active && t > 0 && cl.kind[0] == Z_L) {
+        for (int i = 0; i < KP; ++i)
 #pragma unroll
-                for (int i = 0; i < KP; ++i) ldv<CPL>(xp[i], p.Bbar + (m - p.n) * k * v + i * v + cl.col[0]);
-            } else {
-#pragma unroll
-                for (int i = 0; i < KP; ++i)
-#pragma unroll
-                    for (int cc = 0; cc < CPL; ++cc)
-                        xp[i][cc] = (t == 0 && cl.kind[cc] == Z_M && i == cl.col[cc]) ? 1.f : 0.f;
+            for (int cc = 0; cc < CPL; ++cc) S[i][cc] = 0.f;
+        if (chunk < last) {
+            if (slot_lane) {
+                float Z[KP][CPL];
+                get_cols<KP, CPL>(Z, s_X + hs * bs, NCP, c0);
+                payload_store<KP, CPL>(p.ws.agg + slot * slot_sz + hoff, NCP, c0, Z);
             }
-        } else {
+            const int dist = wait_ready(p.ws.flags, slot + 1, +1, last - chunk, p.ws.hdr + 1, p.ws.flags + slot,
+                                        FLAG_AGG);
+            const int j0 = chunk + 1 + dist;
+            const uint32_t hb = 4u * (uint32_t)hoff;
+            const int64_t slot_bytes = 4 * slot_sz;
+            // slot j0 holds a state; chunks j0-1 .. chunk+1 hold transforms
+            payload_cols<KP, CPL>(S, make_rows(p.ws.inc + ((int64_t)grp * p.n_chunks + j0) * slot_sz, slot_bytes),
+                                  hb, NCP, c0);
 #pragma unroll
             for (int i = 0; i < KP; ++i)
 #pragma unroll
-                for (int cc = 0; cc < CPL; ++cc) {
-                    float xv = 0.f;
-                    if (active && i < k) {
-                        if (cl.kind[cc] == Z_M)
-                            xv = (t > 0) ? p.Abar[(m - p.n) * k * k + i * k + cl.col[cc]]
-                                         : (i == cl.col[cc] ? 1.f : 0.f);
-                        else if (cl.kind[cc] == Z_L && t > 0)
-                            xv = p.Bbar[(m - p.n) * k * v + i * v + cl.col[cc]];
-                    }
-                    xp[i][cc] = xv;
-                }
+                for (int cc = 0; cc < CPL; ++cc) S[i][cc] = is_y[cc] ? S[i][cc] : 0.f;
+            for (int jj = j0 - 1; jj > chunk; --jj)
+                payload_apply<KP, CPL>(S, make_rows(p.ws.agg + ((int64_t)grp * p.n_chunks + jj) * slot_sz, slot_bytes),
+                                       hb, NCP, k, c0, is_y);
         }
+        if (slot_lane) put_cols<KP, CPL>(s_S + hs * bs, NCP, c0, S);
+        block_apply<KP, CPL>(S, s_X + hsc * bs, NCP, k, c0, is_y);  // through the whole chunk
+        if (slot_lane) payload_store<KP, CPL>(p.ws.inc + slot * slot_sz + hoff, NCP, c0, S);
+        publish_flag(p.ws.flags + slot, FLAG_INC);
+    }
+    lds_barrier();
 
-        // dB_t = Lam_t (own Lam columns).
+    // 5. Y entering this wave from later time, reverse rescan, outputs.
+    float S[KP][CPL];
+    get_cols<KP, CPL>(S, s_S + hsc * bs, NCP, c0);
+    if (wave + 1 < NW) block_apply<KP, CPL>(S, s_X + ((wave + 1) * HPW + hsc) * bs, NCP, k, c0, is_y);
+    float *part = s_part + wave * pw;
+#pragma unroll
+    for (int r = L - 1; r >= 0; --r) {
+        const int64_t t = t_w + r;
+        step_lds<KP, CPL>(S, s_A + ((wave * L + r) * HPW + hsc) * AS, rg[r]);  // S = Y_t
+        if (t >= p.T) continue;  // wave-uniform
+        const int64_t m = m0 + t * p.n;
+        // dB_t = Lam_t
         if (active) {
             if constexpr (VIO) {
                 if (cl.kind[0] == Z_L) {
@@ -772,9 +834,7 @@ __global__ __launch_bounds__(64) void affine_bwd_kernel(BwdArgs p) {
                         if (i < k && cl.kind[cc] == Z_L) p.dB[m * k * v + i * v + cl.col[cc]] = S[i][cc];
             }
         }
-
-        // dA_t rows in blocks of RB: partial sums over the lane's own columns,
-        // then the head's lanes add the G partials of each row through LDS.
+        // dA_t = Y_t X_{t-1}^T, RB rows a round
 #pragma unroll
         for (int ib = 0; ib < KP; ib += RB) {
             if (slot_lane) {
@@ -787,37 +847,47 @@ __global__ __launch_bounds__(64) void affine_bwd_kernel(BwdArgs p) {
                     for (int cc = 0; cc < CPL; ++cc) {
                         const float y = is_y[cc] ? S[ib + ii][cc] : 0.f;
 #pragma unroll
-                        for (int j = 0; j < KP; ++j) row[j] = fmaf(y, xp[j][cc], row[j]);
+                        for (int j = 0; j < KP; ++j) row[j] = fmaf(y, rx[r][j][cc], row[j]);
                     }
-                    stv<KP, false>(part_mine + ii * KP, row);
+                    stv<KP, false>(part + ((hs * G + g) * RB + ii) * KP, row);
                 }
             }
-            __syncthreads();
+            // the wave's own partial sums are in LDS before any lane reads them
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
             if (active) {
-                for (int ii = g; ii < RB; ii += p.G) {
-                    const int i = ib + ii;
-                    if (i < k) {
-                        float acc[KP];
+                if constexpr (KP % 4 == 0) {
+                    // groups of 4 consecutive entries of a row: vector LDS reads
+                    for (int e = 4 * g; e < RB * KP; e += 4 * G) {
+                        const int ii = e / KP, j0 = e - (e / KP) * KP;
+                        const int i = ib + ii;
+                        float acc[4] = {0.f, 0.f, 0.f, 0.f};
+                        for (int gg = 0; gg < G; ++gg) {
+                            float q[4];
+                            ldv<4>(q, part + ((hs * G + gg) * RB + ii) * KP + j0);
 #pragma unroll
-                        for (int j = 0; j < KP; ++j) acc[j] = 0.f;
-                        for (int gg = 0; gg < p.G; ++gg) {
-                            float q[KP];
-                            ldv<KP>(q, part_head + ((int64_t)gg * RB + ii) * KP);
-#pragma unroll
-                            for (int j = 0; j < KP; ++j) acc[j] += q[j];
+                            for (int u = 0; u < 4; ++u) acc[u] += q[u];
                         }
-                        float *dst = p.dA + m * k * k + (int64_t)i * k;
                         if constexpr (VIO) {
-                            stv<KP, true>(dst, acc);
+                            if (i < k) stv<4, true>(p.dA + m * k * k + (int64_t)i * k + j0, acc);
                         } else {
 #pragma unroll
-                            for (int j = 0; j < KP; ++j)
-                                if (j < k) dst[j] = acc[j];
+                            for (int u = 0; u < 4; ++u)
+                                if (i < k && j0 + u < k) p.dA[m * k * k + (int64_t)i * k + j0 + u] = acc[u];
                         }
+                    }
+                } else {
+                    for (int e = g; e < RB * KP; e += G) {
+                        const int ii = e / KP, j = e - (e / KP) * KP;
+                        const int i = ib + ii;
+                        float acc = 0.f;
+                        for (int gg = 0; gg < G; ++gg) acc += part[((hs * G + gg) * RB + ii) * KP + j];
+                        if (i < k && j < k) p.dA[m * k * k + (int64_t)i * k + j] = acc;
                     }
                 }
             }
-            __syncthreads();
+            // LDS operations of one wave complete in order: the next round's
+            // writes land after these reads; this keeps the compiler's order too.
+            asm volatile("" ::: "memory");
         }
     }
 }
@@ -825,129 +895,120 @@ __global__ __launch_bounds__(64) void affine_bwd_kernel(BwdArgs p) {
 // ---------------------------------------------------------------------------
 // Host side: tile selection and launch.
 // ---------------------------------------------------------------------------
-#ifndef MISCAN_AFF_LC
-#define MISCAN_AFF_LC 32
-#endif
-constexpr int LC_STEPS = MISCAN_AFF_LC;  // time steps per work item
-
 struct AffPlan {
     int KP, CPL;
     bool VIO;
-    int G, HPW, NCP, n_groups, n_chunks, LC, RB, NW;
+    int G, HPW, NCP, n_groups, n_chunks, LC, NW;
     size_t n_slots, payload, lds_bytes;
-    bool ok;  // the work-item count fits the int32 ticket space
+    bool ok;  // the work-item count fits the int32 ticket space, the LDS the workgroup
 };
 
 inline int next_pow2_16(int k) { return k <= 1 ? 1 : k <= 2 ? 2 : k <= 4 ? 4 : k <= 8 ? 8 : 16; }
 
-inline AffPlan make_plan(int64_t B, int64_t T, int64_t n, int k, int ncols, bool bwd, int CPL, bool VIO) {
-    AffPlan pl;
-    pl.KP = next_pow2_16(k);
-    pl.CPL = CPL;
-    pl.VIO = VIO;
-    pl.G = (ncols + CPL - 1) / CPL;
-    pl.HPW = 64 / pl.G;
-    pl.NCP = (int)round_up((size_t)pl.G * CPL, 4);
-    const int64_t heads = B * n;
-    const int64_t ng = (heads + pl.HPW - 1) / pl.HPW;
-    pl.LC = LC_STEPS;
-    const int64_t nc = (T + pl.LC - 1) / pl.LC;
-    pl.ok = ng <= INT32_MAX && nc <= INT32_MAX && ng * nc <= (int64_t)INT32_MAX;
-    pl.n_groups = (int)ng;
-    pl.n_chunks = (int)nc;
-    pl.RB = pl.KP < 8 ? pl.KP : 8;
-    pl.NW = 1;
-    pl.n_slots = pl.ok ? (size_t)ng * (size_t)nc : 0;
-    pl.payload = (size_t)pl.HPW * pl.KP * pl.NCP;
-    pl.lds_bytes = sizeof(float) * (size_t)pl.HPW * pl.KP * pl.KP;
-    if (bwd) pl.lds_bytes += sizeof(float) * (size_t)pl.HPW * pl.G * pl.RB * pl.KP;
-    return pl;
-}
-
-// Forward tiling: L steps per wave (AffL), NW waves per workgroup, chunks of
-// NW * L steps; NW as large as 64 KiB of LDS allows.
+// LDS per workgroup: the forward keeps two workgroups per CU possible; the
+// backward (its registers allow one workgroup per CU at the larger k anyway)
+// may take all 160 KiB for its dA partial-sum buffers.
 constexpr size_t FWD_LDS_MAX = 65536;
+#ifndef MISCAN_AFF_BWD_LDS
+#define MISCAN_AFF_BWD_LDS 163840
+#endif
+constexpr size_t BWD_LDS_MAX = MISCAN_AFF_BWD_LDS;
+// Shapes that need more than the budget even with one wave (large padded k
+// with element-wise IO) take up to the device's 160 KiB per workgroup.
+constexpr size_t LDS_DEVICE_MAX = 163840;
 
-inline int aff_L(int KP, int CPL) {
-    const int raw = MISCAN_AFF_BREGS * (KP >= 8 ? 2 : 1) / (KP * CPL);
+inline int aff_L(int KP, int CPL, bool bwd) {
+    const int raw = (bwd ? MISCAN_AFF_BWD_BREGS : MISCAN_AFF_BREGS) * (KP >= 8 ? 2 : 1) / (KP * CPL);
     return raw < 1 ? 1 : raw > 16 ? 16 : raw;
 }
 
-inline AffPlan make_fwd_plan(int64_t B, int64_t T, int64_t n, int k, int v, int CPL, bool VIO) {
+// Tiling: G lanes x CPL columns per head (k + v columns forward, 2k + v
+// backward), HPW heads per wave, L steps per wave (AffL), NW waves per
+// workgroup (as many as the LDS budget allows), chunks of NW * L steps.
+inline AffPlan make_plan(int64_t B, int64_t T, int64_t n, int k, int v, bool bwd, int CPL, bool VIO) {
     AffPlan pl;
     pl.KP = next_pow2_16(k);
     pl.CPL = CPL;
     pl.VIO = VIO;
-    pl.G = (k + v + CPL - 1) / CPL;
+    const int ncols = bwd ? 2 * k + v : k + v;
+    pl.G = (ncols + CPL - 1) / CPL;
+    if (pl.G > 64) {  // a head must fit one wave: this tiling is not usable
+        pl.HPW = 0; pl.NCP = 0; pl.n_groups = 0; pl.n_chunks = 0; pl.LC = 0; pl.NW = 0;
+        pl.n_slots = 0; pl.payload = 0; pl.lds_bytes = 0; pl.ok = false;
+        return pl;
+    }
     pl.HPW = 64 / pl.G;
     pl.NCP = (int)round_up((size_t)pl.G * CPL, 4);
-    pl.RB = 0;
-    const int L = aff_L(pl.KP, CPL);
-    const size_t per_head = (size_t)pl.KP * pl.NCP;      // payload block
+    const int L = aff_L(pl.KP, CPL, bwd);
     const size_t a_ld = (size_t)pad_bank(pl.KP * pl.KP);  // LDS strides (see pad_bank)
     const size_t x_ld = (size_t)pad_bank(pl.KP * pl.NCP);
+    const int rb = pl.KP < MISCAN_AFF_RBMAX ? pl.KP : MISCAN_AFF_RBMAX;  // AffRB
+    const size_t part = round_up((size_t)pl.HPW * pl.G * rb * pl.KP, 4);
+    const size_t limit = bwd ? BWD_LDS_MAX : FWD_LDS_MAX;
+    auto lds_floats = [&](int nw) {
+        const size_t common = round_up((size_t)nw * L * pl.HPW * a_ld, 4) + (size_t)nw * pl.HPW * x_ld;
+        return bwd ? common + (size_t)pl.HPW * x_ld + (size_t)nw * part : common + 2 * (size_t)pl.HPW * x_ld;
+    };
     pl.NW = 1;
-    for (int nw = MISCAN_AFF_NWMAX; nw >= 1; nw /= 2) {
-        const size_t f = round_up((size_t)nw * L * pl.HPW * a_ld, 4) + (size_t)nw * pl.HPW * x_ld +
-                         2 * (size_t)pl.HPW * x_ld;
-        if (f * sizeof(float) <= FWD_LDS_MAX) { pl.NW = nw; break; }
-    }
+    for (int nw = bwd ? MISCAN_AFF_BWD_NWMAX : MISCAN_AFF_NWMAX; nw >= 1; nw /= 2)
+        if (lds_floats(nw) * sizeof(float) <= limit) { pl.NW = nw; break; }
     pl.LC = pl.NW * L;
-    pl.lds_bytes = sizeof(float) * (round_up((size_t)pl.LC * pl.HPW * a_ld, 4) + (size_t)pl.NW * pl.HPW * x_ld +
-                                    2 * (size_t)pl.HPW * x_ld);
+    pl.lds_bytes = lds_floats(pl.NW) * sizeof(float);
     const int64_t heads = B * n;
     const int64_t ng = (heads + pl.HPW - 1) / pl.HPW;
     const int64_t nc = (T + pl.LC - 1) / pl.LC;
-    pl.ok = ng <= INT32_MAX && nc <= INT32_MAX && ng * nc <= (int64_t)INT32_MAX && pl.lds_bytes <= FWD_LDS_MAX;
+    pl.ok = ng <= INT32_MAX && nc <= INT32_MAX && ng * nc <= (int64_t)INT32_MAX &&
+            pl.lds_bytes <= LDS_DEVICE_MAX;
     pl.n_groups = (int)ng;
     pl.n_chunks = (int)nc;
     pl.n_slots = pl.ok ? (size_t)ng * (size_t)nc : 0;
-    pl.payload = (size_t)pl.HPW * per_head;
+    pl.payload = (size_t)pl.HPW * pl.KP * pl.NCP;
     return pl;
 }
 
-// Forward column tiling: of the vector tilings the alignment allows, the one
-// with the longest chunk (fewer look-back steps and payload bytes per step of
-// data), four columns per lane on a tie.
-inline AffPlan choose_fwd_plan(int64_t B, int64_t T, int64_t n, int k, int v, bool ptrs16) {
+// Column tiling: of the vector tilings the alignment allows (k a power of two
+// so that rows load as vectors, k and v multiples of CPL so that column groups
+// never straddle tensors, 16-byte aligned pointers), the one with the longest
+// chunk (fewer look-back steps and payload bytes per step of data), four
+// columns per lane on a tie; otherwise four columns with element accesses.
+inline AffPlan choose_plan(int64_t B, int64_t T, int64_t n, int k, int v, bool bwd, bool ptrs16) {
     const bool kpow2 = next_pow2_16(k) == k;
     AffPlan best;
     bool have = false;
     const int cands[2] = {4, 2};
     for (int cpl : cands) {
-        if (!(ptrs16 && kpow2 && k % cpl == 0 && v % cpl == 0 && (k + v + cpl - 1) / cpl <= 64)) continue;
-        AffPlan pl = make_fwd_plan(B, T, n, k, v, cpl, true);
+        if (!(ptrs16 && kpow2 && k % cpl == 0 && v % cpl == 0)) continue;
+        AffPlan pl = make_plan(B, T, n, k, v, bwd, cpl, true);
         if (!pl.ok) continue;
         if (!have || pl.LC > best.LC) { best = pl; have = true; }
     }
-    if (!have) best = make_fwd_plan(B, T, n, k, v, 4, false);
+    if (!have) best = make_plan(B, T, n, k, v, bwd, 4, false);
     return best;
 }
 
 inline bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) % 16) == 0; }
 
-// Vector IO needs k to be a power of two (rows load as vectors), k and v to be
-// multiples of CPL (column groups never straddle tensors), 16-byte aligned
-// base pointers, and a head to fit one wave (G <= 64).  Otherwise four
-// columns per lane with element-wise accesses.
-inline void choose_cols(int k, int v, int ncols, bool ptrs16, int &CPL, bool &VIO) {
-    const bool kpow2 = next_pow2_16(k) == k;
-    if (ptrs16 && kpow2 && k % 4 == 0 && v % 4 == 0) { CPL = 4; VIO = true; return; }
-    if (ptrs16 && kpow2 && k % 2 == 0 && v % 2 == 0 && (ncols + 1) / 2 <= 64) { CPL = 2; VIO = true; return; }
-    CPL = 4;
-    VIO = false;
+// More than 64 KiB of dynamic LDS (the device allows 160 KiB per workgroup).
+template <class K>
+inline mi_status allow_lds(K kernel, size_t bytes) {
+    if (bytes <= 65536) return MI_OK;
+    return hipFuncSetAttribute(reinterpret_cast<const void *>(kernel), hipFuncAttributeMaxDynamicSharedMemorySize,
+                               (int)bytes) == hipSuccess ? MI_OK : MI_ERR_LAUNCH;
 }
 
 template <int KP, int CPL, bool VIO>
 mi_status fwd_launch(const AffPlan &pl, FwdArgs &a, hipStream_t s) {
     if (pl.LC != pl.NW * AffL<KP, CPL>::L) return MI_ERR_UNSUPPORTED;  // host and kernel tilings agree
+    if (allow_lds(&affine_fwd_kernel<KP, CPL, VIO>, pl.lds_bytes) != MI_OK) return MI_ERR_LAUNCH;
     hipLaunchKernelGGL((affine_fwd_kernel<KP, CPL, VIO>), dim3((unsigned)pl.n_slots), dim3(64 * pl.NW),
                        pl.lds_bytes, s, a);
     return launch_status();
 }
 template <int KP, int CPL, bool VIO>
 mi_status bwd_launch(const AffPlan &pl, BwdArgs &a, hipStream_t s) {
-    hipLaunchKernelGGL((affine_bwd_kernel<KP, CPL, VIO>), dim3((unsigned)pl.n_slots), dim3(64),
+    if (pl.LC != pl.NW * AffL<KP, CPL, true>::L) return MI_ERR_UNSUPPORTED;
+    if (allow_lds(&affine_bwd_kernel<KP, CPL, VIO>, pl.lds_bytes) != MI_OK) return MI_ERR_LAUNCH;
+    hipLaunchKernelGGL((affine_bwd_kernel<KP, CPL, VIO>), dim3((unsigned)pl.n_slots), dim3(64 * pl.NW),
                        pl.lds_bytes, s, a);
     return launch_status();
 }
@@ -985,18 +1046,12 @@ size_t affine_workspace_bytes(int64_t B, int64_t T, int64_t n, int64_t k, int64_
     // The column tiling depends on pointer alignment, known only at the call:
     // size for the largest of the tilings either alignment can select.
     size_t m = 0;
-    for (int a16 = 0; a16 < 2; ++a16) {
-        const int nc = (int)(2 * k + v);
-        int CPL;
-        bool VIO;
-        choose_cols((int)k, (int)v, nc, a16 != 0, CPL, VIO);
-        AffPlan pb = make_plan(B, T, n, (int)k, nc, true, CPL, VIO);
-        AffPlan pf = choose_fwd_plan(B, T, n, (int)k, (int)v, a16 != 0);
-        const size_t wb = WsLayout(pb.n_slots, pb.payload).total;
-        const size_t wf = WsLayout(pf.n_slots, pf.payload).total;
-        m = wb > m ? wb : m;
-        m = wf > m ? wf : m;
-    }
+    for (int a16 = 0; a16 < 2; ++a16)
+        for (int bwd = 0; bwd < 2; ++bwd) {
+            const AffPlan pl = choose_plan(B, T, n, (int)k, (int)v, bwd != 0, a16 != 0);
+            const size_t w = WsLayout(pl.n_slots, pl.payload).total;
+            m = w > m ? w : m;
+        }
     return m;
 }
 
@@ -1004,7 +1059,7 @@ mi_status launch_affine_fwd(const void *A, const void *Bm, void *Abar, void *Bba
                             int64_t T, int64_t n, int64_t k, int64_t v, void *ws,
                             size_t ws_bytes, hipStream_t s) {
     const bool p16 = aligned16(A) && aligned16(Bm) && aligned16(Abar) && aligned16(Bbar);
-    AffPlan pl = choose_fwd_plan(B, T, n, (int)k, (int)v, p16);
+    AffPlan pl = choose_plan(B, T, n, (int)k, (int)v, false, p16);
     if (!pl.ok) return MI_ERR_UNSUPPORTED;
     WsLayout lay(pl.n_slots, pl.payload);
     if (ws == nullptr || ws_bytes < lay.total) return MI_ERR_WORKSPACE;
@@ -1027,11 +1082,7 @@ mi_status launch_affine_bwd(const void *A, const void *Abar, const void *Bbar,
     const void *ptrs[7] = {A, Abar, Bbar, gAbar, gBbar, dA, dB};
     bool p16 = true;
     for (const void *q : ptrs) p16 = p16 && aligned16(q);
-    const int nc = (int)(2 * k + v);
-    int CPL;
-    bool VIO;
-    choose_cols((int)k, (int)v, nc, p16, CPL, VIO);
-    AffPlan pl = make_plan(B, T, n, (int)k, nc, true, CPL, VIO);
+    AffPlan pl = choose_plan(B, T, n, (int)k, (int)v, true, p16);
     if (!pl.ok) return MI_ERR_UNSUPPORTED;
     WsLayout lay(pl.n_slots, pl.payload);
     if (ws == nullptr || ws_bytes < lay.total) return MI_ERR_WORKSPACE;
@@ -1042,7 +1093,7 @@ mi_status launch_affine_bwd(const void *A, const void *Abar, const void *Bbar,
     a.dA = static_cast<float *>(dA); a.dB = static_cast<float *>(dB);
     a.T = T; a.heads = B * n; a.n = (int)n; a.k = (int)k; a.v = (int)v;
     a.G = pl.G; a.HPW = pl.HPW; a.NCP = pl.NCP; a.n_groups = pl.n_groups;
-    a.n_chunks = pl.n_chunks; a.LC = pl.LC;
+    a.n_chunks = pl.n_chunks; a.NW = pl.NW;
     a.ws = ws_ptrs(ws, lay);
     mi_status st = clear_workspace(a.ws, pl.n_slots, s);
     if (st != MI_OK) return st;

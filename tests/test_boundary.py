@@ -129,6 +129,16 @@ def test_log_bwd_validation():
     assert L.mi_scan_log_bwd(*args(dlv=None), 2, 0, 8, F32, None, 0, None) == MI_ERR_INVALID_ARG
 
 
+def test_affine_plan_whole_envelope():
+    """The k x k host planning (column tiling, waves, LDS budget) runs for every
+    k in [1, 16] and v in [1, 128], forward and backward: the workspace query
+    drives the same code as the launchers and must return a size for each."""
+    L = lib()
+    for k in range(1, 17):
+        for v in range(1, 129):
+            assert L.mi_affine_scan_workspace(2, 37, 3, k, v, F32) > 0, (k, v)
+
+
 def test_affine_envelope():
     L = lib()
     A, Bm, Ab, Bb, ws = ptrs(5)
