@@ -52,11 +52,16 @@ def _load():
         lib.lrs_oracle_scan_log_fwd.argtypes = [i64, i64, i64, p, p, p]
         lib.lrs_oracle_scan_log_fwd_logspace.argtypes = [i64, i64, i64, p, p, p]
         lib.lrs_oracle_scan_log_bwd.argtypes = [i64, i64, i64] + [p] * 6
+        lib.lrs_oracle_linear_fwd_h0.argtypes = [i64, i64, i64] + [p] * 5
+        lib.lrs_oracle_linear_bwd_h0.argtypes = [i64, i64, i64] + [p] * 9
+        lib.lrs_oracle_affine_fwd_h0.argtypes = [i64] * 5 + [p] * 5
+        lib.lrs_oracle_affine_bwd_h0.argtypes = [i64] * 5 + [p] * 9
         lib.lrs_oracle_affine_fwd.argtypes = [i64] * 5 + [p] * 4
         lib.lrs_oracle_affine_bwd.argtypes = [i64] * 5 + [p] * 7
         for f in ("lrs_oracle_linear_fwd", "lrs_oracle_linear_bwd",
                   "lrs_oracle_scan_log_fwd", "lrs_oracle_scan_log_fwd_logspace",
-                  "lrs_oracle_scan_log_bwd",
+                  "lrs_oracle_scan_log_bwd", "lrs_oracle_linear_fwd_h0", "lrs_oracle_linear_bwd_h0",
+                  "lrs_oracle_affine_fwd_h0", "lrs_oracle_affine_bwd_h0",
                   "lrs_oracle_affine_fwd", "lrs_oracle_affine_bwd"):
             getattr(lib, f).restype = None
         _lib = lib
@@ -169,3 +174,64 @@ def affine_scan_bwd(A, Abar, Bbar, gAbar, gBbar):
     _load().lrs_oracle_affine_bwd(Bn, T, n, k, v, _ptr(A), _ptr(Abar), _ptr(Bbar),
                                   _ptr(gAbar), _ptr(gBbar), _ptr(dA), _ptr(dB))
     return dA, dB
+
+
+# ---------------------------------------------------------------------------
+# given initial state (h0 / H0; None = zero)
+# ---------------------------------------------------------------------------
+
+def _opt(x, shape):
+    if x is None:
+        return None
+    x = _f64(x)
+    if x.shape != shape:
+        raise ValueError("initial state must have shape %s" % (shape,))
+    return x
+
+
+def _optptr(x):
+    return None if x is None else _ptr(x)
+
+
+def linear_scan_fwd_h0(a, b, h0):
+    """(A, H) with H_t = a_t H_{t-1} + b_t from H_0 = h0 (B, D)."""
+    a, b = _f64(a), _f64(b)
+    Bn, T, D = a.shape
+    h0 = _opt(h0, (Bn, D))
+    A, H = np.empty_like(a), np.empty_like(a)
+    _load().lrs_oracle_linear_fwd_h0(Bn, T, D, _ptr(a), _ptr(b), _optptr(h0), _ptr(A), _ptr(H))
+    return A, H
+
+
+def linear_scan_bwd_h0(a, A, H, h0, gA, gH):
+    """(da, db, dh0): gradient of linear_scan_fwd_h0."""
+    a, A, H, gA, gH = (_f64(x) for x in (a, A, H, gA, gH))
+    Bn, T, D = a.shape
+    h0 = _opt(h0, (Bn, D))
+    da, db, dh0 = np.empty_like(a), np.empty_like(a), np.empty((Bn, D))
+    _load().lrs_oracle_linear_bwd_h0(Bn, T, D, _ptr(a), _ptr(A), _ptr(H), _optptr(h0), _ptr(gA), _ptr(gH),
+                                     _ptr(da), _ptr(db), _ptr(dh0))
+    return da, db, dh0
+
+
+def affine_scan_fwd_h0(A, Bm, H0):
+    """(Abar, H) from X_0 = [I | H0], H0 (B, n, k, v)."""
+    A, Bm = _f64(A), _f64(Bm)
+    Bn, T, n, k, _ = A.shape
+    v = Bm.shape[4]
+    H0 = _opt(H0, (Bn, n, k, v))
+    Abar, H = np.empty_like(A), np.empty_like(Bm)
+    _load().lrs_oracle_affine_fwd_h0(Bn, T, n, k, v, _ptr(A), _ptr(Bm), _optptr(H0), _ptr(Abar), _ptr(H))
+    return Abar, H
+
+
+def affine_scan_bwd_h0(A, Abar, H, H0, gAbar, gH):
+    """(dA, dB, dH0): gradient of affine_scan_fwd_h0."""
+    A, Abar, H, gAbar, gH = (_f64(x) for x in (A, Abar, H, gAbar, gH))
+    Bn, T, n, k, _ = A.shape
+    v = H.shape[4]
+    H0 = _opt(H0, (Bn, n, k, v))
+    dA, dB, dH0 = np.empty_like(A), np.empty_like(H), np.empty((Bn, n, k, v))
+    _load().lrs_oracle_affine_bwd_h0(Bn, T, n, k, v, _ptr(A), _ptr(Abar), _ptr(H), _optptr(H0), _ptr(gAbar),
+                                     _ptr(gH), _ptr(dA), _ptr(dB), _ptr(dH0))
+    return dA, dB, dH0

@@ -354,3 +354,157 @@ void lrs_oracle_affine_bwd(int64_t B, int64_t T, int64_t n, int64_t k, int64_t v
         free(M); free(L); free(Mn); free(Ln); free(Pprev); free(Hprev); free(T1); free(T2);
     }
 }
+
+/* ------------------------------------------------------------------------- */
+/* Given initial state.  The pages define Bc and Bbar as the solutions from  */
+/* a zero state ("Triton kernels" page, Kernel entry points: linear_scan_fwd,*/
+/* affine_scan_fwd); a caller with an initial state h_0 (or H_0) composes    */
+/* h_t = A_t h_0 + Bc_t itself.  These four functions run the same           */
+/* recurrences from a given h_0 / H_0 and return the states directly, with   */
+/* the gradient of h_0 / H_0 in the backward.  A NULL h0 (H0) means zero.    */
+/* ------------------------------------------------------------------------- */
+
+/* h_t = a_t h_{t-1} + b_t from h_0 = h0[b, d]; A_t = a_t A_{t-1}, A_0 = 1.   */
+void lrs_oracle_linear_fwd_h0(int64_t B, int64_t T, int64_t D,
+                              const double *a, const double *b, const double *h0,
+                              double *A, double *H) {
+    int64_t channels = B * D;
+#ifdef _OPENMP
+#pragma omp parallel for schedule(static)
+#endif
+    for (int64_t c = 0; c < channels; ++c) {
+        int64_t bb = c / D, dd = c % D;
+        double A_prev = 1.0;
+        double h_prev = h0 ? h0[bb * D + dd] : 0.0;
+        for (int64_t t = 0; t < T; ++t) {
+            int64_t i = idx3(bb, t, dd, T, D);
+            A_prev = a[i] * A_prev;
+            h_prev = a[i] * h_prev + b[i];
+            A[i] = A_prev;
+            H[i] = h_prev;
+        }
+    }
+}
+
+/* Gradient of the above for L = sum_t gA_t A_t + gH_t H_t: the recurrences  */
+/* of lrs_oracle_linear_bwd with H in place of Bc, H_0 = h_0 instead of 0 in */
+/* da_1 = lam_1 h_0 + mu_1, and dh0 = dL/dh_0 = a_1 lam_1 (zero when T = 0). */
+void lrs_oracle_linear_bwd_h0(int64_t B, int64_t T, int64_t D,
+                              const double *a, const double *A, const double *H,
+                              const double *h0, const double *gA, const double *gH,
+                              double *da, double *db, double *dh0) {
+    int64_t channels = B * D;
+#ifdef _OPENMP
+#pragma omp parallel for schedule(static)
+#endif
+    for (int64_t c = 0; c < channels; ++c) {
+        int64_t bb = c / D, dd = c % D;
+        double lam = 0.0, mu = 0.0, a_next = 0.0;
+        for (int64_t t = T - 1; t >= 0; --t) {
+            int64_t i = idx3(bb, t, dd, T, D);
+            lam = gH[i] + a_next * lam;
+            mu = gA[i] + a_next * mu;
+            double A_prev = (t > 0) ? A[idx3(bb, t - 1, dd, T, D)] : 1.0;
+            double H_prev = (t > 0) ? H[idx3(bb, t - 1, dd, T, D)] : (h0 ? h0[bb * D + dd] : 0.0);
+            db[i] = lam;
+            da[i] = lam * H_prev + mu * A_prev;
+            a_next = a[i];
+        }
+        dh0[bb * D + dd] = a_next * lam; /* a_1 lam_1; a_next stays 0 when T = 0 */
+    }
+}
+
+/* X_t = A_t X_{t-1} + [0 | Bm_t] from X_0 = [I | H0[b, head]]: Abar_t as in */
+/* lrs_oracle_affine_fwd, H_t = A_t H_{t-1} + Bm_t from H_0 = H0.             */
+void lrs_oracle_affine_fwd_h0(int64_t B, int64_t T, int64_t n, int64_t k, int64_t v,
+                              const double *A, const double *Bm, const double *H0,
+                              double *Abar, double *H) {
+    int64_t heads = B * n;
+#ifdef _OPENMP
+#pragma omp parallel for schedule(static)
+#endif
+    for (int64_t hidx = 0; hidx < heads; ++hidx) {
+        int64_t bb = hidx / n, hd = hidx % n;
+        double *P = (double *)malloc(sizeof(double) * k * k);
+        double *Hc = (double *)malloc(sizeof(double) * k * v);
+        double *Pn = (double *)malloc(sizeof(double) * k * k);
+        double *Hn = (double *)malloc(sizeof(double) * k * v);
+        for (int64_t i = 0; i < k; ++i)
+            for (int64_t j = 0; j < k; ++j) P[i * k + j] = (i == j) ? 1.0 : 0.0;
+        for (int64_t i = 0; i < k * v; ++i) Hc[i] = H0 ? H0[hidx * k * v + i] : 0.0;
+        for (int64_t t = 0; t < T; ++t) {
+            const double *At = A + mat_off(bb, t, hd, T, n, k, k);
+            const double *Bt = Bm + mat_off(bb, t, hd, T, n, k, v);
+            matmul(At, P, Pn, k, k, k);
+            matmul(At, Hc, Hn, k, k, v);
+            for (int64_t i = 0; i < k * v; ++i) Hn[i] += Bt[i];
+            memcpy(P, Pn, sizeof(double) * k * k);
+            memcpy(Hc, Hn, sizeof(double) * k * v);
+            memcpy(Abar + mat_off(bb, t, hd, T, n, k, k), P, sizeof(double) * k * k);
+            memcpy(H + mat_off(bb, t, hd, T, n, k, v), Hc, sizeof(double) * k * v);
+        }
+        free(P); free(Hc); free(Pn); free(Hn);
+    }
+}
+
+/* Gradient of the above: the recurrences of lrs_oracle_affine_bwd with H in  */
+/* place of Bbar, H_0 = H0 instead of 0 in dA_1 = M_1 + Lam_1 H0^T, and        */
+/* dH0 = dL/dH_0 = A_1^T Lam_1 (zero when T = 0).                             */
+void lrs_oracle_affine_bwd_h0(int64_t B, int64_t T, int64_t n, int64_t k, int64_t v,
+                              const double *A, const double *Abar, const double *H,
+                              const double *H0, const double *gAbar, const double *gH,
+                              double *dA, double *dB, double *dH0) {
+    int64_t heads = B * n;
+#ifdef _OPENMP
+#pragma omp parallel for schedule(static)
+#endif
+    for (int64_t hidx = 0; hidx < heads; ++hidx) {
+        int64_t bb = hidx / n, hd = hidx % n;
+        double *M = (double *)malloc(sizeof(double) * k * k);
+        double *L = (double *)malloc(sizeof(double) * k * v);
+        double *Mn = (double *)malloc(sizeof(double) * k * k);
+        double *Ln = (double *)malloc(sizeof(double) * k * v);
+        double *Pprev = (double *)malloc(sizeof(double) * k * k);
+        double *Hprev = (double *)malloc(sizeof(double) * k * v);
+        double *T1 = (double *)malloc(sizeof(double) * k * k);
+        double *T2 = (double *)malloc(sizeof(double) * k * k);
+        for (int64_t i = 0; i < k * k; ++i) M[i] = 0.0;
+        for (int64_t i = 0; i < k * v; ++i) L[i] = 0.0;
+        for (int64_t t = T - 1; t >= 0; --t) {
+            const double *gAt = gAbar + mat_off(bb, t, hd, T, n, k, k);
+            const double *gHt = gH + mat_off(bb, t, hd, T, n, k, v);
+            if (t == T - 1) {
+                memcpy(Mn, gAt, sizeof(double) * k * k);
+                memcpy(Ln, gHt, sizeof(double) * k * v);
+            } else {
+                const double *Anext = A + mat_off(bb, t + 1, hd, T, n, k, k);
+                matmul_tn(Anext, M, Mn, k, k, k);
+                matmul_tn(Anext, L, Ln, k, k, v);
+                for (int64_t i = 0; i < k * k; ++i) Mn[i] += gAt[i];
+                for (int64_t i = 0; i < k * v; ++i) Ln[i] += gHt[i];
+            }
+            memcpy(M, Mn, sizeof(double) * k * k);
+            memcpy(L, Ln, sizeof(double) * k * v);
+            if (t > 0) {
+                memcpy(Pprev, Abar + mat_off(bb, t - 1, hd, T, n, k, k), sizeof(double) * k * k);
+                memcpy(Hprev, H + mat_off(bb, t - 1, hd, T, n, k, v), sizeof(double) * k * v);
+            } else {
+                for (int64_t i = 0; i < k; ++i)
+                    for (int64_t j = 0; j < k; ++j) Pprev[i * k + j] = (i == j) ? 1.0 : 0.0;
+                for (int64_t i = 0; i < k * v; ++i) Hprev[i] = H0 ? H0[hidx * k * v + i] : 0.0;
+            }
+            matmul_nt(M, Pprev, T1, k, k, k);
+            matmul_nt(L, Hprev, T2, k, v, k);
+            double *dAt = dA + mat_off(bb, t, hd, T, n, k, k);
+            for (int64_t i = 0; i < k * k; ++i) dAt[i] = T1[i] + T2[i];
+            memcpy(dB + mat_off(bb, t, hd, T, n, k, v), L, sizeof(double) * k * v);
+        }
+        /* dH0 = A_1^T Lam_1: L holds Lam_1 after the loop */
+        double *dH = dH0 + hidx * k * v;
+        if (T > 0)
+            matmul_tn(A + mat_off(bb, 0, hd, T, n, k, k), L, dH, k, k, v);
+        else
+            for (int64_t i = 0; i < k * v; ++i) dH[i] = 0.0;
+        free(M); free(L); free(Mn); free(Ln); free(Pprev); free(Hprev); free(T1); free(T2);
+    }
+}

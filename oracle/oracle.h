@@ -82,6 +82,23 @@ void lrs_oracle_affine_bwd(int64_t B, int64_t T, int64_t n, int64_t k, int64_t v
                            const double *gAbar, const double *gBbar,
                            double *dA, double *dB);
 
+/* Initial state (NULL = zero): states from h0 (B,D) / H0 (B,n,k,v) and the
+ * gradients including dh0 / dH0.  H replaces Bc / Bbar. */
+void lrs_oracle_linear_fwd_h0(int64_t B, int64_t T, int64_t D,
+                              const double *a, const double *b, const double *h0,
+                              double *A, double *H);
+void lrs_oracle_linear_bwd_h0(int64_t B, int64_t T, int64_t D,
+                              const double *a, const double *A, const double *H,
+                              const double *h0, const double *gA, const double *gH,
+                              double *da, double *db, double *dh0);
+void lrs_oracle_affine_fwd_h0(int64_t B, int64_t T, int64_t n, int64_t k, int64_t v,
+                              const double *A, const double *Bm, const double *H0,
+                              double *Abar, double *H);
+void lrs_oracle_affine_bwd_h0(int64_t B, int64_t T, int64_t n, int64_t k, int64_t v,
+                              const double *A, const double *Abar, const double *H,
+                              const double *H0, const double *gAbar, const double *gH,
+                              double *dA, double *dB, double *dH0);
+
 #ifdef __cplusplus
 }
 #endif

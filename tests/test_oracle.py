@@ -567,5 +567,157 @@ def test_affine_bwd_dot_product_long():
     assert abs(jd - jtg) <= 1e-6 * abs(jtg), (jd, jtg)
 
 
+# --------------------------------------------------------------------------
+# given initial state (h0 / H0)
+# --------------------------------------------------------------------------
+
+def test_h0_linear_is_the_composed_state():
+    """H from h0 equals A * h0 + Bc of the zero-state scan (a numpy product of
+    two independent oracle outputs); h0 = None is the zero-state scan."""
+    r = rng(170)
+    a = r.uniform(0.5, 0.999, size=(2, 300, 4))
+    b = r.standard_normal((2, 300, 4))
+    h0 = r.standard_normal((2, 4))
+    A, H = oracle.linear_scan_fwd_h0(a, b, h0)
+    A0, Bc = oracle.linear_scan_fwd(a, b)
+    np.testing.assert_array_equal(A, A0)
+    np.testing.assert_allclose(H, A0 * h0[:, None, :] + Bc, rtol=1e-12, atol=1e-12)
+    _, H_none = oracle.linear_scan_fwd_h0(a, b, None)
+    np.testing.assert_array_equal(H_none, Bc)
+
+
+def test_h0_linear_closed_form():
+    """Constant a, b: H_t = a^t h0 + b (1 - a^t) / (1 - a)."""
+    T = 2000
+    for aval, bval, h0 in ((0.5, 0.3, -2.0), (0.99, 0.01, 5.0)):
+        a = np.full((1, T, 1), aval)
+        b = np.full((1, T, 1), bval)
+        _, H = oracle.linear_scan_fwd_h0(a, b, np.array([[h0]]))
+        t = np.arange(1, T + 1, dtype=np.float64)
+        np.testing.assert_allclose(H[0, :, 0], aval ** t * h0 + bval * (1 - aval ** t) / (1 - aval), rtol=1e-11)
+
+
+def test_h0_linear_resume():
+    """Scanning [0, T) equals scanning [0, T1) and resuming [T1, T) from the
+    last state: the semantics that carries state across calls."""
+    r = rng(171)
+    a = r.uniform(0.5, 1.0, size=(2, 90, 3))
+    b = r.standard_normal((2, 90, 3))
+    h0 = r.standard_normal((2, 3))
+    A, H = oracle.linear_scan_fwd_h0(a, b, h0)
+    for T1 in (1, 37, 89):
+        A1, H1 = oracle.linear_scan_fwd_h0(a[:, :T1], b[:, :T1], h0)
+        A2, H2 = oracle.linear_scan_fwd_h0(a[:, T1:], b[:, T1:], H1[:, -1])
+        np.testing.assert_allclose(H[:, T1:], H2, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(A[:, T1:], A2 * A1[:, -1:], rtol=1e-13)
+
+
+def _loss_linear_h0(a, b, h0, gA, gH):
+    A, H = oracle.linear_scan_fwd_h0(a, b, h0)
+    return float(np.sum(gA * A) + np.sum(gH * H))
+
+
+def test_h0_linear_bwd_finite_differences():
+    r = rng(172)
+    eps = 1e-6
+    for T in (1, 2, 6):
+        a = r.uniform(-1.2, 1.2, size=(1, T, 2))
+        b = r.standard_normal((1, T, 2))
+        h0 = r.standard_normal((1, 2))
+        gA, gH = r.standard_normal((1, T, 2)), r.standard_normal((1, T, 2))
+        A, H = oracle.linear_scan_fwd_h0(a, b, h0)
+        da, db, dh0 = oracle.linear_scan_bwd_h0(a, A, H, h0, gA, gH)
+        for x, g in ((a, da), (b, db), (h0, dh0)):
+            for idx in np.ndindex(x.shape):
+                xp, xm = x.copy(), x.copy()
+                xp[idx] += eps
+                xm[idx] -= eps
+                args_p = [xp if y is x else y for y in (a, b, h0)]
+                args_m = [xm if y is x else y for y in (a, b, h0)]
+                fd = (_loss_linear_h0(*args_p, gA, gH) - _loss_linear_h0(*args_m, gA, gH)) / (2 * eps)
+                assert abs(fd - g[idx]) <= 1e-7 * max(1.0, abs(fd)), (T, idx, fd, g[idx])
+
+
+def test_h0_linear_bwd_zero_state_agrees():
+    """With h0 = None the gradient equals lrs_oracle_linear_bwd's, and dh0 is
+    sum_t gH_t A_t (a numpy sum, a formula of its own)."""
+    r = rng(173)
+    a = r.uniform(0.5, 0.999, size=(2, 200, 3))
+    b = r.standard_normal((2, 200, 3))
+    gA, gH = r.standard_normal(a.shape), r.standard_normal(a.shape)
+    A, Bc = oracle.linear_scan_fwd(a, b)
+    da0, db0 = oracle.linear_scan_bwd(a, A, Bc, gA, gH)
+    da, db, dh0 = oracle.linear_scan_bwd_h0(a, A, Bc, None, gA, gH)
+    np.testing.assert_array_equal(da, da0)
+    np.testing.assert_array_equal(db, db0)
+    np.testing.assert_allclose(dh0, np.sum(gH * A, axis=1), rtol=1e-11)
+
+
+def test_h0_affine_is_the_composed_state():
+    """H from H0 equals Abar @ H0 + Bbar of the zero-state scan (numpy matmul of
+    independent oracle outputs)."""
+    r = rng(174)
+    from workloads import affine_inputs_diag
+    x = affine_inputs_diag(2, 120, 3, 4, 5, seed=175)
+    H0 = r.standard_normal((2, 3, 4, 5))
+    Abar, H = oracle.affine_scan_fwd_h0(x["A"], x["Bm"], H0)
+    Abar0, Bbar = oracle.affine_scan_fwd(x["A"], x["Bm"])
+    np.testing.assert_array_equal(Abar, Abar0)
+    np.testing.assert_allclose(H, np.matmul(Abar0, H0[:, None]) + Bbar, rtol=1e-11, atol=1e-12)
+
+
+def test_h0_affine_resume():
+    r = rng(176)
+    from workloads import affine_inputs_rotation
+    x = affine_inputs_rotation(1, 60, 2, 3, 4, seed=177)
+    H0 = r.standard_normal((1, 2, 3, 4))
+    Abar, H = oracle.affine_scan_fwd_h0(x["A"], x["Bm"], H0)
+    for T1 in (1, 25):
+        Ab1, H1 = oracle.affine_scan_fwd_h0(x["A"][:, :T1], x["Bm"][:, :T1], H0)
+        Ab2, H2 = oracle.affine_scan_fwd_h0(x["A"][:, T1:], x["Bm"][:, T1:], H1[:, -1])
+        np.testing.assert_allclose(H[:, T1:], H2, rtol=1e-11, atol=1e-12)
+        np.testing.assert_allclose(Abar[:, T1:], np.matmul(Ab2, Ab1[:, -1:]), rtol=1e-11, atol=1e-12)
+
+
+def _loss_affine_h0(A, Bm, H0, gAbar, gH):
+    Abar, H = oracle.affine_scan_fwd_h0(A, Bm, H0)
+    return float(np.sum(gAbar * Abar) + np.sum(gH * H))
+
+
+def test_h0_affine_bwd_finite_differences():
+    r = rng(178)
+    eps = 1e-6
+    for T, k, v in ((1, 2, 3), (4, 3, 2)):
+        A = r.uniform(-0.9, 0.9, size=(1, T, 1, k, k))
+        Bm = r.standard_normal((1, T, 1, k, v))
+        H0 = r.standard_normal((1, 1, k, v))
+        gAbar, gH = r.standard_normal(A.shape), r.standard_normal(Bm.shape)
+        Abar, H = oracle.affine_scan_fwd_h0(A, Bm, H0)
+        dA, dB, dH0 = oracle.affine_scan_bwd_h0(A, Abar, H, H0, gAbar, gH)
+        for x, g in ((A, dA), (Bm, dB), (H0, dH0)):
+            for idx in np.ndindex(x.shape):
+                xp, xm = x.copy(), x.copy()
+                xp[idx] += eps
+                xm[idx] -= eps
+                args_p = [xp if y is x else y for y in (A, Bm, H0)]
+                args_m = [xm if y is x else y for y in (A, Bm, H0)]
+                fd = (_loss_affine_h0(*args_p, gAbar, gH) - _loss_affine_h0(*args_m, gAbar, gH)) / (2 * eps)
+                assert abs(fd - g[idx]) <= 1e-7 * max(1.0, abs(fd)), (T, k, v, idx, fd, g[idx])
+
+
+def test_h0_affine_bwd_zero_state_agrees():
+    """H0 = None gives lrs_oracle_affine_bwd's gradient; dH0 = sum_t Abar_t^T gH_t
+    (numpy, a formula of its own: H_t depends on H0 through Abar_t H0)."""
+    from workloads import affine_inputs_diag
+    x = affine_inputs_diag(1, 80, 2, 3, 4, seed=179, grads=True)
+    Abar, Bbar = oracle.affine_scan_fwd(x["A"], x["Bm"])
+    dA0, dB0 = oracle.affine_scan_bwd(x["A"], Abar, Bbar, x["gAbar"], x["gBbar"])
+    dA, dB, dH0 = oracle.affine_scan_bwd_h0(x["A"], Abar, Bbar, None, x["gAbar"], x["gBbar"])
+    np.testing.assert_array_equal(dA, dA0)
+    np.testing.assert_array_equal(dB, dB0)
+    want = np.sum(np.matmul(np.swapaxes(Abar, -1, -2), x["gBbar"]), axis=1)
+    np.testing.assert_allclose(dH0, want, rtol=1e-10, atol=1e-12)
+
+
 def test_oracle_threads_reported():
     assert oracle.num_threads() >= 1
