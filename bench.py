@@ -69,7 +69,7 @@ def device_inputs(wid, torch, workloads):
     return {k: v.to(torch.bfloat16) for k, v in out.items()}
 
 
-def build_workload(wid, torch, lrs, workloads, on_device=False):
+def build_workload(wid, torch, lrs, workloads, on_device=False, initial_state=False):
     """Returns (description dict, list of (kernel name, fn, algorithmic bytes), units, inputs)."""
     w = workloads.WORKLOADS[wid]
     log("generating inputs for workload", wid, w["name"])
@@ -96,19 +96,34 @@ def build_workload(wid, torch, lrs, workloads, on_device=False):
         state["A"] = torch.empty_like(d["a"])
         state["Bc"] = torch.empty_like(d["a"])
 
-        def fwd():
-            lrs.mi_linear_scan_fwd(d["a"], d["b"], state["A"], state["Bc"], ws=ws)
-        kernels.append(("linear_scan_fwd", fwd, 4 * es * N))
+        if initial_state:  # the scans from a given h0 (B, D) and its gradient
+            g = torch.Generator(device="cuda").manual_seed(wid)
+            state["h0"] = torch.randn(Bn, D, device="cuda", generator=g).to(dtype)
+            state["dh0"] = torch.empty_like(state["h0"])
+
+            def fwd():
+                lrs.mi_linear_scan_fwd_h0(d["a"], d["b"], state["h0"], state["A"], state["Bc"], ws=ws)
+            kernels.append(("linear_scan_fwd_h0", fwd, 4 * es * N + es * Bn * D))
+        else:
+            def fwd():
+                lrs.mi_linear_scan_fwd(d["a"], d["b"], state["A"], state["Bc"], ws=ws)
+            kernels.append(("linear_scan_fwd", fwd, 4 * es * N))
         if "gA" in d:
             state["da"] = torch.empty_like(d["a"])
             state["db"] = torch.empty_like(d["a"])
-
-            def bwd():
-                lrs.mi_linear_scan_bwd(d["a"], state["A"], state["Bc"], d["gA"], d["gBc"],
-                                       state["da"], state["db"], ws=ws)
-            kernels.append(("linear_scan_bwd", bwd, 7 * es * N))
-        desc = {"workload": "linear_scan %s k=1, B=%d, T=%d, D=%d, %s storage / fp32 arithmetic"
-                % ("fwd+bwd" if len(kernels) == 2 else "fwd", Bn, T, D, w["dtype"]),
+            if initial_state:
+                def bwd():
+                    lrs.mi_linear_scan_bwd_h0(d["a"], state["A"], state["Bc"], state["h0"], d["gA"], d["gBc"],
+                                              state["da"], state["db"], state["dh0"], ws=ws)
+                kernels.append(("linear_scan_bwd_h0", bwd, 7 * es * N + 2 * es * Bn * D))
+            else:
+                def bwd():
+                    lrs.mi_linear_scan_bwd(d["a"], state["A"], state["Bc"], d["gA"], d["gBc"],
+                                           state["da"], state["db"], ws=ws)
+                kernels.append(("linear_scan_bwd", bwd, 7 * es * N))
+        desc = {"workload": "linear_scan%s %s k=1, B=%d, T=%d, D=%d, %s storage / fp32 arithmetic"
+                % (" from h0" if initial_state else "", "fwd+bwd" if len(kernels) == 2 else "fwd", Bn, T, D,
+                   w["dtype"]),
                 "B": Bn, "T": T, "D": D, "storage": w["dtype"]}
         units = N
     elif w["op"] == "log":
@@ -140,19 +155,34 @@ def build_workload(wid, torch, lrs, workloads, on_device=False):
         state["Abar"] = torch.empty_like(d["A"])
         state["Bbar"] = torch.empty_like(d["Bm"])
 
-        def afwd():
-            lrs.mi_affine_scan_fwd(d["A"], d["Bm"], state["Abar"], state["Bbar"], ws=ws)
-        kernels.append(("affine_scan_fwd", afwd, 4 * 2 * (S * k * k + S * k * v)))
+        nh = Bn * n * k * v  # initial-state elements
+        if initial_state:
+            g = torch.Generator(device="cuda").manual_seed(wid)
+            state["H0"] = torch.randn(Bn, n, k, v, device="cuda", generator=g)
+            state["dH0"] = torch.empty_like(state["H0"])
+
+            def afwd():
+                lrs.mi_affine_scan_fwd_h0(d["A"], d["Bm"], state["H0"], state["Abar"], state["Bbar"], ws=ws)
+            kernels.append(("affine_scan_fwd_h0", afwd, 4 * 2 * (S * k * k + S * k * v) + 4 * nh))
+        else:
+            def afwd():
+                lrs.mi_affine_scan_fwd(d["A"], d["Bm"], state["Abar"], state["Bbar"], ws=ws)
+            kernels.append(("affine_scan_fwd", afwd, 4 * 2 * (S * k * k + S * k * v)))
         if "gAbar" in d:
             state["dA"] = torch.empty_like(d["A"])
             state["dB"] = torch.empty_like(d["Bm"])
-
-            def abwd():
-                lrs.mi_affine_scan_bwd(d["A"], state["Abar"], state["Bbar"], d["gAbar"], d["gBbar"],
-                                       state["dA"], state["dB"], ws=ws)
-            kernels.append(("affine_scan_bwd", abwd, 4 * (4 * S * k * k + 3 * S * k * v)))
-        desc = {"workload": "affine_scan %s k x k, B=%d, T=%d, n=%d, k=%d, v=%d, fp32"
-                % ("fwd+bwd" if len(kernels) == 2 else "fwd", Bn, T, n, k, v),
+            if initial_state:
+                def abwd():
+                    lrs.mi_affine_scan_bwd_h0(d["A"], state["Abar"], state["Bbar"], state["H0"], d["gAbar"],
+                                              d["gBbar"], state["dA"], state["dB"], state["dH0"], ws=ws)
+                kernels.append(("affine_scan_bwd_h0", abwd, 4 * (4 * S * k * k + 3 * S * k * v) + 8 * nh))
+            else:
+                def abwd():
+                    lrs.mi_affine_scan_bwd(d["A"], state["Abar"], state["Bbar"], d["gAbar"], d["gBbar"],
+                                           state["dA"], state["dB"], ws=ws)
+                kernels.append(("affine_scan_bwd", abwd, 4 * (4 * S * k * k + 3 * S * k * v)))
+        desc = {"workload": "affine_scan%s %s k x k, B=%d, T=%d, n=%d, k=%d, v=%d, fp32"
+                % (" from H0" if initial_state else "", "fwd+bwd" if len(kernels) == 2 else "fwd", Bn, T, n, k, v),
                 "B": Bn, "T": T, "n": n, "k": k, "v": v, "storage": w["dtype"]}
         units = S
     return desc, kernels, units, d
@@ -256,6 +286,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cold", action="store_true",
                     help="also time each kernel alone after writing 1 GiB to evict the caches")
+    ap.add_argument("--initial-state", action="store_true",
+                    help="time the scans from a given initial state (the *_h0 entry points); "
+                         "linear and k x k workloads")
     ap.add_argument("--device-inputs", action="store_true",
                     help="draw workload-3 inputs on the GPU (seeded torch generator) instead of numpy")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -288,8 +321,10 @@ def main():
         print("bench.py: " + reason, file=sys.stderr)
         sys.exit(1)
 
+    if args.initial_state and workloads.WORKLOADS[args.workload]["op"] not in ("linear", "affine"):
+        raise SystemExit("--initial-state applies to the linear and k x k workloads")
     desc, kernels, units, _keep = build_workload(args.workload, torch, lrs, workloads,
-                                                 on_device=args.device_inputs)
+                                                 on_device=args.device_inputs, initial_state=args.initial_state)
     stream = torch.cuda.current_stream()
 
     log("warmup", args.warmup)
@@ -353,7 +388,8 @@ def main():
         cpu = cpu_baseline(args.workload, torch, workloads)
 
     out = {
-        "metric": METRIC if args.workload == 3 else "scan GB/s and % HBM peak, " + desc["workload"],
+        "metric": (METRIC if args.workload == 3 and not args.initial_state
+                   else "scan GB/s and % HBM peak, " + desc["workload"]),
         "value": round(value, 1),
         "unit": "GB/s",
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),

@@ -94,6 +94,30 @@ mi_status mi_linear_scan_bwd(const void *a, const void *A, const void *Bc,
                              int64_t B, int64_t T, int64_t D, mi_dtype dt,
                              void *ws, size_t ws_bytes, hipStream_t stream);
 
+/* Scans from a given initial state.  The page's linear_scan_fwd returns Bc,
+ * the solution from h_0 = 0, and leaves the initial state to the caller
+ * (h_t = A_t h_0 + Bc_t).  These two calls take h_0 directly; they are what a
+ * caller that carries state across calls (a sequence processed in pieces, or
+ * split in time across devices) needs.
+ *
+ * mi_linear_scan_fwd_h0: h0 (B, D), or NULL for a zero state.  Writes A (the
+ * running product, as mi_linear_scan_fwd) and H (B, T, D) with
+ * H_t = a_t H_{t-1} + b_t, H_0 = h0.  The final state (A_T, H_T) is the last
+ * row of A and H.
+ * mi_linear_scan_bwd_h0: the gradient for L = <gA, A> + <gH, H>: da, db as
+ * mi_linear_scan_bwd with H in place of Bc and h0 as the state before the
+ * first step, and dh0 (B, D) = dL/dh0 = a_1 lam_1 (zero when T = 0).
+ * Same dtypes, layouts, workspace (mi_linear_scan_workspace) and errors as the
+ * calls above; h0 and dh0 must be aligned like the other tensors and must not
+ * overlap outputs. */
+mi_status mi_linear_scan_fwd_h0(const void *a, const void *b, const void *h0, void *A, void *H,
+                                int64_t B, int64_t T, int64_t D, mi_dtype dt,
+                                void *ws, size_t ws_bytes, hipStream_t stream);
+mi_status mi_linear_scan_bwd_h0(const void *a, const void *A, const void *H, const void *h0,
+                                const void *gA, const void *gH, void *da, void *db, void *dh0,
+                                int64_t B, int64_t T, int64_t D, mi_dtype dt,
+                                void *ws, size_t ws_bytes, hipStream_t stream);
+
 /* ------------------------------------------------------------------------ */
 /* Log-space scan ("Triton kernels", Kernel entry points:                   */
 /* parallel_scan_log_fwd).  Dtypes: MI_F32, MI_BF16.                        */
@@ -159,6 +183,25 @@ mi_status mi_affine_scan_bwd(const void *A, const void *Abar, const void *Bbar,
                              int64_t B, int64_t T, int64_t n, int64_t k, int64_t v,
                              mi_dtype dt, void *ws, size_t ws_bytes,
                              hipStream_t stream);
+
+/* Scans from a given initial state (the k x k counterpart of
+ * mi_linear_scan_fwd_h0 / _bwd_h0).  The page's affine_scan_fwd returns Bbar,
+ * the solution from H_0 = 0.
+ * mi_affine_scan_fwd_h0: H0 (B, n, k, v), or NULL for zero.  Writes Abar (as
+ * mi_affine_scan_fwd) and H (B,T,n,k,v), H_t = A_t H_{t-1} + Bm_t, H_0 = H0;
+ * equivalently X_t = A_t X_{t-1} + [0 | Bm_t] from X_0 = [I | H0].
+ * mi_affine_scan_bwd_h0: gradient for L = <gAbar, Abar> + <gH, H>: dA, dB as
+ * mi_affine_scan_bwd with H in place of Bbar and H0 as the state before the
+ * first step (dA_1 = M_1 + Lam_1 H0^T), and dH0 (B,n,k,v) = A_1^T Lam_1 (zero
+ * when T = 0).  Same dtype, envelope, workspace and errors as the calls
+ * above; H0 and dH0 must not overlap outputs. */
+mi_status mi_affine_scan_fwd_h0(const void *A, const void *Bm, const void *H0, void *Abar, void *H,
+                                int64_t B, int64_t T, int64_t n, int64_t k, int64_t v, mi_dtype dt,
+                                void *ws, size_t ws_bytes, hipStream_t stream);
+mi_status mi_affine_scan_bwd_h0(const void *A, const void *Abar, const void *H, const void *H0,
+                                const void *gAbar, const void *gH, void *dA, void *dB, void *dH0,
+                                int64_t B, int64_t T, int64_t n, int64_t k, int64_t v, mi_dtype dt,
+                                void *ws, size_t ws_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

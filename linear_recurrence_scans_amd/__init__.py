@@ -22,8 +22,10 @@ __all__ = [
     "MiscanError", "available", "library_path",
     "mi_status_string", "mi_device_check",
     "mi_linear_scan_workspace", "mi_linear_scan_fwd", "mi_linear_scan_bwd",
+    "mi_linear_scan_fwd_h0", "mi_linear_scan_bwd_h0",
     "mi_scan_log_workspace", "mi_scan_log_fwd", "mi_scan_log_bwd",
     "mi_affine_scan_workspace", "mi_affine_scan_fwd", "mi_affine_scan_bwd",
+    "mi_affine_scan_fwd_h0", "mi_affine_scan_bwd_h0",
     "linear_scan_fwd", "linear_scan_bwd", "parallel_scan_log_fwd", "parallel_scan_log_bwd",
     "affine_scan_fwd", "affine_scan_bwd",
 ]
@@ -43,12 +45,16 @@ _SIGS = {
     "mi_linear_scan_workspace": ([_I64, _I64, _I64, _I], _SZ),
     "mi_linear_scan_fwd": ([_V] * 4 + [_I64] * 3 + [_I, _V, _SZ, _V], _I),
     "mi_linear_scan_bwd": ([_V] * 7 + [_I64] * 3 + [_I, _V, _SZ, _V], _I),
+    "mi_linear_scan_fwd_h0": ([_V] * 5 + [_I64] * 3 + [_I, _V, _SZ, _V], _I),
+    "mi_linear_scan_bwd_h0": ([_V] * 9 + [_I64] * 3 + [_I, _V, _SZ, _V], _I),
     "mi_scan_log_workspace": ([_I64, _I64, _I64, _I], _SZ),
     "mi_scan_log_fwd": ([_V] * 3 + [_I64] * 3 + [_I, _V, _SZ, _V], _I),
     "mi_scan_log_bwd": ([_V] * 6 + [_I64] * 3 + [_I, _V, _SZ, _V], _I),
     "mi_affine_scan_workspace": ([_I64] * 5 + [_I], _SZ),
     "mi_affine_scan_fwd": ([_V] * 4 + [_I64] * 5 + [_I, _V, _SZ, _V], _I),
     "mi_affine_scan_bwd": ([_V] * 7 + [_I64] * 5 + [_I, _V, _SZ, _V], _I),
+    "mi_affine_scan_fwd_h0": ([_V] * 5 + [_I64] * 5 + [_I, _V, _SZ, _V], _I),
+    "mi_affine_scan_bwd_h0": ([_V] * 9 + [_I64] * 5 + [_I, _V, _SZ, _V], _I),
 }
 
 _lib = None
@@ -205,6 +211,57 @@ def mi_linear_scan_bwd(a, A, Bc, gA, gBc, da=None, db=None, *, ws=None, stream=N
     return da, db
 
 
+def _state(t, like: torch.Tensor, shape, name: str):
+    """Optional initial state (None = zero); same device and dtype as `like`."""
+    if t is None:
+        return None
+    t = _dev_tensor(t, name)
+    if tuple(t.shape) != tuple(shape) or t.dtype != like.dtype or t.device != like.device:
+        raise ValueError("%s must be a %s tensor of shape %s on %s" % (name, like.dtype, tuple(shape), like.device))
+    return t
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def mi_linear_scan_fwd_h0(a, b, h0=None, A=None, H=None, *, ws=None, stream=None):
+    """(A, H): the scan from the initial state h0 (B, D) (None = zero);
+    H_t = a_t H_{t-1} + b_t with H_0 = h0.  The final state is (A[:, -1], H[:, -1])."""
+    a, b = _dev_tensor(a, "a"), _dev_tensor(b, "b")
+    if a.dim() != 3 or b.shape != a.shape:
+        raise ValueError("a and b must both be (B, T, D)")
+    _same(a, b)
+    Bn, T, D = a.shape
+    h0 = _state(h0, a, (Bn, D), "h0")
+    A, H = _out(A, a, "A"), _out(H, a, "H")
+    dt = _dt(a)
+    ws = _workspace(ws, _load().mi_linear_scan_workspace(Bn, T, D, dt), a.device)
+    st = _load().mi_linear_scan_fwd_h0(a.data_ptr(), b.data_ptr(), _ptr(h0), A.data_ptr(), H.data_ptr(), Bn, T, D,
+                                       dt, ws.data_ptr(), ws.numel() * ws.element_size(), _stream(stream, a.device))
+    _check(st, "mi_linear_scan_fwd_h0")
+    return A, H
+
+
+def mi_linear_scan_bwd_h0(a, A, H, h0, gA, gH, da=None, db=None, dh0=None, *, ws=None, stream=None):
+    """(da, db, dh0): gradient of mi_linear_scan_fwd_h0 for upstream grads gA, gH."""
+    a, A, H, gA, gH = (_dev_tensor(t, n) for t, n in ((a, "a"), (A, "A"), (H, "H"), (gA, "gA"), (gH, "gH")))
+    if a.dim() != 3 or any(t.shape != a.shape for t in (A, H, gA, gH)):
+        raise ValueError("a, A, H, gA, gH must all be (B, T, D)")
+    _same(a, A, H, gA, gH)
+    Bn, T, D = a.shape
+    h0 = _state(h0, a, (Bn, D), "h0")
+    da, db = _out(da, a, "da"), _out(db, a, "db")
+    dh0 = _out(dh0, a.new_empty((Bn, D)), "dh0")
+    dt = _dt(a)
+    ws = _workspace(ws, _load().mi_linear_scan_workspace(Bn, T, D, dt), a.device)
+    st = _load().mi_linear_scan_bwd_h0(a.data_ptr(), A.data_ptr(), H.data_ptr(), _ptr(h0), gA.data_ptr(),
+                                       gH.data_ptr(), da.data_ptr(), db.data_ptr(), dh0.data_ptr(), Bn, T, D, dt,
+                                       ws.data_ptr(), ws.numel() * ws.element_size(), _stream(stream, a.device))
+    _check(st, "mi_linear_scan_bwd_h0")
+    return da, db, dh0
+
+
 # ---------------------------------------------------------------------------
 # log-space scan
 # ---------------------------------------------------------------------------
@@ -305,6 +362,42 @@ def mi_affine_scan_bwd(A, Abar, Bbar, gAbar, gBbar, dA=None, dB=None, *, ws=None
                                     ws.numel() * ws.element_size(), _stream(stream, A.device))
     _check(st, "mi_affine_scan_bwd")
     return dA, dB
+
+
+def mi_affine_scan_fwd_h0(A, Bm, H0=None, Abar=None, H=None, *, ws=None, stream=None):
+    """(Abar, H): the k x k scan from X_0 = [I | H0], H0 (B, n, k, v) (None = zero)."""
+    A, Bm = _dev_tensor(A, "A"), _dev_tensor(Bm, "Bm")
+    _same(A, Bm)
+    Bn, T, n, k, v = _affine_shapes(A, Bm)
+    H0 = _state(H0, A, (Bn, n, k, v), "H0")
+    Abar, H = _out(Abar, A, "Abar"), _out(H, Bm, "H")
+    dt = _dt(A)
+    ws = _workspace(ws, _load().mi_affine_scan_workspace(Bn, T, n, k, v, dt), A.device)
+    st = _load().mi_affine_scan_fwd_h0(A.data_ptr(), Bm.data_ptr(), _ptr(H0), Abar.data_ptr(), H.data_ptr(),
+                                       Bn, T, n, k, v, dt, ws.data_ptr(), ws.numel() * ws.element_size(),
+                                       _stream(stream, A.device))
+    _check(st, "mi_affine_scan_fwd_h0")
+    return Abar, H
+
+
+def mi_affine_scan_bwd_h0(A, Abar, H, H0, gAbar, gH, dA=None, dB=None, dH0=None, *, ws=None, stream=None):
+    """(dA, dB, dH0): gradient of mi_affine_scan_fwd_h0."""
+    A, Abar, H, gAbar, gH = (_dev_tensor(t, nm) for t, nm in
+                             ((A, "A"), (Abar, "Abar"), (H, "H"), (gAbar, "gAbar"), (gH, "gH")))
+    _same(A, Abar, H, gAbar, gH)
+    Bn, T, n, k, v = _affine_shapes(A, H)
+    if Abar.shape != A.shape or gAbar.shape != A.shape or gH.shape != H.shape:
+        raise ValueError("Abar, gAbar must match A; gH must match H")
+    H0 = _state(H0, A, (Bn, n, k, v), "H0")
+    dA, dB = _out(dA, A, "dA"), _out(dB, H, "dB")
+    dH0 = _out(dH0, A.new_empty((Bn, n, k, v)), "dH0")
+    dt = _dt(A)
+    ws = _workspace(ws, _load().mi_affine_scan_workspace(Bn, T, n, k, v, dt), A.device)
+    st = _load().mi_affine_scan_bwd_h0(A.data_ptr(), Abar.data_ptr(), H.data_ptr(), _ptr(H0), gAbar.data_ptr(),
+                                       gH.data_ptr(), dA.data_ptr(), dB.data_ptr(), dH0.data_ptr(), Bn, T, n, k, v,
+                                       dt, ws.data_ptr(), ws.numel() * ws.element_size(), _stream(stream, A.device))
+    _check(st, "mi_affine_scan_bwd_h0")
+    return dA, dB, dH0
 
 
 # Op names of the minGRU "Triton kernels" page (same arguments and returns).

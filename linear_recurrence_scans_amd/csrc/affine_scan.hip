@@ -87,6 +87,7 @@ __device__ __forceinline__ void stv(float *dst, const float *src) {
 struct FwdArgs {
     const float *A, *Bm;
     float *Abar, *Bbar;
+    const float *H0;  // initial state (B, n, k, v) for the H0 kernels; NULL = zero
     int64_t T, heads;
     int n, k, v;
     int G, HPW, NCP, n_groups, n_chunks, NW;
@@ -96,6 +97,8 @@ struct FwdArgs {
 struct BwdArgs {
     const float *A, *Abar, *Bbar, *gAbar, *gBbar;
     float *dA, *dB;
+    const float *H0;  // initial state (B, n, k, v) for the H0 kernels; NULL = zero
+    float *dH0;       // its gradient, written by the H0 kernels
     int64_t T, heads;
     int n, k, v;
     int G, HPW, NCP, n_groups, n_chunks, NW;
@@ -367,7 +370,9 @@ __device__ __forceinline__ void payload_cols(float (&x)[KP][CPL], rsrc_t r, uint
 //  5. each wave applies the prefix of the waves before it to that state,
 //     rescans its steps from registers and stores Abar_t, Bbar_t.
 // The chunk is read from memory once.
-template <int KP, int CPL, bool VIO>
+// H0: the scan starts from X_0 = [I | H0] (Bbar then holds the states from
+// H0): the state entering chunk 0 is that instead of [I | 0].
+template <int KP, int CPL, bool VIO, bool H0 = false>
 __global__ __launch_bounds__(512) void affine_fwd_kernel(FwdArgs p) {
     constexpr int L = AffL<KP, CPL>::L;
     extern __shared__ __align__(16) float s_dyn[];
@@ -473,6 +478,15 @@ __global__ __launch_bounds__(512) void affine_fwd_kernel(FwdArgs p) {
         for (int i = 0; i < KP; ++i)
 #pragma unroll
             for (int cc = 0; cc < CPL; ++cc) S[i][cc] = (cl.kind[cc] == C_ABAR && i == cl.col[cc]) ? 1.f : 0.f;
+        if constexpr (H0) {
+            if (chunk == 0 && p.H0 != nullptr && active) {  // H columns of the state: H0
+#pragma unroll
+                for (int i = 0; i < KP; ++i)
+#pragma unroll
+                    for (int cc = 0; cc < CPL; ++cc)
+                        if (i < k && cl.kind[cc] == C_H) S[i][cc] = p.H0[gh * k * p.v + i * p.v + cl.col[cc]];
+            }
+        }
         // the wave's own s_C writes are complete before other lanes read them
         asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         if (chunk > 0) {
@@ -568,9 +582,9 @@ __device__ __forceinline__ void load_g(float (&g)[KP][CPL], const BwdArgs &p, co
 
 // The lane's columns of X_{t-1} = [Abar_{t-1} | Bbar_{t-1}] matching its Y
 // columns ([I | 0] at t = 0; zero when !ok).
-template <int KP, int CPL, bool VIO>
+template <int KP, int CPL, bool VIO, bool H0 = false>
 __device__ __forceinline__ void load_xprev(float (&x)[KP][CPL], const BwdArgs &p, const Cols<CPL> &cl, int64_t m,
-                                           int64_t t, bool ok) {
+                                           int64_t t, bool ok, int64_t gh = 0) {
     const int k = p.k, v = p.v;
     if constexpr (VIO) {
         int ld;
@@ -599,6 +613,15 @@ __device__ __forceinline__ void load_xprev(float (&x)[KP][CPL], const BwdArgs &p
                 }
                 x[i][cc] = xv;
             }
+    }
+    if constexpr (H0) {  // X_{-1} = [I | H0]: its H columns at t = 0
+        if (ok && t == 0 && p.H0 != nullptr) {
+#pragma unroll
+            for (int i = 0; i < KP; ++i)
+#pragma unroll
+                for (int cc = 0; cc < CPL; ++cc)
+                    if (i < k && cl.kind[cc] == Z_L) x[i][cc] = p.H0[gh * k * v + i * v + cl.col[cc]];
+        }
     }
 }
 
@@ -673,7 +696,9 @@ __device__ __forceinline__ void stage_at(float *s_A, const BwdArgs &p, int grp, 
 //     later time, rescans its steps backwards, stores dB_t = Lam_t and forms
 //     dA_t = Y_t X_{t-1}^T: per-lane partial sums over its columns, added
 //     across the head's lanes through a per-wave LDS buffer (RB rows a round).
-template <int KP, int CPL, bool VIO>
+// H0: the forward started from [I | H0]: X_{-1} = [I | H0] in dA at the first
+// step, and dH0 = A_1^T Lam_1 is written as well.
+template <int KP, int CPL, bool VIO, bool H0 = false>
 __global__ __launch_bounds__(512) void affine_bwd_kernel(BwdArgs p) {
     constexpr int L = AffL<KP, CPL, true>::L;
     constexpr int RB = AffRB<KP>::RB;
@@ -752,7 +777,7 @@ __global__ __launch_bounds__(512) void affine_bwd_kernel(BwdArgs p) {
     float rx[L][KP][CPL];
 #pragma unroll
     for (int r = 0; r < L; ++r)
-        load_xprev<KP, CPL, VIO>(rx[r], p, cl, m0 + (t_w + r) * p.n, t_w + r, active && t_w + r < p.T);
+        load_xprev<KP, CPL, VIO, H0>(rx[r], p, cl, m0 + (t_w + r) * p.n, t_w + r, active && t_w + r < p.T, gh);
 
     // 3. Inclusive suffix: after the round with offset o, wave w holds
     //    T_w o T_{w+1} o ... (T of later waves applied first).
@@ -819,6 +844,30 @@ __global__ __launch_bounds__(512) void affine_bwd_kernel(BwdArgs p) {
         step_lds<KP, CPL>(S, s_A + ((wave * L + r) * HPW + hsc) * AS, rg[r]);  // S = Y_t
         if (t >= p.T) continue;  // wave-uniform
         const int64_t m = m0 + t * p.n;
+        if constexpr (H0) {
+            if (t == 0 && active) {  // dH0 = A_1^T Lam_1 for the lane's Lam columns
+                float dh[KP][CPL];
+#pragma unroll
+                for (int i = 0; i < KP; ++i)
+#pragma unroll
+                    for (int cc = 0; cc < CPL; ++cc) dh[i][cc] = 0.f;
+#pragma unroll
+                for (int j = 0; j < KP; ++j) {
+                    float arow[KP];  // row j of A_1
+#pragma unroll
+                    for (int i = 0; i < KP; ++i) arow[i] = (j < k && i < k) ? p.A[m * k * k + j * k + i] : 0.f;
+#pragma unroll
+                    for (int i = 0; i < KP; ++i)
+#pragma unroll
+                        for (int cc = 0; cc < CPL; ++cc) dh[i][cc] = fmaf(arow[i], S[j][cc], dh[i][cc]);
+                }
+#pragma unroll
+                for (int cc = 0; cc < CPL; ++cc)
+#pragma unroll
+                    for (int i = 0; i < KP; ++i)
+                        if (i < k && cl.kind[cc] == Z_L) p.dH0[gh * k * v + i * v + cl.col[cc]] = dh[i][cc];
+            }
+        }
         // dB_t = Lam_t
         if (active) {
             if constexpr (VIO) {
@@ -898,6 +947,7 @@ __global__ __launch_bounds__(512) void affine_bwd_kernel(BwdArgs p) {
 struct AffPlan {
     int KP, CPL;
     bool VIO;
+    bool h0;  // launch the initial-state (H0) kernels
     int G, HPW, NCP, n_groups, n_chunks, LC, NW;
     size_t n_slots, payload, lds_bytes;
     bool ok;  // the work-item count fits the int32 ticket space, the LDS the workgroup
@@ -930,6 +980,7 @@ inline AffPlan make_plan(int64_t B, int64_t T, int64_t n, int k, int v, bool bwd
     pl.KP = next_pow2_16(k);
     pl.CPL = CPL;
     pl.VIO = VIO;
+    pl.h0 = false;
     const int ncols = bwd ? 2 * k + v : k + v;
     pl.G = (ncols + CPL - 1) / CPL;
     if (pl.G > 64) {  // a head must fit one wave: this tiling is not usable
@@ -996,21 +1047,30 @@ inline mi_status allow_lds(K kernel, size_t bytes) {
                                (int)bytes) == hipSuccess ? MI_OK : MI_ERR_LAUNCH;
 }
 
+template <int KP, int CPL, bool VIO, bool H0>
+mi_status fwd_launch_h(const AffPlan &pl, FwdArgs &a, hipStream_t s) {
+    if (pl.LC != pl.NW * AffL<KP, CPL>::L) return MI_ERR_UNSUPPORTED;  // host and kernel tilings agree
+    if (allow_lds(&affine_fwd_kernel<KP, CPL, VIO, H0>, pl.lds_bytes) != MI_OK) return MI_ERR_LAUNCH;
+    hipLaunchKernelGGL((affine_fwd_kernel<KP, CPL, VIO, H0>), dim3((unsigned)pl.n_slots), dim3(64 * pl.NW),
+                       pl.lds_bytes, s, a);
+    return launch_status();
+}
+// h0_kernels is carried in the plan's caller: see dispatch_fwd.
 template <int KP, int CPL, bool VIO>
 mi_status fwd_launch(const AffPlan &pl, FwdArgs &a, hipStream_t s) {
-    if (pl.LC != pl.NW * AffL<KP, CPL>::L) return MI_ERR_UNSUPPORTED;  // host and kernel tilings agree
-    if (allow_lds(&affine_fwd_kernel<KP, CPL, VIO>, pl.lds_bytes) != MI_OK) return MI_ERR_LAUNCH;
-    hipLaunchKernelGGL((affine_fwd_kernel<KP, CPL, VIO>), dim3((unsigned)pl.n_slots), dim3(64 * pl.NW),
+    return pl.h0 ? fwd_launch_h<KP, CPL, VIO, true>(pl, a, s) : fwd_launch_h<KP, CPL, VIO, false>(pl, a, s);
+}
+template <int KP, int CPL, bool VIO, bool H0>
+mi_status bwd_launch_h(const AffPlan &pl, BwdArgs &a, hipStream_t s) {
+    if (pl.LC != pl.NW * AffL<KP, CPL, true>::L) return MI_ERR_UNSUPPORTED;
+    if (allow_lds(&affine_bwd_kernel<KP, CPL, VIO, H0>, pl.lds_bytes) != MI_OK) return MI_ERR_LAUNCH;
+    hipLaunchKernelGGL((affine_bwd_kernel<KP, CPL, VIO, H0>), dim3((unsigned)pl.n_slots), dim3(64 * pl.NW),
                        pl.lds_bytes, s, a);
     return launch_status();
 }
 template <int KP, int CPL, bool VIO>
 mi_status bwd_launch(const AffPlan &pl, BwdArgs &a, hipStream_t s) {
-    if (pl.LC != pl.NW * AffL<KP, CPL, true>::L) return MI_ERR_UNSUPPORTED;
-    if (allow_lds(&affine_bwd_kernel<KP, CPL, VIO>, pl.lds_bytes) != MI_OK) return MI_ERR_LAUNCH;
-    hipLaunchKernelGGL((affine_bwd_kernel<KP, CPL, VIO>), dim3((unsigned)pl.n_slots), dim3(64 * pl.NW),
-                       pl.lds_bytes, s, a);
-    return launch_status();
+    return pl.h0 ? bwd_launch_h<KP, CPL, VIO, true>(pl, a, s) : bwd_launch_h<KP, CPL, VIO, false>(pl, a, s);
 }
 
 // Instantiated tiles: vector IO for k in {4,8,16} (CPL 4) and {2,4,8,16}
@@ -1057,15 +1117,17 @@ size_t affine_workspace_bytes(int64_t B, int64_t T, int64_t n, int64_t k, int64_
 
 mi_status launch_affine_fwd(const void *A, const void *Bm, void *Abar, void *Bbar, int64_t B,
                             int64_t T, int64_t n, int64_t k, int64_t v, void *ws,
-                            size_t ws_bytes, hipStream_t s) {
+                            size_t ws_bytes, hipStream_t s, bool h0_kernels, const void *H0) {
     const bool p16 = aligned16(A) && aligned16(Bm) && aligned16(Abar) && aligned16(Bbar);
     AffPlan pl = choose_plan(B, T, n, (int)k, (int)v, false, p16);
     if (!pl.ok) return MI_ERR_UNSUPPORTED;
+    pl.h0 = h0_kernels;
     WsLayout lay(pl.n_slots, pl.payload);
     if (ws == nullptr || ws_bytes < lay.total) return MI_ERR_WORKSPACE;
     FwdArgs a;
     a.A = static_cast<const float *>(A); a.Bm = static_cast<const float *>(Bm);
     a.Abar = static_cast<float *>(Abar); a.Bbar = static_cast<float *>(Bbar);
+    a.H0 = static_cast<const float *>(H0);
     a.T = T; a.heads = B * n; a.n = (int)n; a.k = (int)k; a.v = (int)v;
     a.G = pl.G; a.HPW = pl.HPW; a.NCP = pl.NCP; a.n_groups = pl.n_groups;
     a.n_chunks = pl.n_chunks; a.NW = pl.NW;
@@ -1078,15 +1140,18 @@ mi_status launch_affine_fwd(const void *A, const void *Bm, void *Abar, void *Bba
 mi_status launch_affine_bwd(const void *A, const void *Abar, const void *Bbar,
                             const void *gAbar, const void *gBbar, void *dA, void *dB,
                             int64_t B, int64_t T, int64_t n, int64_t k, int64_t v, void *ws,
-                            size_t ws_bytes, hipStream_t s) {
+                            size_t ws_bytes, hipStream_t s, bool h0_kernels, const void *H0, void *dH0) {
     const void *ptrs[7] = {A, Abar, Bbar, gAbar, gBbar, dA, dB};
     bool p16 = true;
     for (const void *q : ptrs) p16 = p16 && aligned16(q);
     AffPlan pl = choose_plan(B, T, n, (int)k, (int)v, true, p16);
     if (!pl.ok) return MI_ERR_UNSUPPORTED;
+    pl.h0 = h0_kernels;
     WsLayout lay(pl.n_slots, pl.payload);
     if (ws == nullptr || ws_bytes < lay.total) return MI_ERR_WORKSPACE;
     BwdArgs a;
+    a.H0 = static_cast<const float *>(H0);
+    a.dH0 = static_cast<float *>(dH0);
     a.A = static_cast<const float *>(A); a.Abar = static_cast<const float *>(Abar);
     a.Bbar = static_cast<const float *>(Bbar); a.gAbar = static_cast<const float *>(gAbar);
     a.gBbar = static_cast<const float *>(gBbar);

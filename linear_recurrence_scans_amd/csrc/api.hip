@@ -34,6 +34,13 @@ __global__ void zero_bytes_kernel(uint8_t *p, size_t n) {
         p[i] = 0;
 }
 
+mi_status zero_async(void *p, size_t bytes, hipStream_t s) {
+    if (bytes == 0) return MI_OK;
+    const unsigned blocks = (unsigned)std::min<size_t>(256, (bytes + 255) / 256);
+    hipLaunchKernelGGL(zero_bytes_kernel, dim3(blocks), dim3(256), 0, s, static_cast<uint8_t *>(p), bytes);
+    return launch_status();
+}
+
 namespace {
 
 size_t elem_size(mi_dtype dt) { return dt == MI_BF16 ? 2 : 4; }
@@ -196,6 +203,49 @@ mi_status mi_linear_scan_bwd(const void *a, const void *A, const void *Bc, const
     return launch_linear_bwd(a, A, Bc, gA, gBc, da, db, B, T, D, dt, vec, ws, ws_bytes, stream);
 }
 
+mi_status mi_linear_scan_fwd_h0(const void *a, const void *b, const void *h0, void *A, void *H, int64_t B,
+                                int64_t T, int64_t D, mi_dtype dt, void *ws, size_t ws_bytes, hipStream_t stream) {
+    int64_t bytes;
+    bool empty;
+    mi_status st = check_btd(B, T, D, dt, &bytes, &empty);
+    if (st != MI_OK || empty) return st;
+    const int64_t sbytes = B * D * (int64_t)elem_size(dt);
+    // h0 (optional) joins the inputs; A and H are the outputs
+    const Buf with_h0[5] = {{a, bytes}, {b, bytes}, {h0, sbytes}, {A, bytes}, {H, bytes}};
+    const Buf no_h0[4] = {{a, bytes}, {b, bytes}, {A, bytes}, {H, bytes}};
+    const Buf *bufs = h0 ? with_h0 : no_h0;
+    const int nb = h0 ? 5 : 4;
+    if ((st = check_buffers(bufs, nb, 2, elem_size(dt))) != MI_OK) return st;
+    if ((st = check_ws(ws, ws_bytes, linear_workspace_bytes(B, T, D, dt), bufs, nb)) != MI_OK) return st;
+    const int vec = pick_vec(D, elem_size(dt), bufs, nb);
+    return launch_linear_fwd(a, b, A, H, B, T, D, dt, vec, ws, ws_bytes, stream, true, h0);
+}
+
+mi_status mi_linear_scan_bwd_h0(const void *a, const void *A, const void *H, const void *h0, const void *gA,
+                                const void *gH, void *da, void *db, void *dh0, int64_t B, int64_t T, int64_t D,
+                                mi_dtype dt, void *ws, size_t ws_bytes, hipStream_t stream) {
+    int64_t bytes;
+    bool empty;
+    mi_status st = check_btd(B, T, D, dt, &bytes, &empty);
+    if (st != MI_OK) return st;
+    const int64_t sbytes = B * D * (int64_t)elem_size(dt);
+    if (empty && T == 0 && B > 0 && D > 0) {  // no step: dh0 = 0
+        if (dh0 == nullptr || reinterpret_cast<uintptr_t>(dh0) % elem_size(dt) != 0) return MI_ERR_INVALID_ARG;
+        return zero_async(dh0, (size_t)sbytes, stream);
+    }
+    if (empty) return st;
+    const Buf with_h0[9] = {{a, bytes},  {A, bytes},  {H, bytes},  {h0, sbytes}, {gA, bytes},
+                            {gH, bytes}, {da, bytes}, {db, bytes}, {dh0, sbytes}};
+    const Buf no_h0[8] = {{a, bytes},  {A, bytes},  {H, bytes},  {gA, bytes},
+                          {gH, bytes}, {da, bytes}, {db, bytes}, {dh0, sbytes}};
+    const Buf *bufs = h0 ? with_h0 : no_h0;
+    const int nb = h0 ? 9 : 8;
+    if ((st = check_buffers(bufs, nb, 3, elem_size(dt))) != MI_OK) return st;
+    if ((st = check_ws(ws, ws_bytes, linear_workspace_bytes(B, T, D, dt), bufs, nb)) != MI_OK) return st;
+    const int vec = pick_vec(D, elem_size(dt), bufs, nb);
+    return launch_linear_bwd(a, A, H, gA, gH, da, db, B, T, D, dt, vec, ws, ws_bytes, stream, true, h0, dh0);
+}
+
 size_t mi_scan_log_workspace(int64_t B, int64_t T, int64_t D, mi_dtype dt) {
     int64_t bytes;
     bool empty;
@@ -229,10 +279,7 @@ mi_status mi_scan_log_bwd(const void *log_coeffs, const void *log_values, const 
         // dlog_values still has its slot 0, d log h_0 = 0 when there is no step
         const Buf out{dlog_values, B * D * (int64_t)elem_size(dt)};
         if (out.p == nullptr || reinterpret_cast<uintptr_t>(out.p) % elem_size(dt) != 0) return MI_ERR_INVALID_ARG;
-        const size_t n = (size_t)out.bytes;
-        const unsigned blocks = (unsigned)std::min<size_t>(256, (n + 255) / 256);
-        hipLaunchKernelGGL(zero_bytes_kernel, dim3(blocks), dim3(256), 0, stream, (uint8_t *)dlog_values, n);
-        return launch_status();
+        return zero_async(dlog_values, (size_t)out.bytes, stream);
     }
     if (empty) return st;
     const int64_t lv_bytes = B * (T + 1) * D * (int64_t)elem_size(dt);
@@ -304,6 +351,46 @@ mi_status mi_affine_scan_bwd(const void *A, const void *Abar, const void *Bbar, 
     if ((st = check_buffers(bufs, 7, 2, 4)) != MI_OK) return st;
     if ((st = check_ws(ws, ws_bytes, affine_workspace_bytes(B, T, n, k, v), bufs, 7)) != MI_OK) return st;
     return launch_affine_bwd(A, Abar, Bbar, gAbar, gBbar, dA, dB, B, T, n, k, v, ws, ws_bytes, stream);
+}
+
+mi_status mi_affine_scan_fwd_h0(const void *A, const void *Bm, const void *H0, void *Abar, void *H, int64_t B,
+                                int64_t T, int64_t n, int64_t k, int64_t v, mi_dtype dt, void *ws, size_t ws_bytes,
+                                hipStream_t stream) {
+    int64_t ab, bb;
+    bool empty;
+    mi_status st = check_affine(B, T, n, k, v, dt, &ab, &bb, &empty);
+    if (st != MI_OK || empty) return st;
+    const int64_t sb = B * n * k * v * 4;
+    const Buf with_h0[5] = {{A, ab}, {Bm, bb}, {H0, sb}, {Abar, ab}, {H, bb}};
+    const Buf no_h0[4] = {{A, ab}, {Bm, bb}, {Abar, ab}, {H, bb}};
+    const Buf *bufs = H0 ? with_h0 : no_h0;
+    const int nb = H0 ? 5 : 4;
+    if ((st = check_buffers(bufs, nb, 2, 4)) != MI_OK) return st;
+    if ((st = check_ws(ws, ws_bytes, affine_workspace_bytes(B, T, n, k, v), bufs, nb)) != MI_OK) return st;
+    return launch_affine_fwd(A, Bm, Abar, H, B, T, n, k, v, ws, ws_bytes, stream, true, H0);
+}
+
+mi_status mi_affine_scan_bwd_h0(const void *A, const void *Abar, const void *H, const void *H0, const void *gAbar,
+                                const void *gH, void *dA, void *dB, void *dH0, int64_t B, int64_t T, int64_t n,
+                                int64_t k, int64_t v, mi_dtype dt, void *ws, size_t ws_bytes, hipStream_t stream) {
+    int64_t ab, bb;
+    bool empty;
+    mi_status st = check_affine(B, T, n, k, v, dt, &ab, &bb, &empty);
+    if (st != MI_OK) return st;
+    const int64_t sb = B * n * k * v * 4;
+    if (empty && T == 0 && B > 0 && n > 0) {  // no step: dH0 = 0
+        if (dH0 == nullptr || reinterpret_cast<uintptr_t>(dH0) % 4 != 0) return MI_ERR_INVALID_ARG;
+        return zero_async(dH0, (size_t)sb, stream);
+    }
+    if (empty) return st;
+    const Buf with_h0[9] = {{A, ab},  {Abar, ab}, {H, bb},  {H0, sb}, {gAbar, ab},
+                            {gH, bb}, {dA, ab},   {dB, bb}, {dH0, sb}};
+    const Buf no_h0[8] = {{A, ab}, {Abar, ab}, {H, bb}, {gAbar, ab}, {gH, bb}, {dA, ab}, {dB, bb}, {dH0, sb}};
+    const Buf *bufs = H0 ? with_h0 : no_h0;
+    const int nb = H0 ? 9 : 8;
+    if ((st = check_buffers(bufs, nb, 3, 4)) != MI_OK) return st;
+    if ((st = check_ws(ws, ws_bytes, affine_workspace_bytes(B, T, n, k, v), bufs, nb)) != MI_OK) return st;
+    return launch_affine_bwd(A, Abar, H, gAbar, gH, dA, dB, B, T, n, k, v, ws, ws_bytes, stream, true, H0, dH0);
 }
 
 }  // extern "C"

@@ -28,6 +28,7 @@ namespace {
 struct FwdArgs {
     const void *a, *b;
     void *A, *Bc;
+    const void *h0;  // initial state (B, D), used by the H0 kernels; NULL = zero
     int64_t T, D;
     int n_dtiles, n_tiles, n_chunks;
     WsPtrs ws;
@@ -36,6 +37,8 @@ struct FwdArgs {
 struct BwdArgs {
     const void *a, *A, *Bc, *gA, *gBc;
     void *da, *db;
+    const void *h0;  // initial state (B, D) for the H0 kernels; NULL = zero
+    void *dh0;       // its gradient (B, D), written by the H0 kernels
     int64_t T, D;
     int n_dtiles, n_tiles, n_chunks;
     WsPtrs ws;
@@ -99,7 +102,9 @@ __device__ __forceinline__ Item decode_item(uint32_t ticket, int n_tiles, int n_
 // workgroup runs the look-back (wg_lookback), and each wave rescans its rows
 // from its carry-in and stores A_t, Bc_t.
 // ---------------------------------------------------------------------------
-template <typename T, int VEC, int L, int NW>
+// H0: the scan starts from the state p.h0 instead of 0 (Bc then holds the
+// states from h0): the carry entering chunk 0 is (1, h0).
+template <typename T, int VEC, int L, int NW, bool H0 = false>
 __global__ __launch_bounds__(NW * 64) void linear_fwd_kernel(FwdArgs p) {
     using PK = Pack<T, VEC>;
     using raw_t = typename PK::raw_t;
@@ -181,6 +186,14 @@ __global__ __launch_bounds__(NW * 64) void linear_fwd_kernel(FwdArgs p) {
                     FwdOp::then(r, c[q], x);
                     c[q][0] = r[0]; c[q][1] = r[1];
                 }
+            if constexpr (H0) {
+                const int64_t dch = (int64_t)(it.tile - it.bidx * p.n_dtiles) * TILE + ch;
+                if (it.chunk == 0 && ch < TILE && dch < p.D && p.h0 != nullptr) {
+                    float f0[1];
+                    Pack<T, 1>::unpack(load_vec<T, 1>(static_cast<const T *>(p.h0) + (int64_t)it.bidx * p.D + dch), f0);
+                    in[q][1] = f0[0];
+                }
+            }
         }
         wg_lookback<FwdOp, TILE, NT>(p.ws, slot, -1, it.chunk, c, in, &s_k);
 #pragma unroll
@@ -235,7 +248,9 @@ __global__ __launch_bounds__(NW * 64) void linear_fwd_kernel(FwdArgs p) {
 // Same work-item structure as the forward, with chunks taken from the end of
 // time backwards and each wave scanning its rows from the last one.
 // ---------------------------------------------------------------------------
-template <typename T, int VEC, int L, int NW>
+// H0: the forward started from p.h0 (Bc holds those states): Bc_{-1} is h0
+// in da at the first step, and dh0 = a_1 lam_1 is written as well.
+template <typename T, int VEC, int L, int NW, bool H0 = false>
 __global__ __launch_bounds__(NW * 64) void linear_bwd_kernel(BwdArgs p) {
     using PK = Pack<T, VEC>;
     using raw_t = typename PK::raw_t;
@@ -330,6 +345,14 @@ __global__ __launch_bounds__(NW * 64) void linear_bwd_kernel(BwdArgs p) {
             rBp[r] = ok ? xB : zero;
         }
     }
+    raw_t ra0 = splat<T, VEC>(0.f);  // a at time row 0 (H0: dh0 = a_1 lam_1)
+    if constexpr (H0) {
+        if (it.t0 == 0 && it.lane_ok) {  // the wave holding time row 0
+            const T *rowa = static_cast<const T *>(p.a) + (int64_t)it.bidx * p.T * p.D + it.d;
+            ra0 = load_vec<T, VEC>(rowa);
+            if (p.h0 != nullptr) rBp[0] = load_vec<T, VEC>(static_cast<const T *>(p.h0) + (int64_t)it.bidx * p.D + it.d);
+        }
+    }
 
     // 3. Chunk aggregate per channel (waves NW-1 .. 0), look-back over later
     //    chunks, carry.
@@ -400,6 +423,15 @@ __global__ __launch_bounds__(NW * 64) void linear_bwd_kernel(BwdArgs p) {
             row_store<T, VEC>(PK::pack(lam), dbo + so, voff);
         }
     }
+    if constexpr (H0) {
+        if (it.t0 == 0) {  // lam now holds lam_1
+            float fa0[VEC], g0[VEC];
+            PK::unpack(ra0, fa0);
+#pragma unroll
+            for (int v = 0; v < VEC; ++v) g0[v] = fa0[v] * lam[v];
+            row_store<T, VEC>(PK::pack(g0), row_ptr<T>(p.dh0, it.bidx, 0, 1, p.D), voff);
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------
@@ -466,41 +498,41 @@ size_t bwd_ws(int64_t B, int64_t T, int64_t D) {
     return WsLayout(g.n_slots, 64 * 3 * VEC).total;
 }
 
-template <typename E, int VEC>
+template <typename E, int VEC, bool H0 = false>
 mi_status run_fwd(const void *a, const void *b, void *A, void *Bc, int64_t B, int64_t T,
-                  int64_t D, void *ws, size_t ws_bytes, hipStream_t s) {
+                  int64_t D, void *ws, size_t ws_bytes, hipStream_t s, const void *h0 = nullptr) {
     constexpr int L = FwdShape<E, VEC>::L, NW = FwdShape<E, VEC>::NW;
     Grid g = make_grid(B, T, D, 64 * VEC, L * NW, (int)sizeof(E));
     if (!g.ok) return MI_ERR_UNSUPPORTED;
     WsLayout lay(g.n_slots, 64 * 2 * VEC);
     if (ws == nullptr || ws_bytes < lay.total) return MI_ERR_WORKSPACE;
     FwdArgs p;
-    p.a = a; p.b = b; p.A = A; p.Bc = Bc; p.T = T; p.D = D;
+    p.a = a; p.b = b; p.A = A; p.Bc = Bc; p.h0 = h0; p.T = T; p.D = D;
     p.n_dtiles = g.n_dtiles; p.n_tiles = g.n_tiles; p.n_chunks = g.n_chunks;
     p.ws = ws_ptrs(ws, lay);
     mi_status st = clear_workspace(p.ws, g.n_slots, s);
     if (st != MI_OK) return st;
-    hipLaunchKernelGGL((linear_fwd_kernel<E, VEC, L, NW>), dim3((unsigned)g.n_slots), dim3(NW * 64), 0, s, p);
+    hipLaunchKernelGGL((linear_fwd_kernel<E, VEC, L, NW, H0>), dim3((unsigned)g.n_slots), dim3(NW * 64), 0, s, p);
     return launch_status();
 }
 
-template <typename E, int VEC>
+template <typename E, int VEC, bool H0 = false>
 mi_status run_bwd(const void *a, const void *A, const void *Bc, const void *gA,
                   const void *gBc, void *da, void *db, int64_t B, int64_t T, int64_t D,
-                  void *ws, size_t ws_bytes, hipStream_t s) {
+                  void *ws, size_t ws_bytes, hipStream_t s, const void *h0 = nullptr, void *dh0 = nullptr) {
     constexpr int L = BwdShape<E, VEC>::L, NW = BwdShape<E, VEC>::NW;
     Grid g = make_grid(B, T, D, 64 * VEC, L * NW, (int)sizeof(E));
     if (!g.ok) return MI_ERR_UNSUPPORTED;
     WsLayout lay(g.n_slots, 64 * 3 * VEC);
     if (ws == nullptr || ws_bytes < lay.total) return MI_ERR_WORKSPACE;
     BwdArgs p;
-    p.a = a; p.A = A; p.Bc = Bc; p.gA = gA; p.gBc = gBc; p.da = da; p.db = db;
+    p.a = a; p.A = A; p.Bc = Bc; p.gA = gA; p.gBc = gBc; p.da = da; p.db = db; p.h0 = h0; p.dh0 = dh0;
     p.T = T; p.D = D;
     p.n_dtiles = g.n_dtiles; p.n_tiles = g.n_tiles; p.n_chunks = g.n_chunks;
     p.ws = ws_ptrs(ws, lay);
     mi_status st = clear_workspace(p.ws, g.n_slots, s);
     if (st != MI_OK) return st;
-    hipLaunchKernelGGL((linear_bwd_kernel<E, VEC, L, NW>), dim3((unsigned)g.n_slots),
+    hipLaunchKernelGGL((linear_bwd_kernel<E, VEC, L, NW, H0>), dim3((unsigned)g.n_slots),
                        dim3(NW * 64), 0, s, p);
     return launch_status();
 }
@@ -524,43 +556,53 @@ size_t linear_workspace_bytes(int64_t B, int64_t T, int64_t D, mi_dtype dt) {
     return m;
 }
 
+// h0_kernels: the H0 instantiations (initial state in, dh0 out); h0 may be
+// NULL (zero) there.
 mi_status launch_linear_fwd(const void *a, const void *b, void *A, void *Bc, int64_t B,
                             int64_t T, int64_t D, mi_dtype dt, int vec, void *ws,
-                            size_t ws_bytes, hipStream_t s) {
+                            size_t ws_bytes, hipStream_t s, bool h0_kernels, const void *h0) {
+#define MISCAN_LIN_FWD(E, V)                                                                     \
+    (h0_kernels ? run_fwd<E, V, true>(a, b, A, Bc, B, T, D, ws, ws_bytes, s, h0)                 \
+                : run_fwd<E, V, false>(a, b, A, Bc, B, T, D, ws, ws_bytes, s))
     if (dt == MI_F32) {
         switch (vec) {
-            case 4: return run_fwd<float, 4>(a, b, A, Bc, B, T, D, ws, ws_bytes, s);
-            case 2: return run_fwd<float, 2>(a, b, A, Bc, B, T, D, ws, ws_bytes, s);
-            default: return run_fwd<float, 1>(a, b, A, Bc, B, T, D, ws, ws_bytes, s);
+            case 4: return MISCAN_LIN_FWD(float, 4);
+            case 2: return MISCAN_LIN_FWD(float, 2);
+            default: return MISCAN_LIN_FWD(float, 1);
         }
     }
     if (vec > MISCAN_LIN_FWD_BF16_VMAX) vec = MISCAN_LIN_FWD_BF16_VMAX;
     switch (vec) {
-        case 8: return run_fwd<bf16_t, 8>(a, b, A, Bc, B, T, D, ws, ws_bytes, s);
-        case 4: return run_fwd<bf16_t, 4>(a, b, A, Bc, B, T, D, ws, ws_bytes, s);
-        case 2: return run_fwd<bf16_t, 2>(a, b, A, Bc, B, T, D, ws, ws_bytes, s);
-        default: return run_fwd<bf16_t, 1>(a, b, A, Bc, B, T, D, ws, ws_bytes, s);
+        case 8: return MISCAN_LIN_FWD(bf16_t, 8);
+        case 4: return MISCAN_LIN_FWD(bf16_t, 4);
+        case 2: return MISCAN_LIN_FWD(bf16_t, 2);
+        default: return MISCAN_LIN_FWD(bf16_t, 1);
     }
+#undef MISCAN_LIN_FWD
 }
 
 mi_status launch_linear_bwd(const void *a, const void *A, const void *Bc, const void *gA,
                             const void *gBc, void *da, void *db, int64_t B, int64_t T,
                             int64_t D, mi_dtype dt, int vec, void *ws, size_t ws_bytes,
-                            hipStream_t s) {
+                            hipStream_t s, bool h0_kernels, const void *h0, void *dh0) {
+#define MISCAN_LIN_BWD(E, V)                                                                               \
+    (h0_kernels ? run_bwd<E, V, true>(a, A, Bc, gA, gBc, da, db, B, T, D, ws, ws_bytes, s, h0, dh0)        \
+                : run_bwd<E, V, false>(a, A, Bc, gA, gBc, da, db, B, T, D, ws, ws_bytes, s))
     if (dt == MI_F32) {
         switch (vec) {
-            case 4: return run_bwd<float, 4>(a, A, Bc, gA, gBc, da, db, B, T, D, ws, ws_bytes, s);
-            case 2: return run_bwd<float, 2>(a, A, Bc, gA, gBc, da, db, B, T, D, ws, ws_bytes, s);
-            default: return run_bwd<float, 1>(a, A, Bc, gA, gBc, da, db, B, T, D, ws, ws_bytes, s);
+            case 4: return MISCAN_LIN_BWD(float, 4);
+            case 2: return MISCAN_LIN_BWD(float, 2);
+            default: return MISCAN_LIN_BWD(float, 1);
         }
     }
     if (vec > MISCAN_LIN_BWD_BF16_VMAX) vec = MISCAN_LIN_BWD_BF16_VMAX;
     switch (vec) {
-        case 8: return run_bwd<bf16_t, 8>(a, A, Bc, gA, gBc, da, db, B, T, D, ws, ws_bytes, s);
-        case 4: return run_bwd<bf16_t, 4>(a, A, Bc, gA, gBc, da, db, B, T, D, ws, ws_bytes, s);
-        case 2: return run_bwd<bf16_t, 2>(a, A, Bc, gA, gBc, da, db, B, T, D, ws, ws_bytes, s);
-        default: return run_bwd<bf16_t, 1>(a, A, Bc, gA, gBc, da, db, B, T, D, ws, ws_bytes, s);
+        case 8: return MISCAN_LIN_BWD(bf16_t, 8);
+        case 4: return MISCAN_LIN_BWD(bf16_t, 4);
+        case 2: return MISCAN_LIN_BWD(bf16_t, 2);
+        default: return MISCAN_LIN_BWD(bf16_t, 1);
     }
+#undef MISCAN_LIN_BWD
 }
 
 }  // namespace miscan

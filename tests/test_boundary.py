@@ -129,6 +129,26 @@ def test_log_bwd_validation():
     assert L.mi_scan_log_bwd(*args(dlv=None), 2, 0, 8, F32, None, 0, None) == MI_ERR_INVALID_ARG
 
 
+def test_initial_state_validation():
+    L = lib()
+    a, b, h0, A, H, ws = ptrs(6)
+    # h0 may be NULL (zero state); outputs must not overlap it
+    assert L.mi_linear_scan_fwd_h0(a, b, h0, A, H, 2, 8, 8, F32, None, 0, None) == MI_ERR_WORKSPACE
+    assert L.mi_linear_scan_fwd_h0(a, b, None, A, H, 2, 8, 8, F32, None, 0, None) == MI_ERR_WORKSPACE
+    assert L.mi_linear_scan_fwd_h0(a, b, h0, A, h0, 2, 8, 8, F32, ws, 1 << 40, None) == MI_ERR_INVALID_ARG
+    q = ptrs(10)
+    # dh0 aliasing h0
+    assert L.mi_linear_scan_bwd_h0(*q[:8], q[3], 2, 8, 8, F32, q[9], 1 << 40, None) == MI_ERR_INVALID_ARG
+    assert L.mi_linear_scan_bwd_h0(*q[:8], None, 2, 8, 8, F32, q[9], 1 << 40, None) == MI_ERR_INVALID_ARG
+    # T = 0 still zeroes dh0 (a launch) after checking its pointer
+    assert L.mi_linear_scan_bwd_h0(*q[:8], None, 2, 0, 8, F32, None, 0, None) == MI_ERR_INVALID_ARG
+    r = ptrs(10)
+    assert L.mi_affine_scan_fwd_h0(*r[:5], 1, 4, 2, 4, 8, F32, None, 0, None) == MI_ERR_WORKSPACE
+    assert L.mi_affine_scan_fwd_h0(*r[:5], 1, 4, 2, 17, 8, F32, None, 0, None) == MI_ERR_UNSUPPORTED
+    assert L.mi_affine_scan_bwd_h0(*r[:8], r[3], 1, 4, 2, 4, 8, F32, r[9], 1 << 40, None) == MI_ERR_INVALID_ARG
+    assert L.mi_affine_scan_bwd_h0(*r[:8], None, 1, 0, 2, 4, 8, F32, None, 0, None) == MI_ERR_INVALID_ARG
+
+
 def test_affine_plan_whole_envelope():
     """The k x k host planning (column tiling, waves, LDS budget) runs for every
     k in [1, 16] and v in [1, 128], forward and backward: the workspace query

@@ -168,6 +168,88 @@ def test_linear_workload3_full():
 
 
 # ---------------------------------------------------------------------------
+# k = 1 scan from a given initial state
+# ---------------------------------------------------------------------------
+
+def run_linear_h0(x, dtype, seed, with_h0=True):
+    """GPU fwd + bwd from an initial state h0 against the oracle."""
+    a_d, a = quantise(x["a"], dtype)
+    b_d, b = quantise(x["b"], dtype)
+    Bn, T, D = a.shape
+    rg = np.random.Generator(np.random.PCG64(2000 + seed))
+    if with_h0:
+        h0_d, h0 = quantise(rg.standard_normal((Bn, D)), dtype)
+    else:
+        h0_d, h0 = None, None
+    A_d, H_d = lrs.mi_linear_scan_fwd_h0(a_d, b_d, h0_d)
+    torch.cuda.synchronize()
+    A_r, H_r = oracle.linear_scan_fwd_h0(a, b, h0)
+    _, H_s = oracle.linear_scan_fwd_h0(np.abs(a), np.abs(b), None if h0 is None else np.abs(h0))
+    errs = {"A": scaled_err(to_np(A_d), A_r, A_r), "H": scaled_err(to_np(H_d), H_r, H_s)}
+    A_in_d, A_in = quantise(A_r, dtype)
+    H_in_d, H_in = quantise(H_r, dtype)
+    gA_d, gA = quantise(x["gA"], dtype)
+    gH_d, gH = quantise(x["gBc"], dtype)
+    da_d, db_d, dh0_d = lrs.mi_linear_scan_bwd_h0(a_d, A_in_d, H_in_d, h0_d, gA_d, gH_d)
+    torch.cuda.synchronize()
+    da_r, db_r, dh0_r = oracle.linear_scan_bwd_h0(a, A_in, H_in, h0, gA, gH)
+    ab = [np.abs(t) for t in (a, A_in, H_in)]
+    da_s, db_s, dh0_s = oracle.linear_scan_bwd_h0(*ab, None if h0 is None else np.abs(h0), np.abs(gA), np.abs(gH))
+    errs.update(da=scaled_err(to_np(da_d), da_r, da_s), db=scaled_err(to_np(db_d), db_r, db_s),
+                dh0=scaled_err(to_np(dh0_d), dh0_r, dh0_s))
+    return errs
+
+
+@pytest.mark.parametrize("shape", [(1, 1, 1), (2, 63, 3), (1, 300, 100), (2, 1000, 520), (1, 4097, 64)])
+def test_linear_h0_edge_shapes_f32(shape):
+    say("linear fwd+bwd from h0, fp32, shape", shape)
+    errs = run_linear_h0(lin_case(*shape, seed=sum(shape)), torch.float32, sum(shape))
+    assert max(errs.values()) <= TOL[torch.float32], (shape, errs)
+
+
+@pytest.mark.parametrize("shape", [(2, 1000, 4104), (1, 77, 37)])
+def test_linear_h0_bf16(shape):
+    say("linear fwd+bwd from h0, bf16, shape", shape)
+    errs = run_linear_h0(lin_case(*shape, seed=19, a_lo=0.9, a_hi=0.9999), torch.bfloat16, 19)
+    assert max(errs.values()) <= TOL[torch.bfloat16], (shape, errs)
+
+
+def test_linear_h0_none_is_zero_state():
+    say("linear fwd+bwd from h0 = None, fp32 B=2 T=300 D=64")
+    errs = run_linear_h0(lin_case(2, 300, 64, seed=23), torch.float32, 23, with_h0=False)
+    assert max(errs.values()) <= TOL[torch.float32], errs
+
+
+def test_linear_h0_resume_matches_one_pass():
+    """Two calls, the second started from the first's last state, give the states
+    of one call over the whole sequence."""
+    say("linear fwd resume fp32 B=2 T=3000 D=256 split at 1234")
+    x = lin_case(2, 3000, 256, seed=24)
+    a_d, a = quantise(x["a"], torch.float32)
+    b_d, b = quantise(x["b"], torch.float32)
+    _, H_full = lrs.mi_linear_scan_fwd_h0(a_d, b_d, None)
+    _, H1 = lrs.mi_linear_scan_fwd_h0(a_d[:, :1234].contiguous(), b_d[:, :1234].contiguous(), None)
+    _, H2 = lrs.mi_linear_scan_fwd_h0(a_d[:, 1234:].contiguous(), b_d[:, 1234:].contiguous(),
+                                      H1[:, -1].contiguous())
+    torch.cuda.synchronize()
+    _, H_r = oracle.linear_scan_fwd(a, b)
+    _, H_s = oracle.linear_scan_fwd(np.abs(a), np.abs(b))
+    e = scaled_err(np.concatenate([to_np(H1), to_np(H2)], axis=1), H_r, H_s)
+    assert e <= TOL[torch.float32], e
+    assert scaled_err(to_np(H_full), H_r, H_s) <= TOL[torch.float32]
+
+
+def test_linear_h0_no_steps():
+    say("linear bwd from h0, T=0 B=2 D=8")
+    z = torch.empty(2, 0, 8, device="cuda")
+    h0 = torch.ones(2, 8, device="cuda")
+    dh0 = torch.full((2, 8), float("nan"), device="cuda")
+    _, _, dh0 = lrs.mi_linear_scan_bwd_h0(z, z, z, h0, z, z, dh0=dh0)
+    torch.cuda.synchronize()
+    assert bool(torch.all(dh0 == 0))
+
+
+# ---------------------------------------------------------------------------
 # log-space scan
 # ---------------------------------------------------------------------------
 
@@ -351,6 +433,54 @@ def test_affine_edge_shapes(kv):
         x = affine_inputs_diag(Bn, T, n, k, v, seed=k * 100 + v + T, grads=True)
         errs = run_affine(x, with_bwd=True, metric="abs")
         assert max(errs.values()) <= TOL[torch.float32], ((Bn, T, n, k, v), errs)
+
+
+def run_affine_h0(x, seed, with_h0=True):
+    """GPU k x k fwd + bwd from an initial state H0 (condition-normalised error,
+    diagonally dominant inputs)."""
+    A_d, A = quantise(x["A"], torch.float32)
+    B_d, Bm = quantise(x["Bm"], torch.float32)
+    Bn, T, n, k, _ = A.shape
+    v = Bm.shape[4]
+    rg = np.random.Generator(np.random.PCG64(3000 + seed))
+    H0_d, H0 = quantise(rg.standard_normal((Bn, n, k, v)), torch.float32) if with_h0 else (None, None)
+    Ab_d, H_d = lrs.mi_affine_scan_fwd_h0(A_d, B_d, H0_d)
+    torch.cuda.synchronize()
+    Ab_r, H_r = oracle.affine_scan_fwd_h0(A, Bm, H0)
+    Ab_s, H_s = oracle.affine_scan_fwd_h0(np.abs(A), np.abs(Bm), None if H0 is None else np.abs(H0))
+    errs = {"Abar": scaled_err(to_np(Ab_d), Ab_r, Ab_s), "H": scaled_err(to_np(H_d), H_r, H_s)}
+    Ab_in_d, Ab_in = quantise(Ab_r, torch.float32)
+    H_in_d, H_in = quantise(H_r, torch.float32)
+    gA_d, gA = quantise(x["gAbar"], torch.float32)
+    gH_d, gH = quantise(x["gBbar"], torch.float32)
+    dA_d, dB_d, dH0_d = lrs.mi_affine_scan_bwd_h0(A_d, Ab_in_d, H_in_d, H0_d, gA_d, gH_d)
+    torch.cuda.synchronize()
+    dA_r, dB_r, dH0_r = oracle.affine_scan_bwd_h0(A, Ab_in, H_in, H0, gA, gH)
+    dA_s, dB_s, dH0_s = oracle.affine_scan_bwd_h0(np.abs(A), np.abs(Ab_in), np.abs(H_in),
+                                                  None if H0 is None else np.abs(H0), np.abs(gA), np.abs(gH))
+    errs.update(dA=scaled_err(to_np(dA_d), dA_r, dA_s), dB=scaled_err(to_np(dB_d), dB_r, dB_s),
+                dH0=scaled_err(to_np(dH0_d), dH0_r, dH0_s))
+    return errs
+
+
+@pytest.mark.parametrize("kv", [(4, 16), (8, 32), (3, 5), (1, 1), (16, 4)])
+def test_affine_h0(kv):
+    k, v = kv
+    for (Bn, T, n) in ((1, 1, 1), (2, 130, 5)):
+        say("affine fwd+bwd from H0 fp32 B,T,n,k,v =", (Bn, T, n, k, v))
+        x = affine_inputs_diag(Bn, T, n, k, v, seed=k * 10 + v + T, grads=True)
+        errs = run_affine_h0(x, k + v + T)
+        assert max(errs.values()) <= TOL[torch.float32], ((Bn, T, n, k, v), errs)
+
+
+def test_affine_h0_none_and_workload5_size():
+    say("affine fwd+bwd from H0 = None at workload-5 size, and with H0")
+    x = workload_inputs(5)
+    errs = run_affine_h0(x, 5, with_h0=False)
+    assert max(errs.values()) <= TOL[torch.float32], errs
+    errs = run_affine_h0(x, 5, with_h0=True)
+    print("errors", errs, flush=True)
+    assert max(errs.values()) <= TOL[torch.float32], errs
 
 
 def test_affine_rotation_long():
