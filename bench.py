@@ -69,9 +69,12 @@ def device_inputs(wid, torch, workloads):
     return {k: v.to(torch.bfloat16) for k, v in out.items()}
 
 
-def build_workload(wid, torch, lrs, workloads, on_device=False, initial_state=False):
-    """Returns (description dict, list of (kernel name, fn, algorithmic bytes), units, inputs)."""
-    w = workloads.WORKLOADS[wid]
+def build_workload(wid, torch, lrs, workloads, on_device=False, initial_state=False, storage=None):
+    """Returns (description dict, list of (kernel name, fn, algorithmic bytes), units, inputs).
+    storage overrides the workload's storage type ("f32" or "bf16")."""
+    w = dict(workloads.WORKLOADS[wid])
+    if storage:
+        w["dtype"] = storage
     log("generating inputs for workload", wid, w["name"])
     t0 = time.time()
     dtype = torch.bfloat16 if w["dtype"] == "bf16" else torch.float32
@@ -151,23 +154,23 @@ def build_workload(wid, torch, lrs, workloads, on_device=False, initial_state=Fa
     else:
         Bn, T, n, k, v = w["B"], w["T"], w["n"], w["k"], w["v"]
         S = Bn * T * n
-        ws = torch.empty(lrs.mi_affine_scan_workspace(Bn, T, n, k, v), dtype=torch.uint8, device="cuda")
+        ws = torch.empty(lrs.mi_affine_scan_workspace(Bn, T, n, k, v, dtype), dtype=torch.uint8, device="cuda")
         state["Abar"] = torch.empty_like(d["A"])
         state["Bbar"] = torch.empty_like(d["Bm"])
 
         nh = Bn * n * k * v  # initial-state elements
         if initial_state:
             g = torch.Generator(device="cuda").manual_seed(wid)
-            state["H0"] = torch.randn(Bn, n, k, v, device="cuda", generator=g)
+            state["H0"] = torch.randn(Bn, n, k, v, device="cuda", generator=g).to(dtype)
             state["dH0"] = torch.empty_like(state["H0"])
 
             def afwd():
                 lrs.mi_affine_scan_fwd_h0(d["A"], d["Bm"], state["H0"], state["Abar"], state["Bbar"], ws=ws)
-            kernels.append(("affine_scan_fwd_h0", afwd, 4 * 2 * (S * k * k + S * k * v) + 4 * nh))
+            kernels.append(("affine_scan_fwd_h0", afwd, es * 2 * (S * k * k + S * k * v) + es * nh))
         else:
             def afwd():
                 lrs.mi_affine_scan_fwd(d["A"], d["Bm"], state["Abar"], state["Bbar"], ws=ws)
-            kernels.append(("affine_scan_fwd", afwd, 4 * 2 * (S * k * k + S * k * v)))
+            kernels.append(("affine_scan_fwd", afwd, es * 2 * (S * k * k + S * k * v)))
         if "gAbar" in d:
             state["dA"] = torch.empty_like(d["A"])
             state["dB"] = torch.empty_like(d["Bm"])
@@ -175,14 +178,15 @@ def build_workload(wid, torch, lrs, workloads, on_device=False, initial_state=Fa
                 def abwd():
                     lrs.mi_affine_scan_bwd_h0(d["A"], state["Abar"], state["Bbar"], state["H0"], d["gAbar"],
                                               d["gBbar"], state["dA"], state["dB"], state["dH0"], ws=ws)
-                kernels.append(("affine_scan_bwd_h0", abwd, 4 * (4 * S * k * k + 3 * S * k * v) + 8 * nh))
+                kernels.append(("affine_scan_bwd_h0", abwd, es * (4 * S * k * k + 3 * S * k * v) + 2 * es * nh))
             else:
                 def abwd():
                     lrs.mi_affine_scan_bwd(d["A"], state["Abar"], state["Bbar"], d["gAbar"], d["gBbar"],
                                            state["dA"], state["dB"], ws=ws)
-                kernels.append(("affine_scan_bwd", abwd, 4 * (4 * S * k * k + 3 * S * k * v)))
-        desc = {"workload": "affine_scan%s %s k x k, B=%d, T=%d, n=%d, k=%d, v=%d, fp32"
-                % (" from H0" if initial_state else "", "fwd+bwd" if len(kernels) == 2 else "fwd", Bn, T, n, k, v),
+                kernels.append(("affine_scan_bwd", abwd, es * (4 * S * k * k + 3 * S * k * v)))
+        desc = {"workload": "affine_scan%s %s k x k, B=%d, T=%d, n=%d, k=%d, v=%d, %s"
+                % (" from H0" if initial_state else "", "fwd+bwd" if len(kernels) == 2 else "fwd", Bn, T, n, k, v,
+                   "fp32" if w["dtype"] == "f32" else "bf16 storage / fp32 arithmetic"),
                 "B": Bn, "T": T, "n": n, "k": k, "v": v, "storage": w["dtype"]}
         units = S
     return desc, kernels, units, d
@@ -192,10 +196,12 @@ def build_workload(wid, torch, lrs, workloads, on_device=False, initial_state=Fa
 # CPU baseline: the fp64 oracle, as it stands, on a bounded sample
 # ---------------------------------------------------------------------------
 
-def cpu_baseline(wid, torch, workloads):
+def cpu_baseline(wid, torch, workloads, storage=None):
     import numpy as np
     import oracle
-    w = workloads.WORKLOADS[wid]
+    w = dict(workloads.WORKLOADS[wid])
+    if storage:
+        w["dtype"] = storage
     dtype = torch.bfloat16 if w["dtype"] == "bf16" else torch.float32
 
     def q(a):
@@ -245,9 +251,10 @@ def cpu_baseline(wid, torch, workloads):
             if wid == 5:
                 oracle.affine_scan_bwd(x["A"], Abar, Bbar, x["gAbar"], x["gBbar"])
 
-        nbytes = 4 * 2 * (S * k * k + S * k * v)
+        es = 2 if dtype == torch.bfloat16 else 4
+        nbytes = es * 2 * (S * k * k + S * k * v)
         if wid == 5:
-            nbytes += 4 * (4 * S * k * k + 3 * S * k * v)
+            nbytes += es * (4 * S * k * k + 3 * S * k * v)
         sample = "B=1 of %d batch rows: %d head-steps" % (w["B"], S)
     # The sample is run repeatedly until about CPU_SECONDS of work is done.
     reps, t0 = 0, time.perf_counter()
@@ -263,7 +270,12 @@ def cpu_baseline(wid, torch, workloads):
 
 # ---------------------------------------------------------------------------
 
-def stored_traffic(kernel_name, digest):
+def traffic_key(kernel_name, desc):
+    """Counter readings are stored per kernel and workload shape."""
+    return "%s@%s" % (kernel_name, desc["workload"])
+
+
+def stored_traffic(key, digest):
     """HBM bytes per launch from committed rocprofv3 counter runs, if they were
     taken on the current kernel sources."""
     try:
@@ -271,7 +283,7 @@ def stored_traffic(kernel_name, digest):
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    e = t.get(kernel_name)
+    e = t.get(key)
     if not e or e.get("source_digest") != digest:
         return None
     return e.get("hbm_bytes_per_launch")
@@ -289,6 +301,8 @@ def main():
     ap.add_argument("--initial-state", action="store_true",
                     help="time the scans from a given initial state (the *_h0 entry points); "
                          "linear and k x k workloads")
+    ap.add_argument("--storage", choices=["f32", "bf16"], default=None,
+                    help="storage type of the k x k workloads (4, 5); default: the workload's own")
     ap.add_argument("--device-inputs", action="store_true",
                     help="draw workload-3 inputs on the GPU (seeded torch generator) instead of numpy")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -323,8 +337,11 @@ def main():
 
     if args.initial_state and workloads.WORKLOADS[args.workload]["op"] not in ("linear", "affine"):
         raise SystemExit("--initial-state applies to the linear and k x k workloads")
+    if args.storage and workloads.WORKLOADS[args.workload]["op"] != "affine":
+        raise SystemExit("--storage applies to the k x k workloads")
     desc, kernels, units, _keep = build_workload(args.workload, torch, lrs, workloads,
-                                                 on_device=args.device_inputs, initial_state=args.initial_state)
+                                                 on_device=args.device_inputs, initial_state=args.initial_state,
+                                                 storage=args.storage)
     stream = torch.cuda.current_stream()
 
     log("warmup", args.warmup)
@@ -376,19 +393,21 @@ def main():
     dom = max(per_kernel, key=lambda n: per_kernel[n]["avg_ms"])
     dk = per_kernel[dom]
     digest = source_digest()
+    for name in per_kernel:
+        per_kernel[name]["hbm_traffic"] = stored_traffic(traffic_key(name, desc), digest)
     achieved = dk["GB/s"]
     roofline = {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": stored_traffic(dom, digest),
+                "traffic": stored_traffic(traffic_key(dom, desc), digest),
                 "algorithmic_bytes_per_launch": dk["bytes"], "avg_launch_ms": dk["avg_ms"]}
 
     cpu = None
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle on a sample)")
-        cpu = cpu_baseline(args.workload, torch, workloads)
+        cpu = cpu_baseline(args.workload, torch, workloads, storage=args.storage)
 
     out = {
-        "metric": (METRIC if args.workload == 3 and not args.initial_state
+        "metric": (METRIC if args.workload == 3 and not args.initial_state and not args.storage
                    else "scan GB/s and % HBM peak, " + desc["workload"]),
         "value": round(value, 1),
         "unit": "GB/s",

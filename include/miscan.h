@@ -155,7 +155,8 @@ mi_status mi_scan_log_bwd(const void *log_coeffs, const void *log_values, const 
 
 /* ------------------------------------------------------------------------ */
 /* k x k matrix-affine scan ("Triton kernels", Kernel entry points:         */
-/* affine_scan_fwd, affine_scan_bwd).  Dtype: MI_F32.  1 <= k <= 16,        */
+/* affine_scan_fwd, affine_scan_bwd).  Dtypes: MI_F32, MI_BF16 (storage;   */
+/* arithmetic fp32).  1 <= k <= 16,                                          */
 /* 1 <= v <= 128.                                                           */
 /* ------------------------------------------------------------------------ */
 

@@ -328,7 +328,7 @@ def _affine_shapes(A, Bm):
 
 
 def mi_affine_scan_fwd(A, Bm, Abar=None, Bbar=None, *, ws=None, stream=None):
-    """(Abar, Bbar) = affine_scan_fwd(A (B,T,n,k,k), Bm (B,T,n,k,v)); float32."""
+    """(Abar, Bbar) = affine_scan_fwd(A (B,T,n,k,k), Bm (B,T,n,k,v)); float32 or bfloat16 storage."""
     A, Bm = _dev_tensor(A, "A"), _dev_tensor(Bm, "Bm")
     _same(A, Bm)
     Bn, T, n, k, v = _affine_shapes(A, Bm)
@@ -344,7 +344,7 @@ def mi_affine_scan_fwd(A, Bm, Abar=None, Bbar=None, *, ws=None, stream=None):
 
 
 def mi_affine_scan_bwd(A, Abar, Bbar, gAbar, gBbar, dA=None, dB=None, *, ws=None, stream=None):
-    """(dA, dB) = affine_scan_bwd(A, Abar, Bbar, gAbar, gBbar); float32."""
+    """(dA, dB) = affine_scan_bwd(A, Abar, Bbar, gAbar, gBbar); float32 or bfloat16 storage."""
     A, Abar, Bbar, gAbar, gBbar = (_dev_tensor(t, nm) for t, nm in
                                    ((A, "A"), (Abar, "Abar"), (Bbar, "Bbar"),
                                     (gAbar, "gAbar"), (gBbar, "gBbar")))

@@ -84,10 +84,47 @@ __device__ __forceinline__ void stv(float *dst, const float *src) {
     }
 }
 
+// Global tensors are stored as TS (float or bf16); arithmetic is fp32.
+// ld_g / st_g move N consecutive elements (a vector access when the width
+// allows), widening bf16 on loads and rounding to nearest even on stores.
+template <typename TS, int N>
+__device__ __forceinline__ void ld_g(float *dst, const TS *src) {
+    constexpr int W = (int)(16 / sizeof(TS)) < N ? (int)(16 / sizeof(TS)) : N;  // elements per access
+    static_assert(N % W == 0, "vector width");
+    using PK = Pack<TS, W>;
+#pragma unroll
+    for (int i = 0; i < N; i += W)
+        PK::unpack(*reinterpret_cast<const typename PK::raw_t *>(src + i), dst + i);
+}
+template <typename TS, int N, bool NT>
+__device__ __forceinline__ void st_g(TS *dst, const float *src) {
+    constexpr int W = (int)(16 / sizeof(TS)) < N ? (int)(16 / sizeof(TS)) : N;
+    static_assert(N % W == 0, "vector width");
+    using PK = Pack<TS, W>;
+#pragma unroll
+    for (int i = 0; i < N; i += W) {
+        const typename PK::raw_t r = PK::pack(src + i);
+        if constexpr (NT) __builtin_nontemporal_store(r, reinterpret_cast<typename PK::raw_t *>(dst + i));
+        else *reinterpret_cast<typename PK::raw_t *>(dst + i) = r;
+    }
+}
+template <typename TS>
+__device__ __forceinline__ float ld1(const TS *src) {
+    float f[1];
+    ld_g<TS, 1>(f, src);
+    return f[0];
+}
+template <typename TS>
+__device__ __forceinline__ void st1(TS *dst, float v) {
+    const float f[1] = {v};
+    st_g<TS, 1, false>(dst, f);
+}
+
+// Tensor pointers are untyped here; the kernels read them as TS.
 struct FwdArgs {
-    const float *A, *Bm;
-    float *Abar, *Bbar;
-    const float *H0;  // initial state (B, n, k, v) for the H0 kernels; NULL = zero
+    const void *A, *Bm;
+    void *Abar, *Bbar;
+    const void *H0;  // initial state (B, n, k, v) for the H0 kernels; NULL = zero
     int64_t T, heads;
     int n, k, v;
     int G, HPW, NCP, n_groups, n_chunks, NW;
@@ -95,10 +132,10 @@ struct FwdArgs {
 };
 
 struct BwdArgs {
-    const float *A, *Abar, *Bbar, *gAbar, *gBbar;
-    float *dA, *dB;
-    const float *H0;  // initial state (B, n, k, v) for the H0 kernels; NULL = zero
-    float *dH0;       // its gradient, written by the H0 kernels
+    const void *A, *Abar, *Bbar, *gAbar, *gBbar;
+    void *dA, *dB;
+    const void *H0;  // initial state (B, n, k, v) for the H0 kernels; NULL = zero
+    void *dH0;       // its gradient, written by the H0 kernels
     int64_t T, heads;
     int n, k, v;
     int G, HPW, NCP, n_groups, n_chunks, NW;
@@ -139,48 +176,52 @@ template <int KP, int CPL, bool BWD = false> struct AffL {
 };
 
 // The lane's columns of B_t (zero for Abar and padding columns, or when !ok).
-template <int KP, int CPL, bool VIO>
+template <typename TS, int KP, int CPL, bool VIO>
 __device__ __forceinline__ void load_b(float (&b)[KP][CPL], const FwdArgs &p, const Cols<CPL> &cl, int64_t m,
                                        bool ok) {
-    const int k = p.k, v = p.v;
-    const float *Bt = p.Bm + m * k * v;
+    const int k = VIO ? KP : p.k, v = p.v;
+    const TS *Bm = static_cast<const TS *>(p.Bm);
     if constexpr (VIO) {
-        if (ok && cl.kind[0] == C_H) {
+        // every lane loads (other kinds from a valid element) and selects: no
+        // branch around the loads
+        const bool use = ok && cl.kind[0] == C_H;
+        const TS *src = use ? Bm + m * k * v + cl.col[0] : Bm;
+        const int ld = use ? v : 0;
 #pragma unroll
-            for (int i = 0; i < KP; ++i) ldv<CPL>(b[i], Bt + i * v + cl.col[0]);
-        } else {
+        for (int i = 0; i < KP; ++i) {
+            ld_g<TS, CPL>(b[i], src + i * ld);
 #pragma unroll
-            for (int i = 0; i < KP; ++i)
-#pragma unroll
-                for (int cc = 0; cc < CPL; ++cc) b[i][cc] = 0.f;
+            for (int cc = 0; cc < CPL; ++cc) b[i][cc] = use ? b[i][cc] : 0.f;
         }
     } else {
 #pragma unroll
         for (int i = 0; i < KP; ++i)
 #pragma unroll
             for (int cc = 0; cc < CPL; ++cc)
-                b[i][cc] = (ok && cl.kind[cc] == C_H && i < k) ? Bt[i * v + cl.col[cc]] : 0.f;
+                b[i][cc] = (ok && cl.kind[cc] == C_H && i < k) ? ld1(Bm + m * k * v + i * v + cl.col[cc]) : 0.f;
     }
 }
 
 // Store the lane's columns of X_t = [Abar_t | H_t].
-template <int KP, int CPL, bool VIO>
+template <typename TS, int KP, int CPL, bool VIO>
 __device__ __forceinline__ void store_x(const FwdArgs &p, const Cols<CPL> &cl, int64_t m, const float (&x)[KP][CPL]) {
-    const int k = p.k, v = p.v;
+    const int k = VIO ? KP : p.k, v = p.v;
+    TS *Abar = static_cast<TS *>(p.Abar);
+    TS *Bbar = static_cast<TS *>(p.Bbar);
     if constexpr (VIO) {
         if (cl.kind[0] != C_PAD) {
-            float *dst = (cl.kind[0] == C_ABAR) ? p.Abar + m * k * k + cl.col[0] : p.Bbar + m * k * v + cl.col[0];
+            TS *dst = (cl.kind[0] == C_ABAR) ? Abar + m * k * k + cl.col[0] : Bbar + m * k * v + cl.col[0];
             const int ld = (cl.kind[0] == C_ABAR) ? k : v;
 #pragma unroll
-            for (int i = 0; i < KP; ++i) stv<CPL, true>(dst + i * ld, x[i]);
+            for (int i = 0; i < KP; ++i) st_g<TS, CPL, true>(dst + i * ld, x[i]);
         }
     } else {
 #pragma unroll
         for (int cc = 0; cc < CPL; ++cc)
 #pragma unroll
             for (int i = 0; i < KP; ++i) {
-                if (i < k && cl.kind[cc] == C_ABAR) p.Abar[m * k * k + i * k + cl.col[cc]] = x[i][cc];
-                if (i < k && cl.kind[cc] == C_H) p.Bbar[m * k * v + i * v + cl.col[cc]] = x[i][cc];
+                if (i < k && cl.kind[cc] == C_ABAR) st1(Abar + m * k * k + i * k + cl.col[cc], x[i][cc]);
+                if (i < k && cl.kind[cc] == C_H) st1(Bbar + m * k * v + i * v + cl.col[cc], x[i][cc]);
             }
     }
 }
@@ -195,8 +236,9 @@ __host__ __device__ constexpr int pad_bank(int f) { return f < 4 ? f : f + ((4 -
 // padded to KP x KP; identity for steps past T and for heads past the last).
 // Cooperative, coalesced: consecutive threads take consecutive float4s (or
 // floats) of the source.
-template <int KP, bool VIO>
+template <typename TS, int KP, bool VIO>
 __device__ __forceinline__ void stage_a(float *s_A, const FwdArgs &p, int grp, int64_t t_c, int CH) {
+    const TS *Ag = static_cast<const TS *>(p.A);
     constexpr int KK = KP * KP;
     constexpr int AS = pad_bank(KK);
     const int per_step = p.HPW * KK;
@@ -212,7 +254,9 @@ __device__ __forceinline__ void stage_a(float *s_A, const FwdArgs &p, int grp, i
             f32x4 val;
             if (t < p.T && gh < p.heads) {
                 const int64_t b = gh / p.n, h = gh - b * p.n;
-                val = *reinterpret_cast<const f32x4 *>(p.A + ((b * p.T + t) * p.n + h) * KK + q);
+                float w[4];
+                ld_g<TS, 4>(w, Ag + ((b * p.T + t) * p.n + h) * KK + q);
+                val.x = w[0]; val.y = w[1]; val.z = w[2]; val.w = w[3];
             } else {
                 val.x = (q / KP == q % KP) ? 1.f : 0.f;
                 val.y = ((q + 1) / KP == (q + 1) % KP) ? 1.f : 0.f;
@@ -234,7 +278,7 @@ __device__ __forceinline__ void stage_a(float *s_A, const FwdArgs &p, int grp, i
             float val = (i == j) ? 1.f : 0.f;
             if (t < p.T && gh < p.heads && i < k && j < k) {
                 const int64_t b = gh / p.n, h = gh - b * p.n;
-                val = p.A[((b * p.T + t) * p.n + h) * k * k + i * k + j];
+                val = ld1(Ag + ((b * p.T + t) * p.n + h) * k * k + i * k + j);
             }
             s_A[(s * p.HPW + hs) * AS + q] = val;
         }
@@ -372,7 +416,7 @@ __device__ __forceinline__ void payload_cols(float (&x)[KP][CPL], rsrc_t r, uint
 // The chunk is read from memory once.
 // H0: the scan starts from X_0 = [I | H0] (Bbar then holds the states from
 // H0): the state entering chunk 0 is that instead of [I | 0].
-template <int KP, int CPL, bool VIO, bool H0 = false>
+template <typename TS, int KP, int CPL, bool VIO, bool H0 = false>
 __global__ __launch_bounds__(512) void affine_fwd_kernel(FwdArgs p) {
     constexpr int L = AffL<KP, CPL>::L;
     extern __shared__ __align__(16) float s_dyn[];
@@ -427,8 +471,8 @@ __global__ __launch_bounds__(512) void affine_fwd_kernel(FwdArgs p) {
     // 1. B of the wave's steps (registers) and the chunk's A (LDS).
     float rb[L][KP][CPL];
 #pragma unroll
-    for (int r = 0; r < L; ++r) load_b<KP, CPL, VIO>(rb[r], p, cl, m0 + (t_w + r) * p.n, active && t_w + r < p.T);
-    stage_a<KP, VIO>(s_A, p, grp, t_c, CH);
+    for (int r = 0; r < L; ++r) load_b<TS, KP, CPL, VIO>(rb[r], p, cl, m0 + (t_w + r) * p.n, active && t_w + r < p.T);
+    stage_a<TS, KP, VIO>(s_A, p, grp, t_c, CH);
     lds_barrier();
 
     // 2. The wave's transform from [I | 0].
@@ -484,7 +528,8 @@ __global__ __launch_bounds__(512) void affine_fwd_kernel(FwdArgs p) {
                 for (int i = 0; i < KP; ++i)
 #pragma unroll
                     for (int cc = 0; cc < CPL; ++cc)
-                        if (i < k && cl.kind[cc] == C_H) S[i][cc] = p.H0[gh * k * p.v + i * p.v + cl.col[cc]];
+                        if (i < k && cl.kind[cc] == C_H)
+                            S[i][cc] = ld1(static_cast<const TS *>(p.H0) + gh * k * p.v + i * p.v + cl.col[cc]);
             }
         }
         // the wave's own s_C writes are complete before other lanes read them
@@ -521,7 +566,7 @@ __global__ __launch_bounds__(512) void affine_fwd_kernel(FwdArgs p) {
 #pragma unroll
     for (int r = 0; r < L; ++r) {
         step_lds<KP, CPL>(S, s_A + ((wave * L + r) * HPW + hsc) * AS, rb[r]);
-        if (active && t_w + r < p.T) store_x<KP, CPL, VIO>(p, cl, m0 + (t_w + r) * p.n, S);
+        if (active && t_w + r < p.T) store_x<TS, KP, CPL, VIO>(p, cl, m0 + (t_w + r) * p.n, S);
     }
 }
 
@@ -541,9 +586,10 @@ template <int KP> struct AffRB {
 // matrix index m: the k x k tensor for Z_M columns, the k x v tensor for Z_L
 // columns.  Lanes of other kinds (and !ok) point at a valid element and are
 // zeroed by the caller: every lane loads, so no branch sits around the loads.
-template <int CPL>
-__device__ __forceinline__ const float *y_src(const float *kk, const float *kv, const Cols<CPL> &cl, int64_t m,
-                                              int k, int v, bool ok, int &ld) {
+template <typename TS, int CPL>
+__device__ __forceinline__ const TS *y_src(const void *kk_, const void *kv_, const Cols<CPL> &cl, int64_t m,
+                                           int k, int v, bool ok, int &ld) {
+    const TS *kk = static_cast<const TS *>(kk_), *kv = static_cast<const TS *>(kv_);
     const bool is_m = ok && cl.kind[0] == Z_M, is_l = ok && cl.kind[0] == Z_L;
     ld = is_l ? v : k;
     return is_m ? kk + m * k * k + cl.col[0] : is_l ? kv + m * k * v + cl.col[0] : kk;
@@ -551,17 +597,17 @@ __device__ __forceinline__ const float *y_src(const float *kk, const float *kv, 
 
 // The lane's columns of G_t = [gAbar_t | gBbar_t] (zero for P and padding
 // columns, or when !ok).
-template <int KP, int CPL, bool VIO>
+template <typename TS, int KP, int CPL, bool VIO>
 __device__ __forceinline__ void load_g(float (&g)[KP][CPL], const BwdArgs &p, const Cols<CPL> &cl, int64_t m,
                                        bool ok) {
-    const int k = p.k, v = p.v;
+    const int k = VIO ? KP : p.k, v = p.v;
     if constexpr (VIO) {
         int ld;
-        const float *src = y_src<CPL>(p.gAbar, p.gBbar, cl, m, k, v, ok, ld);
+        const TS *src = y_src<TS, CPL>(p.gAbar, p.gBbar, cl, m, k, v, ok, ld);
         const bool use = ok && (cl.kind[0] == Z_M || cl.kind[0] == Z_L);
 #pragma unroll
         for (int i = 0; i < KP; ++i) {
-            ldv<CPL>(g[i], src + i * ld);
+            ld_g<TS, CPL>(g[i], src + i * ld);
 #pragma unroll
             for (int cc = 0; cc < CPL; ++cc) g[i][cc] = use ? g[i][cc] : 0.f;
         }
@@ -572,8 +618,8 @@ __device__ __forceinline__ void load_g(float (&g)[KP][CPL], const BwdArgs &p, co
             for (int cc = 0; cc < CPL; ++cc) {
                 float gv = 0.f;
                 if (ok && i < k) {
-                    if (cl.kind[cc] == Z_M) gv = p.gAbar[m * k * k + i * k + cl.col[cc]];
-                    else if (cl.kind[cc] == Z_L) gv = p.gBbar[m * k * v + i * v + cl.col[cc]];
+                    if (cl.kind[cc] == Z_M) gv = ld1(static_cast<const TS *>(p.gAbar) + m * k * k + i * k + cl.col[cc]);
+                    else if (cl.kind[cc] == Z_L) gv = ld1(static_cast<const TS *>(p.gBbar) + m * k * v + i * v + cl.col[cc]);
                 }
                 g[i][cc] = gv;
             }
@@ -582,17 +628,17 @@ __device__ __forceinline__ void load_g(float (&g)[KP][CPL], const BwdArgs &p, co
 
 // The lane's columns of X_{t-1} = [Abar_{t-1} | Bbar_{t-1}] matching its Y
 // columns ([I | 0] at t = 0; zero when !ok).
-template <int KP, int CPL, bool VIO, bool H0 = false>
+template <typename TS, int KP, int CPL, bool VIO, bool H0 = false>
 __device__ __forceinline__ void load_xprev(float (&x)[KP][CPL], const BwdArgs &p, const Cols<CPL> &cl, int64_t m,
                                            int64_t t, bool ok, int64_t gh = 0) {
-    const int k = p.k, v = p.v;
+    const int k = VIO ? KP : p.k, v = p.v;
     if constexpr (VIO) {
         int ld;
-        const float *src = y_src<CPL>(p.Abar, p.Bbar, cl, m - p.n, k, v, ok && t > 0, ld);
+        const TS *src = y_src<TS, CPL>(p.Abar, p.Bbar, cl, m - p.n, k, v, ok && t > 0, ld);
         const bool use = ok && t > 0 && (cl.kind[0] == Z_M || cl.kind[0] == Z_L);
 #pragma unroll
         for (int i = 0; i < KP; ++i) {
-            ldv<CPL>(x[i], src + i * ld);
+            ld_g<TS, CPL>(x[i], src + i * ld);
 #pragma unroll
             for (int cc = 0; cc < CPL; ++cc) {
                 const float id = (ok && t == 0 && cl.kind[cc] == Z_M && i == cl.col[cc]) ? 1.f : 0.f;
@@ -607,9 +653,10 @@ __device__ __forceinline__ void load_xprev(float (&x)[KP][CPL], const BwdArgs &p
                 float xv = 0.f;
                 if (ok && i < k) {
                     if (cl.kind[cc] == Z_M)
-                        xv = (t > 0) ? p.Abar[(m - p.n) * k * k + i * k + cl.col[cc]] : (i == cl.col[cc] ? 1.f : 0.f);
+                        xv = (t > 0) ? ld1(static_cast<const TS *>(p.Abar) + (m - p.n) * k * k + i * k + cl.col[cc])
+                                     : (i == cl.col[cc] ? 1.f : 0.f);
                     else if (cl.kind[cc] == Z_L && t > 0)
-                        xv = p.Bbar[(m - p.n) * k * v + i * v + cl.col[cc]];
+                        xv = ld1(static_cast<const TS *>(p.Bbar) + (m - p.n) * k * v + i * v + cl.col[cc]);
                 }
                 x[i][cc] = xv;
             }
@@ -620,7 +667,8 @@ __device__ __forceinline__ void load_xprev(float (&x)[KP][CPL], const BwdArgs &p
             for (int i = 0; i < KP; ++i)
 #pragma unroll
                 for (int cc = 0; cc < CPL; ++cc)
-                    if (i < k && cl.kind[cc] == Z_L) x[i][cc] = p.H0[gh * k * v + i * v + cl.col[cc]];
+                    if (i < k && cl.kind[cc] == Z_L)
+                        x[i][cc] = ld1(static_cast<const TS *>(p.H0) + gh * k * v + i * v + cl.col[cc]);
         }
     }
 }
@@ -629,8 +677,9 @@ __device__ __forceinline__ void load_xprev(float (&x)[KP][CPL], const BwdArgs &p
 // stage_a: zero for t = T - 1 (A_{T+1} = 0 in the page's 1-based time) and the
 // identity for steps past T or heads past the last.  Sources are read as
 // float4 rows and written transposed.
-template <int KP, bool VIO>
+template <typename TS, int KP, bool VIO>
 __device__ __forceinline__ void stage_at(float *s_A, const BwdArgs &p, int grp, int64_t t_c, int CH) {
+    const TS *Ag = static_cast<const TS *>(p.A);
     constexpr int KK = KP * KP;
     constexpr int AS = pad_bank(KK);
     const int per_step = p.HPW * KK;
@@ -648,8 +697,7 @@ __device__ __forceinline__ void stage_at(float *s_A, const BwdArgs &p, int grp, 
             float val[4];
             if (t + 1 < p.T && gh < p.heads) {
                 const int64_t b = gh / p.n, h = gh - b * p.n;
-                const f32x4 w = *reinterpret_cast<const f32x4 *>(p.A + ((b * p.T + t + 1) * p.n + h) * KK + q);
-                val[0] = w.x; val[1] = w.y; val[2] = w.z; val[3] = w.w;
+                ld_g<TS, 4>(val, Ag + ((b * p.T + t + 1) * p.n + h) * KK + q);
             } else {
                 const float d = (t < p.T && gh < p.heads) ? 0.f : 1.f;  // A_{T+1} = 0, identity elsewhere
 #pragma unroll
@@ -671,7 +719,7 @@ __device__ __forceinline__ void stage_at(float *s_A, const BwdArgs &p, int grp, 
             float val;
             if (t + 1 < p.T && gh < p.heads) {
                 const int64_t b = gh / p.n, h = gh - b * p.n;
-                val = (i < k && j < k) ? p.A[((b * p.T + t + 1) * p.n + h) * k * k + j * k + i] : (i == j ? 1.f : 0.f);
+                val = (i < k && j < k) ? ld1(Ag + ((b * p.T + t + 1) * p.n + h) * k * k + j * k + i) : (i == j ? 1.f : 0.f);
             } else {
                 val = (i == j) ? ((t < p.T && gh < p.heads) ? 0.f : 1.f) : 0.f;
             }
@@ -698,7 +746,7 @@ __device__ __forceinline__ void stage_at(float *s_A, const BwdArgs &p, int grp, 
 //     across the head's lanes through a per-wave LDS buffer (RB rows a round).
 // H0: the forward started from [I | H0]: X_{-1} = [I | H0] in dA at the first
 // step, and dH0 = A_1^T Lam_1 is written as well.
-template <int KP, int CPL, bool VIO, bool H0 = false>
+template <typename TS, int KP, int CPL, bool VIO, bool H0 = false>
 __global__ __launch_bounds__(512) void affine_bwd_kernel(BwdArgs p) {
     constexpr int L = AffL<KP, CPL, true>::L;
     constexpr int RB = AffRB<KP>::RB;
@@ -756,8 +804,8 @@ __global__ __launch_bounds__(512) void affine_bwd_kernel(BwdArgs p) {
     // 1. G columns (registers), A_{t+1}^T (LDS).
     float rg[L][KP][CPL];
 #pragma unroll
-    for (int r = 0; r < L; ++r) load_g<KP, CPL, VIO>(rg[r], p, cl, m0 + (t_w + r) * p.n, active && t_w + r < p.T);
-    stage_at<KP, VIO>(s_A, p, grp, t_c, CH);
+    for (int r = 0; r < L; ++r) load_g<TS, KP, CPL, VIO>(rg[r], p, cl, m0 + (t_w + r) * p.n, active && t_w + r < p.T);
+    stage_at<TS, KP, VIO>(s_A, p, grp, t_c, CH);
     lds_barrier();
 
     // 2. The wave's reverse transform from [I | 0 | 0].
@@ -777,7 +825,7 @@ __global__ __launch_bounds__(512) void affine_bwd_kernel(BwdArgs p) {
     float rx[L][KP][CPL];
 #pragma unroll
     for (int r = 0; r < L; ++r)
-        load_xprev<KP, CPL, VIO, H0>(rx[r], p, cl, m0 + (t_w + r) * p.n, t_w + r, active && t_w + r < p.T, gh);
+        load_xprev<TS, KP, CPL, VIO, H0>(rx[r], p, cl, m0 + (t_w + r) * p.n, t_w + r, active && t_w + r < p.T, gh);
 
     // 3. Inclusive suffix: after the round with offset o, wave w holds
     //    T_w o T_{w+1} o ... (T of later waves applied first).
@@ -855,7 +903,8 @@ __global__ __launch_bounds__(512) void affine_bwd_kernel(BwdArgs p) {
                 for (int j = 0; j < KP; ++j) {
                     float arow[KP];  // row j of A_1
 #pragma unroll
-                    for (int i = 0; i < KP; ++i) arow[i] = (j < k && i < k) ? p.A[m * k * k + j * k + i] : 0.f;
+                    for (int i = 0; i < KP; ++i)
+                        arow[i] = (j < k && i < k) ? ld1(static_cast<const TS *>(p.A) + m * k * k + j * k + i) : 0.f;
 #pragma unroll
                     for (int i = 0; i < KP; ++i)
 #pragma unroll
@@ -865,7 +914,7 @@ __global__ __launch_bounds__(512) void affine_bwd_kernel(BwdArgs p) {
                 for (int cc = 0; cc < CPL; ++cc)
 #pragma unroll
                     for (int i = 0; i < KP; ++i)
-                        if (i < k && cl.kind[cc] == Z_L) p.dH0[gh * k * v + i * v + cl.col[cc]] = dh[i][cc];
+                        if (i < k && cl.kind[cc] == Z_L) st1(static_cast<TS *>(p.dH0) + gh * k * v + i * v + cl.col[cc], dh[i][cc]);
             }
         }
         // dB_t = Lam_t
@@ -873,14 +922,14 @@ __global__ __launch_bounds__(512) void affine_bwd_kernel(BwdArgs p) {
             if constexpr (VIO) {
                 if (cl.kind[0] == Z_L) {
 #pragma unroll
-                    for (int i = 0; i < KP; ++i) stv<CPL, true>(p.dB + m * k * v + i * v + cl.col[0], S[i]);
+                    for (int i = 0; i < KP; ++i) st_g<TS, CPL, true>(static_cast<TS *>(p.dB) + m * k * v + i * v + cl.col[0], S[i]);
                 }
             } else {
 #pragma unroll
                 for (int cc = 0; cc < CPL; ++cc)
 #pragma unroll
                     for (int i = 0; i < KP; ++i)
-                        if (i < k && cl.kind[cc] == Z_L) p.dB[m * k * v + i * v + cl.col[cc]] = S[i][cc];
+                        if (i < k && cl.kind[cc] == Z_L) st1(static_cast<TS *>(p.dB) + m * k * v + i * v + cl.col[cc], S[i][cc]);
             }
         }
         // dA_t = Y_t X_{t-1}^T, RB rows a round
@@ -917,11 +966,11 @@ __global__ __launch_bounds__(512) void affine_bwd_kernel(BwdArgs p) {
                             for (int u = 0; u < 4; ++u) acc[u] += q[u];
                         }
                         if constexpr (VIO) {
-                            if (i < k) stv<4, true>(p.dA + m * k * k + (int64_t)i * k + j0, acc);
+                            if (i < k) st_g<TS, 4, true>(static_cast<TS *>(p.dA) + m * k * k + (int64_t)i * k + j0, acc);
                         } else {
 #pragma unroll
                             for (int u = 0; u < 4; ++u)
-                                if (i < k && j0 + u < k) p.dA[m * k * k + (int64_t)i * k + j0 + u] = acc[u];
+                                if (i < k && j0 + u < k) st1(static_cast<TS *>(p.dA) + m * k * k + (int64_t)i * k + j0 + u, acc[u]);
                         }
                     }
                 } else {
@@ -930,7 +979,7 @@ __global__ __launch_bounds__(512) void affine_bwd_kernel(BwdArgs p) {
                         const int i = ib + ii;
                         float acc = 0.f;
                         for (int gg = 0; gg < G; ++gg) acc += part[((hs * G + gg) * RB + ii) * KP + j];
-                        if (i < k && j < k) p.dA[m * k * k + (int64_t)i * k + j] = acc;
+                        if (i < k && j < k) st1(static_cast<TS *>(p.dA) + m * k * k + (int64_t)i * k + j, acc);
                     }
                 }
             }
@@ -947,7 +996,8 @@ __global__ __launch_bounds__(512) void affine_bwd_kernel(BwdArgs p) {
 struct AffPlan {
     int KP, CPL;
     bool VIO;
-    bool h0;  // launch the initial-state (H0) kernels
+    bool h0;    // launch the initial-state (H0) kernels
+    bool bf16;  // bf16 storage (fp32 otherwise)
     int G, HPW, NCP, n_groups, n_chunks, LC, NW;
     size_t n_slots, payload, lds_bytes;
     bool ok;  // the work-item count fits the int32 ticket space, the LDS the workgroup
@@ -981,6 +1031,7 @@ inline AffPlan make_plan(int64_t B, int64_t T, int64_t n, int k, int v, bool bwd
     pl.CPL = CPL;
     pl.VIO = VIO;
     pl.h0 = false;
+    pl.bf16 = false;
     const int ncols = bwd ? 2 * k + v : k + v;
     pl.G = (ncols + CPL - 1) / CPL;
     if (pl.G > 64) {  // a head must fit one wave: this tiling is not usable
@@ -1047,30 +1098,36 @@ inline mi_status allow_lds(K kernel, size_t bytes) {
                                (int)bytes) == hipSuccess ? MI_OK : MI_ERR_LAUNCH;
 }
 
-template <int KP, int CPL, bool VIO, bool H0>
+template <typename TS, int KP, int CPL, bool VIO, bool H0>
 mi_status fwd_launch_h(const AffPlan &pl, FwdArgs &a, hipStream_t s) {
     if (pl.LC != pl.NW * AffL<KP, CPL>::L) return MI_ERR_UNSUPPORTED;  // host and kernel tilings agree
-    if (allow_lds(&affine_fwd_kernel<KP, CPL, VIO, H0>, pl.lds_bytes) != MI_OK) return MI_ERR_LAUNCH;
-    hipLaunchKernelGGL((affine_fwd_kernel<KP, CPL, VIO, H0>), dim3((unsigned)pl.n_slots), dim3(64 * pl.NW),
+    if (allow_lds(&affine_fwd_kernel<TS, KP, CPL, VIO, H0>, pl.lds_bytes) != MI_OK) return MI_ERR_LAUNCH;
+    hipLaunchKernelGGL((affine_fwd_kernel<TS, KP, CPL, VIO, H0>), dim3((unsigned)pl.n_slots), dim3(64 * pl.NW),
                        pl.lds_bytes, s, a);
     return launch_status();
 }
-// h0_kernels is carried in the plan's caller: see dispatch_fwd.
+// Storage type and initial-state kernels from the plan.
 template <int KP, int CPL, bool VIO>
 mi_status fwd_launch(const AffPlan &pl, FwdArgs &a, hipStream_t s) {
-    return pl.h0 ? fwd_launch_h<KP, CPL, VIO, true>(pl, a, s) : fwd_launch_h<KP, CPL, VIO, false>(pl, a, s);
+    if (pl.bf16)
+        return pl.h0 ? fwd_launch_h<bf16_t, KP, CPL, VIO, true>(pl, a, s)
+                     : fwd_launch_h<bf16_t, KP, CPL, VIO, false>(pl, a, s);
+    return pl.h0 ? fwd_launch_h<float, KP, CPL, VIO, true>(pl, a, s) : fwd_launch_h<float, KP, CPL, VIO, false>(pl, a, s);
 }
-template <int KP, int CPL, bool VIO, bool H0>
+template <typename TS, int KP, int CPL, bool VIO, bool H0>
 mi_status bwd_launch_h(const AffPlan &pl, BwdArgs &a, hipStream_t s) {
     if (pl.LC != pl.NW * AffL<KP, CPL, true>::L) return MI_ERR_UNSUPPORTED;
-    if (allow_lds(&affine_bwd_kernel<KP, CPL, VIO, H0>, pl.lds_bytes) != MI_OK) return MI_ERR_LAUNCH;
-    hipLaunchKernelGGL((affine_bwd_kernel<KP, CPL, VIO, H0>), dim3((unsigned)pl.n_slots), dim3(64 * pl.NW),
+    if (allow_lds(&affine_bwd_kernel<TS, KP, CPL, VIO, H0>, pl.lds_bytes) != MI_OK) return MI_ERR_LAUNCH;
+    hipLaunchKernelGGL((affine_bwd_kernel<TS, KP, CPL, VIO, H0>), dim3((unsigned)pl.n_slots), dim3(64 * pl.NW),
                        pl.lds_bytes, s, a);
     return launch_status();
 }
 template <int KP, int CPL, bool VIO>
 mi_status bwd_launch(const AffPlan &pl, BwdArgs &a, hipStream_t s) {
-    return pl.h0 ? bwd_launch_h<KP, CPL, VIO, true>(pl, a, s) : bwd_launch_h<KP, CPL, VIO, false>(pl, a, s);
+    if (pl.bf16)
+        return pl.h0 ? bwd_launch_h<bf16_t, KP, CPL, VIO, true>(pl, a, s)
+                     : bwd_launch_h<bf16_t, KP, CPL, VIO, false>(pl, a, s);
+    return pl.h0 ? bwd_launch_h<float, KP, CPL, VIO, true>(pl, a, s) : bwd_launch_h<float, KP, CPL, VIO, false>(pl, a, s);
 }
 
 // Instantiated tiles: vector IO for k in {4,8,16} (CPL 4) and {2,4,8,16}
@@ -1116,18 +1173,17 @@ size_t affine_workspace_bytes(int64_t B, int64_t T, int64_t n, int64_t k, int64_
 }
 
 mi_status launch_affine_fwd(const void *A, const void *Bm, void *Abar, void *Bbar, int64_t B,
-                            int64_t T, int64_t n, int64_t k, int64_t v, void *ws,
+                            int64_t T, int64_t n, int64_t k, int64_t v, mi_dtype dt, void *ws,
                             size_t ws_bytes, hipStream_t s, bool h0_kernels, const void *H0) {
     const bool p16 = aligned16(A) && aligned16(Bm) && aligned16(Abar) && aligned16(Bbar);
     AffPlan pl = choose_plan(B, T, n, (int)k, (int)v, false, p16);
     if (!pl.ok) return MI_ERR_UNSUPPORTED;
     pl.h0 = h0_kernels;
+    pl.bf16 = dt == MI_BF16;
     WsLayout lay(pl.n_slots, pl.payload);
     if (ws == nullptr || ws_bytes < lay.total) return MI_ERR_WORKSPACE;
     FwdArgs a;
-    a.A = static_cast<const float *>(A); a.Bm = static_cast<const float *>(Bm);
-    a.Abar = static_cast<float *>(Abar); a.Bbar = static_cast<float *>(Bbar);
-    a.H0 = static_cast<const float *>(H0);
+    a.A = A; a.Bm = Bm; a.Abar = Abar; a.Bbar = Bbar; a.H0 = H0;
     a.T = T; a.heads = B * n; a.n = (int)n; a.k = (int)k; a.v = (int)v;
     a.G = pl.G; a.HPW = pl.HPW; a.NCP = pl.NCP; a.n_groups = pl.n_groups;
     a.n_chunks = pl.n_chunks; a.NW = pl.NW;
@@ -1139,7 +1195,7 @@ mi_status launch_affine_fwd(const void *A, const void *Bm, void *Abar, void *Bba
 
 mi_status launch_affine_bwd(const void *A, const void *Abar, const void *Bbar,
                             const void *gAbar, const void *gBbar, void *dA, void *dB,
-                            int64_t B, int64_t T, int64_t n, int64_t k, int64_t v, void *ws,
+                            int64_t B, int64_t T, int64_t n, int64_t k, int64_t v, mi_dtype dt, void *ws,
                             size_t ws_bytes, hipStream_t s, bool h0_kernels, const void *H0, void *dH0) {
     const void *ptrs[7] = {A, Abar, Bbar, gAbar, gBbar, dA, dB};
     bool p16 = true;
@@ -1147,15 +1203,12 @@ mi_status launch_affine_bwd(const void *A, const void *Abar, const void *Bbar,
     AffPlan pl = choose_plan(B, T, n, (int)k, (int)v, true, p16);
     if (!pl.ok) return MI_ERR_UNSUPPORTED;
     pl.h0 = h0_kernels;
+    pl.bf16 = dt == MI_BF16;
     WsLayout lay(pl.n_slots, pl.payload);
     if (ws == nullptr || ws_bytes < lay.total) return MI_ERR_WORKSPACE;
     BwdArgs a;
-    a.H0 = static_cast<const float *>(H0);
-    a.dH0 = static_cast<float *>(dH0);
-    a.A = static_cast<const float *>(A); a.Abar = static_cast<const float *>(Abar);
-    a.Bbar = static_cast<const float *>(Bbar); a.gAbar = static_cast<const float *>(gAbar);
-    a.gBbar = static_cast<const float *>(gBbar);
-    a.dA = static_cast<float *>(dA); a.dB = static_cast<float *>(dB);
+    a.H0 = H0; a.dH0 = dH0;
+    a.A = A; a.Abar = Abar; a.Bbar = Bbar; a.gAbar = gAbar; a.gBbar = gBbar; a.dA = dA; a.dB = dB;
     a.T = T; a.heads = B * n; a.n = (int)n; a.k = (int)k; a.v = (int)v;
     a.G = pl.G; a.HPW = pl.HPW; a.NCP = pl.NCP; a.n_groups = pl.n_groups;
     a.n_chunks = pl.n_chunks; a.NW = pl.NW;

@@ -302,13 +302,13 @@ mi_status check_affine(int64_t B, int64_t T, int64_t n, int64_t k, int64_t v, mi
                        int64_t *a_bytes, int64_t *b_bytes, bool *empty) {
     if (B < 0 || T < 0 || n < 0 || k < 0 || v < 0) return MI_ERR_INVALID_ARG;
     if (!dtype_known(dt)) return MI_ERR_UNSUPPORTED;
-    if (dt != MI_F32) return MI_ERR_UNSUPPORTED;
     if (k < 1 || k > 16 || v < 1 || v > 128) return MI_ERR_UNSUPPORTED;
     *empty = (B == 0 || T == 0 || n == 0);
     int64_t s;
+    const int64_t es = (int64_t)elem_size(dt);
     if (!mul_ok(B, T, n, 1, &s)) return MI_ERR_INVALID_ARG;
-    if (!mul_ok(s, k, k, 4, a_bytes)) return MI_ERR_INVALID_ARG;
-    if (!mul_ok(s, k, v, 4, b_bytes)) return MI_ERR_INVALID_ARG;
+    if (!mul_ok(s, k, k, es, a_bytes)) return MI_ERR_INVALID_ARG;
+    if (!mul_ok(s, k, v, es, b_bytes)) return MI_ERR_INVALID_ARG;
     return MI_OK;
 }
 
@@ -333,9 +333,9 @@ mi_status mi_affine_scan_fwd(const void *A, const void *Bm, void *Abar, void *Bb
     mi_status st = check_affine(B, T, n, k, v, dt, &ab, &bb, &empty);
     if (st != MI_OK || empty) return st;
     const Buf bufs[4] = {{A, ab}, {Bm, bb}, {Abar, ab}, {Bbar, bb}};
-    if ((st = check_buffers(bufs, 4, 2, 4)) != MI_OK) return st;
+    if ((st = check_buffers(bufs, 4, 2, elem_size(dt))) != MI_OK) return st;
     if ((st = check_ws(ws, ws_bytes, affine_workspace_bytes(B, T, n, k, v), bufs, 4)) != MI_OK) return st;
-    return launch_affine_fwd(A, Bm, Abar, Bbar, B, T, n, k, v, ws, ws_bytes, stream);
+    return launch_affine_fwd(A, Bm, Abar, Bbar, B, T, n, k, v, dt, ws, ws_bytes, stream);
 }
 
 mi_status mi_affine_scan_bwd(const void *A, const void *Abar, const void *Bbar, const void *gAbar,
@@ -348,9 +348,9 @@ mi_status mi_affine_scan_bwd(const void *A, const void *Abar, const void *Bbar, 
     if (st != MI_OK || empty) return st;
     const Buf bufs[7] = {{A, ab},     {Abar, ab}, {Bbar, bb}, {gAbar, ab},
                          {gBbar, bb}, {dA, ab},   {dB, bb}};
-    if ((st = check_buffers(bufs, 7, 2, 4)) != MI_OK) return st;
+    if ((st = check_buffers(bufs, 7, 2, elem_size(dt))) != MI_OK) return st;
     if ((st = check_ws(ws, ws_bytes, affine_workspace_bytes(B, T, n, k, v), bufs, 7)) != MI_OK) return st;
-    return launch_affine_bwd(A, Abar, Bbar, gAbar, gBbar, dA, dB, B, T, n, k, v, ws, ws_bytes, stream);
+    return launch_affine_bwd(A, Abar, Bbar, gAbar, gBbar, dA, dB, B, T, n, k, v, dt, ws, ws_bytes, stream);
 }
 
 mi_status mi_affine_scan_fwd_h0(const void *A, const void *Bm, const void *H0, void *Abar, void *H, int64_t B,
@@ -360,14 +360,14 @@ mi_status mi_affine_scan_fwd_h0(const void *A, const void *Bm, const void *H0, v
     bool empty;
     mi_status st = check_affine(B, T, n, k, v, dt, &ab, &bb, &empty);
     if (st != MI_OK || empty) return st;
-    const int64_t sb = B * n * k * v * 4;
+    const int64_t sb = B * n * k * v * (int64_t)elem_size(dt);
     const Buf with_h0[5] = {{A, ab}, {Bm, bb}, {H0, sb}, {Abar, ab}, {H, bb}};
     const Buf no_h0[4] = {{A, ab}, {Bm, bb}, {Abar, ab}, {H, bb}};
     const Buf *bufs = H0 ? with_h0 : no_h0;
     const int nb = H0 ? 5 : 4;
-    if ((st = check_buffers(bufs, nb, 2, 4)) != MI_OK) return st;
+    if ((st = check_buffers(bufs, nb, 2, elem_size(dt))) != MI_OK) return st;
     if ((st = check_ws(ws, ws_bytes, affine_workspace_bytes(B, T, n, k, v), bufs, nb)) != MI_OK) return st;
-    return launch_affine_fwd(A, Bm, Abar, H, B, T, n, k, v, ws, ws_bytes, stream, true, H0);
+    return launch_affine_fwd(A, Bm, Abar, H, B, T, n, k, v, dt, ws, ws_bytes, stream, true, H0);
 }
 
 mi_status mi_affine_scan_bwd_h0(const void *A, const void *Abar, const void *H, const void *H0, const void *gAbar,
@@ -377,9 +377,9 @@ mi_status mi_affine_scan_bwd_h0(const void *A, const void *Abar, const void *H, 
     bool empty;
     mi_status st = check_affine(B, T, n, k, v, dt, &ab, &bb, &empty);
     if (st != MI_OK) return st;
-    const int64_t sb = B * n * k * v * 4;
+    const int64_t sb = B * n * k * v * (int64_t)elem_size(dt);
     if (empty && T == 0 && B > 0 && n > 0) {  // no step: dH0 = 0
-        if (dH0 == nullptr || reinterpret_cast<uintptr_t>(dH0) % 4 != 0) return MI_ERR_INVALID_ARG;
+        if (dH0 == nullptr || reinterpret_cast<uintptr_t>(dH0) % elem_size(dt) != 0) return MI_ERR_INVALID_ARG;
         return zero_async(dH0, (size_t)sb, stream);
     }
     if (empty) return st;
@@ -388,9 +388,9 @@ mi_status mi_affine_scan_bwd_h0(const void *A, const void *Abar, const void *H, 
     const Buf no_h0[8] = {{A, ab}, {Abar, ab}, {H, bb}, {gAbar, ab}, {gH, bb}, {dA, ab}, {dB, bb}, {dH0, sb}};
     const Buf *bufs = H0 ? with_h0 : no_h0;
     const int nb = H0 ? 9 : 8;
-    if ((st = check_buffers(bufs, nb, 3, 4)) != MI_OK) return st;
+    if ((st = check_buffers(bufs, nb, 3, elem_size(dt))) != MI_OK) return st;
     if ((st = check_ws(ws, ws_bytes, affine_workspace_bytes(B, T, n, k, v), bufs, nb)) != MI_OK) return st;
-    return launch_affine_bwd(A, Abar, H, gAbar, gH, dA, dB, B, T, n, k, v, ws, ws_bytes, stream, true, H0, dH0);
+    return launch_affine_bwd(A, Abar, H, gAbar, gH, dA, dB, B, T, n, k, v, dt, ws, ws_bytes, stream, true, H0, dH0);
 }
 
 }  // extern "C"

@@ -37,12 +37,12 @@ mi_status launch_log_bwd(const void *lc, const void *lv, const void *h, const vo
 size_t affine_workspace_bytes(int64_t B, int64_t T, int64_t n, int64_t k, int64_t v);
 // h0_kernels selects the initial-state kernels (H0 in, dH0 out; H0 may be NULL).
 mi_status launch_affine_fwd(const void *A, const void *Bm, void *Abar, void *Bbar,
-                            int64_t B, int64_t T, int64_t n, int64_t k, int64_t v,
+                            int64_t B, int64_t T, int64_t n, int64_t k, int64_t v, mi_dtype dt,
                             void *ws, size_t ws_bytes, hipStream_t s, bool h0_kernels = false,
                             const void *H0 = nullptr);
 mi_status launch_affine_bwd(const void *A, const void *Abar, const void *Bbar,
                             const void *gAbar, const void *gBbar, void *dA, void *dB,
-                            int64_t B, int64_t T, int64_t n, int64_t k, int64_t v,
+                            int64_t B, int64_t T, int64_t n, int64_t k, int64_t v, mi_dtype dt,
                             void *ws, size_t ws_bytes, hipStream_t s, bool h0_kernels = false,
                             const void *H0 = nullptr, void *dH0 = nullptr);
 

@@ -167,7 +167,8 @@ def test_affine_envelope():
     assert call(17, 4) == MI_ERR_UNSUPPORTED
     assert call(4, 0) == MI_ERR_UNSUPPORTED
     assert call(4, 129) == MI_ERR_UNSUPPORTED
-    assert call(4, 4, BF16) == MI_ERR_UNSUPPORTED   # k x k is built for fp32 only
+    assert call(4, 4, BF16) == MI_ERR_WORKSPACE      # bf16 storage is inside the envelope
+    assert call(4, 4, 7) == MI_ERR_UNSUPPORTED       # unknown dtype
     assert call(16, 128) == MI_ERR_WORKSPACE        # inside the envelope
     assert call(1, 1) == MI_ERR_WORKSPACE
     assert L.mi_affine_scan_workspace(1, 4, 2, 17, 4, F32) == 0

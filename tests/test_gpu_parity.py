@@ -367,17 +367,17 @@ def test_log_bwd_repeated_runs():
 # k x k scan
 # ---------------------------------------------------------------------------
 
-def run_affine(x, with_bwd, metric):
+def run_affine(x, with_bwd, metric, dtype=torch.float32):
     """metric "block": per (b, t, head) block relative to the block's largest
     entry -- for rotation inputs, whose elementwise-absolute products grow
     geometrically.  metric "abs": the condition-normalised reading of the k = 1
     scan (oracle on absolute values as the scale) -- for diagonally dominant
     inputs, whose absolute products stay bounded."""
-    A_d, A = quantise(x["A"], torch.float32)
-    B_d, Bm = quantise(x["Bm"], torch.float32)
+    A_d, A = quantise(x["A"], dtype)
+    B_d, Bm = quantise(x["Bm"], dtype)
     Bn, T, n, k, _ = A.shape
     v = Bm.shape[4]
-    ws = torch.empty(max(lrs.mi_affine_scan_workspace(Bn, T, n, k, v), 8), dtype=torch.uint8,
+    ws = torch.empty(max(lrs.mi_affine_scan_workspace(Bn, T, n, k, v, dtype), 8), dtype=torch.uint8,
                      device="cuda")
     Abar_d, Bbar_d = lrs.mi_affine_scan_fwd(A_d, B_d, ws=ws)
     torch.cuda.synchronize()
@@ -392,10 +392,10 @@ def run_affine(x, with_bwd, metric):
                 "Bbar": scaled_err(to_np(Bbar_d), Bbar_r, Bbar_s)}
     if with_bwd:
         assert metric == "abs"
-        Ab_in_d, Ab_in = quantise(Abar_r, torch.float32)
-        Bb_in_d, Bb_in = quantise(Bbar_r, torch.float32)
-        gA_d, gA = quantise(x["gAbar"], torch.float32)
-        gB_d, gB = quantise(x["gBbar"], torch.float32)
+        Ab_in_d, Ab_in = quantise(Abar_r, dtype)
+        Bb_in_d, Bb_in = quantise(Bbar_r, dtype)
+        gA_d, gA = quantise(x["gAbar"], dtype)
+        gB_d, gB = quantise(x["gBbar"], dtype)
         dA_d, dB_d = lrs.mi_affine_scan_bwd(A_d, Ab_in_d, Bb_in_d, gA_d, gB_d, ws=ws)
         torch.cuda.synchronize()
         assert timeouts(ws) == 0
@@ -481,6 +481,30 @@ def test_affine_h0_none_and_workload5_size():
     errs = run_affine_h0(x, 5, with_h0=True)
     print("errors", errs, flush=True)
     assert max(errs.values()) <= TOL[torch.float32], errs
+
+
+@pytest.mark.parametrize("kv", [(4, 16), (8, 32), (3, 5), (2, 2), (16, 8)])
+def test_affine_bf16(kv):
+    """bf16 storage, fp32 arithmetic (k x k, forward and backward)."""
+    k, v = kv
+    for (Bn, T, n) in ((1, 1, 1), (2, 300, 5)):
+        say("affine fwd+bwd bf16 B,T,n,k,v =", (Bn, T, n, k, v))
+        x = affine_inputs_diag(Bn, T, n, k, v, seed=k * 7 + v + T, grads=True)
+        errs = run_affine(x, with_bwd=True, metric="abs", dtype=torch.bfloat16)
+        assert max(errs.values()) <= TOL[torch.bfloat16], ((Bn, T, n, k, v), errs)
+
+
+def test_affine_bf16_workload_shapes():
+    """bf16 storage at the workload-5 size (fwd + bwd) and the workload-4 size
+    (fwd; rotations, block metric)."""
+    say("affine fwd+bwd bf16 at workload-5 size")
+    errs = run_affine(workload_inputs(5), with_bwd=True, metric="abs", dtype=torch.bfloat16)
+    print("errors", errs, flush=True)
+    assert max(errs.values()) <= TOL[torch.bfloat16], errs
+    say("affine fwd bf16 at workload-4 size")
+    errs = run_affine(workload_inputs(4), with_bwd=False, metric="block", dtype=torch.bfloat16)
+    print("errors", errs, flush=True)
+    assert max(errs.values()) <= TOL[torch.bfloat16], errs
 
 
 def test_affine_rotation_long():
