@@ -12,20 +12,25 @@
 // Forward.  X_t = [Abar_t | H_t] is k x (k+v) and X_t = A_t X_{t-1} + [0 | B_t]
 // with X_0 = [I | 0]: every column of X evolves on its own under the same
 // A_t.  A lane therefore owns CPL columns of one head and keeps them (k*CPL
-// fp32) in registers; the G = (k+v)/CPL lanes of a head share A_t.  A wave
-// holds HPW = 64/G heads that are adjacent in memory, so its loads and stores
-// at one time step hit one contiguous run of each tensor.  The k x k products
-// are tiny and per step, not a dense contraction: they run on the vector ALU.
+// fp32) in registers; the G = (k+v)/CPL lanes of a head share A_t, and a wave
+// has HPW = 64/G such slots.  The k x k products are tiny and per step, not a
+// dense contraction: they run on the vector ALU.
 //
-// One wave is one work item: HPW heads x one chunk of LC time steps.  Pass 1
-// composes the chunk's transform [Abar_c | H_c] from [I | 0]; the decoupled
-// look-back (common.hpp) yields the state entering the chunk; pass 2 re-reads
-// the chunk (the re-read is served by the caches) and writes the true states.
-// The look-back needs whole k x k blocks of other lanes' columns: those come
-// from the published payloads in memory, or from LDS for the wave's own.
+// In the forward the HPW slots hold HH heads x SEG time segments (HPW =
+// HH * SEG): a workgroup covers HH heads for a chunk of SEG segments of
+// NW * L steps.  Splitting a chunk into segments instead of filling the slots
+// with other heads makes chunks SEG times longer at the same registers and
+// LDS, so the chain of look-backs along time is SEG times shorter.  Pass 1 composes
+// transforms [Abar | H] from [I | 0] (per wave, then over waves and over
+// segments); the decoupled look-back (common.hpp) yields the state entering
+// the chunk; pass 2 rescans from registers and writes the true states.  The
+// look-back needs whole k x k blocks of other lanes' columns: those come from
+// the published payloads in memory, or from LDS for the workgroup's own.
 //
 // Backward.  Y_t = [M_t | Lam_t] = [gAbar_t | gBbar_t] + A_{t+1}^T Y_{t+1}
-// runs in reverse time, again column by column.  A chunk's reverse transform
+// runs in reverse time, again column by column, with HPW adjacent heads per
+// wave (loads and stores at one step hit one contiguous run of each tensor).
+// A chunk's reverse transform
 // also needs P_c = A_{t0+1}^T ... A_{t1+1}^T, so pass 1 carries k extra
 // columns Z = [P | M | Lam] started from [I | 0 | 0].  Pass 2 produces
 // dB_t = Lam_t directly and dA_t = Y_t X_{t-1}^T, a sum over the columns of
@@ -128,6 +133,7 @@ struct FwdArgs {
     int64_t T, heads;
     int n, k, v;
     int G, HPW, NCP, n_groups, n_chunks, NW;
+    int HH;  // heads per workgroup; SEG = HPW / HH time segments per chunk
     WsPtrs ws;
 };
 
@@ -139,6 +145,7 @@ struct BwdArgs {
     int64_t T, heads;
     int n, k, v;
     int G, HPW, NCP, n_groups, n_chunks, NW;
+    int HH;  // heads per workgroup; SEG = HPW / HH time segments per chunk
     WsPtrs ws;
 };
 
@@ -161,6 +168,12 @@ struct Cols {
 #endif
 #ifndef MISCAN_AFF_NWMAX
 #define MISCAN_AFF_NWMAX 8
+#endif
+// The forward at padded k >= 8 needs over 128 VGPRs a lane: with four waves
+// per workgroup two workgroups share a CU and overlap each other's loads,
+// barriers and look-back, where one eight-wave workgroup would stall alone.
+#ifndef MISCAN_AFF_NWMAX_K8
+#define MISCAN_AFF_NWMAX_K8 4
 #endif
 // The backward holds two such sets (G_t and X_{t-1} columns).
 #ifndef MISCAN_AFF_BWD_BREGS
@@ -231,56 +244,65 @@ __device__ __forceinline__ void store_x(const FwdArgs &p, const Cols<CPL> &cl, i
 // heads' blocks start in distinct banks.
 __host__ __device__ constexpr int pad_bank(int f) { return f < 4 ? f : f + ((4 - f % 32) + 32) % 32; }
 
-// A_t of the workgroup's HPW heads for the CH steps of its chunk into LDS,
-// laid out [step][head][AS] with AS = pad_bank(KP * KP) (each block zero
-// padded to KP x KP; identity for steps past T and for heads past the last).
+// Slot s of a wave holds head s % HH of the workgroup's group and segment
+// s / HH of its chunk; row q (0 <= q < CHW = NW * L) of a segment is time step
+// t_c + (s / HH) * CHW + q.
+struct SlotMap {
+    int HH, CHW;
+    __device__ __forceinline__ int64_t t(int64_t t_c, int s, int q) const { return t_c + (int64_t)(s / HH) * CHW + q; }
+    __device__ __forceinline__ int64_t head(int grp, int s) const { return (int64_t)grp * HH + s % HH; }
+};
+
+// A_t of every slot for the CHW rows of its segment into LDS, laid out
+// [row][slot][AS] with AS = pad_bank(KP * KP) (each block zero padded to
+// KP x KP; identity for steps past T and for heads past the last).
 // Cooperative, coalesced: consecutive threads take consecutive float4s (or
-// floats) of the source.
+// floats) of the source blocks.
 template <typename TS, int KP, bool VIO>
-__device__ __forceinline__ void stage_a(float *s_A, const FwdArgs &p, int grp, int64_t t_c, int CH) {
+__device__ __forceinline__ void stage_a(float *s_A, const FwdArgs &p, const SlotMap &sm, int grp, int64_t t_c) {
     const TS *Ag = static_cast<const TS *>(p.A);
     constexpr int KK = KP * KP;
     constexpr int AS = pad_bank(KK);
-    const int per_step = p.HPW * KK;
-    const int total = CH * per_step;
+    const int per_row = p.HPW * KK;
+    const int total = sm.CHW * per_row;
     if constexpr (VIO && KK % 4 == 0) {
         for (int e = (int)threadIdx.x * 4; e < total; e += (int)blockDim.x * 4) {
-            const int s = e / per_step;
-            const int rem = e - s * per_step;
+            const int q = e / per_row;
+            const int rem = e - q * per_row;
             const int hs = rem / KK;
-            const int q = rem - hs * KK;
-            const int64_t t = t_c + s;
-            const int64_t gh = (int64_t)grp * p.HPW + hs;
+            const int o = rem - hs * KK;
+            const int64_t t = sm.t(t_c, hs, q);
+            const int64_t gh = sm.head(grp, hs);
             f32x4 val;
             if (t < p.T && gh < p.heads) {
                 const int64_t b = gh / p.n, h = gh - b * p.n;
                 float w[4];
-                ld_g<TS, 4>(w, Ag + ((b * p.T + t) * p.n + h) * KK + q);
+                ld_g<TS, 4>(w, Ag + ((b * p.T + t) * p.n + h) * KK + o);
                 val.x = w[0]; val.y = w[1]; val.z = w[2]; val.w = w[3];
             } else {
-                val.x = (q / KP == q % KP) ? 1.f : 0.f;
-                val.y = ((q + 1) / KP == (q + 1) % KP) ? 1.f : 0.f;
-                val.z = ((q + 2) / KP == (q + 2) % KP) ? 1.f : 0.f;
-                val.w = ((q + 3) / KP == (q + 3) % KP) ? 1.f : 0.f;
+                val.x = (o / KP == o % KP) ? 1.f : 0.f;
+                val.y = ((o + 1) / KP == (o + 1) % KP) ? 1.f : 0.f;
+                val.z = ((o + 2) / KP == (o + 2) % KP) ? 1.f : 0.f;
+                val.w = ((o + 3) / KP == (o + 3) % KP) ? 1.f : 0.f;
             }
-            *reinterpret_cast<f32x4 *>(s_A + (s * p.HPW + hs) * AS + q) = val;
+            *reinterpret_cast<f32x4 *>(s_A + (q * p.HPW + hs) * AS + o) = val;
         }
     } else {
         const int k = p.k;
         for (int e = (int)threadIdx.x; e < total; e += (int)blockDim.x) {
-            const int s = e / per_step;
-            const int rem = e - s * per_step;
+            const int q = e / per_row;
+            const int rem = e - q * per_row;
             const int hs = rem / KK;
-            const int q = rem - hs * KK;
-            const int i = q / KP, j = q - (q / KP) * KP;
-            const int64_t t = t_c + s;
-            const int64_t gh = (int64_t)grp * p.HPW + hs;
+            const int o = rem - hs * KK;
+            const int i = o / KP, j = o - (o / KP) * KP;
+            const int64_t t = sm.t(t_c, hs, q);
+            const int64_t gh = sm.head(grp, hs);
             float val = (i == j) ? 1.f : 0.f;
             if (t < p.T && gh < p.heads && i < k && j < k) {
                 const int64_t b = gh / p.n, h = gh - b * p.n;
                 val = ld1(Ag + ((b * p.T + t) * p.n + h) * k * k + i * k + j);
             }
-            s_A[(s * p.HPW + hs) * AS + q] = val;
+            s_A[(q * p.HPW + hs) * AS + o] = val;
         }
     }
 }
@@ -403,15 +425,18 @@ __device__ __forceinline__ void payload_cols(float (&x)[KP][CPL], rsrc_t r, uint
     for (int i = 0; i < KP; ++i) carry_row<CPL>(x[i], r, hb + 4u * (uint32_t)(i * NCP + c0));
 }
 
-// One workgroup = NW waves = HPW heads x one chunk of CH = NW * L steps.  Wave
-// w owns steps [w L, (w + 1) L) of the chunk:
+// One workgroup = NW waves; each wave holds HPW slots = HH heads x SEG
+// segments, and wave w owns rows [w L, (w + 1) L) of every segment, so a chunk
+// is SEG * NW * L steps of HH heads:
 //  1. every wave loads its L steps of B (its columns) into registers, and the
-//     workgroup stages the chunk's A_t blocks in LDS;
+//     workgroup stages the A_t blocks of every slot in LDS;
 //  2. each wave composes its steps' transform [Abar_w | H_w] from [I | 0];
-//  3. an inclusive prefix over the waves, through LDS, in log2(NW) rounds;
+//  3. an inclusive prefix over the chunk's SEG * NW pieces (segment-major,
+//     wave-minor: time order) of each head, through LDS, in log2(SEG * NW)
+//     rounds;
 //  4. wave 0 runs the look-back for the state entering the chunk and
 //     publishes the chunk's inclusive state (the last prefix applied to it);
-//  5. each wave applies the prefix of the waves before it to that state,
+//  5. each piece applies the prefix of the pieces before it to that state,
 //     rescans its steps from registers and stores Abar_t, Bbar_t.
 // The chunk is read from memory once.
 // H0: the scan starts from X_0 = [I | H0] (Bbar then holds the states from
@@ -421,15 +446,17 @@ __global__ __launch_bounds__(512) void affine_fwd_kernel(FwdArgs p) {
     constexpr int L = AffL<KP, CPL>::L;
     extern __shared__ __align__(16) float s_dyn[];
     __shared__ uint32_t s_ticket;
-    const int NW = p.NW, HPW = p.HPW, NCP = p.NCP;
+    const int NW = p.NW, HPW = p.HPW, NCP = p.NCP, HH = p.HH;
+    const int SEG = HPW / HH;
     constexpr int AS = pad_bank(KP * KP);  // LDS stride of an A_t block
-    const int CH = NW * L;
+    const int CHW = NW * L;                 // steps per segment
+    const int CH = SEG * CHW;               // steps per chunk
+    const SlotMap sm{HH, CHW};
     const int blk = KP * NCP;               // floats of one head's [KP][NCP] payload block
     const int bs = pad_bank(blk);           // LDS stride of such a block
-    float *s_A = s_dyn;                     // [CH][HPW][AS]
-    float *s_X = s_A + (CH * HPW * AS + 3) / 4 * 4;  // [NW][HPW][bs]: wave transforms (16-byte aligned)
-    float *s_C = s_X + NW * HPW * bs;       // [HPW][bs]: chunk transform
-    float *s_S = s_C + HPW * bs;            // [HPW][bs]: state entering the chunk
+    float *s_A = s_dyn;                     // [CHW][HPW][AS]
+    float *s_X = s_A + (CHW * HPW * AS + 3) / 4 * 4;  // [NW][HPW][bs]: wave transforms (16-byte aligned)
+    float *s_S = s_X + NW * HPW * bs;       // [HH][bs]: state entering the chunk, per head
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -441,12 +468,14 @@ __global__ __launch_bounds__(512) void affine_fwd_kernel(FwdArgs p) {
     const int grp = ticket - chunk * p.n_groups;
     const int hs = lane / p.G;
     const int g = lane - hs * p.G;
-    const bool slot_lane = hs < HPW;  // lane maps to a head slot
+    const bool slot_lane = hs < HPW;  // lane maps to a slot
     const int hsc = slot_lane ? hs : 0;
-    const int64_t gh = (int64_t)grp * HPW + hs;
+    const int sg = hsc / HH;          // the slot's segment
+    const int hh = hsc - sg * HH;     // and head within the group
+    const int64_t gh = sm.head(grp, hsc);
     const bool active = slot_lane && gh < p.heads;
     const int64_t bidx = active ? gh / p.n : 0;
-    const int64_t hh = active ? gh % p.n : 0;
+    const int64_t hn = active ? gh % p.n : 0;
     // With vector IO k equals KP: a compile-time k removes every bounds test
     // (and the branches around the loads) from the block products.
     const int k = VIO ? KP : p.k;
@@ -465,14 +494,14 @@ __global__ __launch_bounds__(512) void affine_fwd_kernel(FwdArgs p) {
     for (int cc = 0; cc < CPL; ++cc) is_h[cc] = cl.kind[cc] == C_H;
 
     const int64_t t_c = (int64_t)chunk * CH;  // first step of the chunk
-    const int64_t t_w = t_c + (int64_t)wave * L;
-    const int64_t m0 = bidx * p.T * p.n + hh;  // matrix index of (b, t = 0, h); + t n per step
+    const int64_t t_w = sm.t(t_c, hsc, wave * L);  // first step of the lane's rows
+    const int64_t m0 = bidx * p.T * p.n + hn;  // matrix index of (b, t = 0, h); + t n per step
 
-    // 1. B of the wave's steps (registers) and the chunk's A (LDS).
+    // 1. B of the wave's steps (registers) and the A_t blocks (LDS).
     float rb[L][KP][CPL];
 #pragma unroll
     for (int r = 0; r < L; ++r) load_b<TS, KP, CPL, VIO>(rb[r], p, cl, m0 + (t_w + r) * p.n, active && t_w + r < p.T);
-    stage_a<TS, KP, VIO>(s_A, p, grp, t_c, CH);
+    stage_a<TS, KP, VIO>(s_A, p, sm, grp, t_c);
     lds_barrier();
 
     // 2. The wave's transform from [I | 0].
@@ -483,39 +512,42 @@ __global__ __launch_bounds__(512) void affine_fwd_kernel(FwdArgs p) {
         for (int cc = 0; cc < CPL; ++cc) x[i][cc] = (cl.kind[cc] == C_ABAR && i == cl.col[cc]) ? 1.f : 0.f;
 #pragma unroll
     for (int r = 0; r < L; ++r) step_lds<KP, CPL>(x, s_A + ((wave * L + r) * HPW + hsc) * AS, rb[r]);
-    // 3. Inclusive prefix over the waves (Hillis-Steele): after the round
-    //    with offset o, wave w holds T_w o ... o T_{max(0, w - 2o + 1)}.  Each
-    //    round applies the block of wave w - o to the wave's own transform:
+    // 3. Inclusive prefix (Hillis-Steele) over the chunk's SEG * NW pieces in
+    //    time order, e = segment * NW + wave; piece e of a head is wave e % NW
+    //    in slot (e / NW) * HH + head.  After the round with offset o, piece e
+    //    holds T_e o ... o T_{max(0, e - 2o + 1)}.  Each round applies the
+    //    block of piece e - o to the piece's own transform:
     //    X <- X o P  means  [A_X A_P | A_X H_P + H_X], i.e. the lane's columns
     //    of P under A_X, plus H_X on the H columns.
+    const int E = SEG * NW;
+    const int e = sg * NW + wave;
+    auto piece = [&](int q) { return s_X + ((q % NW) * HPW + (q / NW) * HH + hh) * bs; };
     if (slot_lane) put_cols<KP, CPL>(s_X + (wave * HPW + hs) * bs, NCP, c0, x);
     lds_barrier();
-    for (int o = 1; o < NW; o *= 2) {
-        if (wave >= o) {
-            float P[KP][CPL];
-            get_cols<KP, CPL>(P, s_X + ((wave - o) * HPW + hsc) * bs, NCP, c0);
-            block_apply<KP, CPL>(P, s_X + (wave * HPW + hsc) * bs, NCP, k, c0, is_h);
+    for (int o = 1; o < E; o *= 2) {
+        const bool upd = e >= o;
+        float P[KP][CPL];
+        get_cols<KP, CPL>(P, piece(upd ? e - o : e), NCP, c0);
+        block_apply<KP, CPL>(P, s_X + (wave * HPW + hsc) * bs, NCP, k, c0, is_h);
 #pragma unroll
-            for (int i = 0; i < KP; ++i)
+        for (int i = 0; i < KP; ++i)
 #pragma unroll
-                for (int cc = 0; cc < CPL; ++cc) x[i][cc] = P[i][cc];
-        }
+            for (int cc = 0; cc < CPL; ++cc) x[i][cc] = upd ? P[i][cc] : x[i][cc];
         lds_barrier();  // every read of this round is done
-        if (wave >= o && slot_lane) put_cols<KP, CPL>(s_X + (wave * HPW + hs) * bs, NCP, c0, x);
+        if (upd && slot_lane) put_cols<KP, CPL>(s_X + (wave * HPW + hs) * bs, NCP, c0, x);
         lds_barrier();
     }
 
-    // 4. Look-back and publication (wave 0).  The chunk transform is the
-    //    last wave's prefix.
+    // 4. Look-back and publication (wave 0).  The chunk transform of head hh
+    //    is the prefix through its last piece.
     if (wave == 0) {
-        {
-            float C[KP][CPL];
-            get_cols<KP, CPL>(C, s_X + ((NW - 1) * HPW + hsc) * bs, NCP, c0);
-            if (slot_lane) put_cols<KP, CPL>(s_C + hs * bs, NCP, c0, C);
-        }
+        const float *s_C = piece(E - 1);
+        // Every segment's lanes of a head hold the same look-back values (same
+        // loads, same operations) and store them to the same addresses.
+        const bool lb_lane = slot_lane;
 
-        const int64_t slot_sz = (int64_t)HPW * blk;
-        const int64_t hoff = (int64_t)hsc * blk;
+        const int64_t slot_sz = (int64_t)HH * blk;
+        const int64_t hoff = (int64_t)hh * blk;
         const int64_t slot = (int64_t)grp * p.n_chunks + chunk;
         float S[KP][CPL];
 #pragma unroll
@@ -532,12 +564,10 @@ __global__ __launch_bounds__(512) void affine_fwd_kernel(FwdArgs p) {
                             S[i][cc] = ld1(static_cast<const TS *>(p.H0) + gh * k * p.v + i * p.v + cl.col[cc]);
             }
         }
-        // the wave's own s_C writes are complete before other lanes read them
-        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
         if (chunk > 0) {
-            if (slot_lane) {
+            if (lb_lane) {
                 float C[KP][CPL];
-                get_cols<KP, CPL>(C, s_C + hs * bs, NCP, c0);
+                get_cols<KP, CPL>(C, s_C, NCP, c0);
                 payload_store<KP, CPL>(p.ws.agg + slot * slot_sz + hoff, NCP, c0, C);
             }
             const int dist = wait_ready(p.ws.flags, slot - 1, -1, chunk, p.ws.hdr + 1, p.ws.flags + slot, FLAG_AGG);
@@ -551,18 +581,18 @@ __global__ __launch_bounds__(512) void affine_fwd_kernel(FwdArgs p) {
                 payload_apply<KP, CPL>(S, make_rows(p.ws.agg + ((int64_t)grp * p.n_chunks + jj) * slot_sz, slot_bytes),
                                        hb, NCP, k, c0, is_h);
         }
-        if (slot_lane) put_cols<KP, CPL>(s_S + hs * bs, NCP, c0, S);
-        block_apply<KP, CPL>(S, s_C + hsc * bs, NCP, k, c0, is_h);  // S becomes the inclusive state
-        if (slot_lane) payload_store<KP, CPL>(p.ws.inc + slot * slot_sz + hoff, NCP, c0, S);
+        if (lb_lane) put_cols<KP, CPL>(s_S + hh * bs, NCP, c0, S);
+        block_apply<KP, CPL>(S, s_C, NCP, k, c0, is_h);  // S becomes the inclusive state
+        if (lb_lane) payload_store<KP, CPL>(p.ws.inc + slot * slot_sz + hoff, NCP, c0, S);
         publish_flag(p.ws.flags + slot, FLAG_INC);
     }
     lds_barrier();
 
-    // 5. State entering this wave (the chunk's, then the prefix of the waves
+    // 5. State entering this piece (the chunk's, then the prefix of the pieces
     //    before it), rescan, store.
     float S[KP][CPL];
-    get_cols<KP, CPL>(S, s_S + hsc * bs, NCP, c0);
-    if (wave > 0) block_apply<KP, CPL>(S, s_X + ((wave - 1) * HPW + hsc) * bs, NCP, k, c0, is_h);
+    get_cols<KP, CPL>(S, s_S + hh * bs, NCP, c0);
+    if (e > 0) block_apply<KP, CPL>(S, piece(e - 1), NCP, k, c0, is_h);
 #pragma unroll
     for (int r = 0; r < L; ++r) {
         step_lds<KP, CPL>(S, s_A + ((wave * L + r) * HPW + hsc) * AS, rb[r]);
@@ -999,6 +1029,7 @@ struct AffPlan {
     bool h0;    // launch the initial-state (H0) kernels
     bool bf16;  // bf16 storage (fp32 otherwise)
     int G, HPW, NCP, n_groups, n_chunks, LC, NW;
+    int HH, SEG;  // heads per workgroup, time segments per chunk (HH * SEG = HPW)
     size_t n_slots, payload, lds_bytes;
     bool ok;  // the work-item count fits the int32 ticket space, the LDS the workgroup
 };
@@ -1017,14 +1048,21 @@ constexpr size_t BWD_LDS_MAX = MISCAN_AFF_BWD_LDS;
 // with element-wise IO) take up to the device's 160 KiB per workgroup.
 constexpr size_t LDS_DEVICE_MAX = 163840;
 
+// Time segments per forward chunk: the largest divisor of HPW up to this
+// bound.
+#ifndef MISCAN_AFF_SEGMAX
+#define MISCAN_AFF_SEGMAX 64
+#endif
+
 inline int aff_L(int KP, int CPL, bool bwd) {
     const int raw = (bwd ? MISCAN_AFF_BWD_BREGS : MISCAN_AFF_BREGS) * (KP >= 8 ? 2 : 1) / (KP * CPL);
     return raw < 1 ? 1 : raw > 16 ? 16 : raw;
 }
 
 // Tiling: G lanes x CPL columns per head (k + v columns forward, 2k + v
-// backward), HPW heads per wave, L steps per wave (AffL), NW waves per
-// workgroup (as many as the LDS budget allows), chunks of NW * L steps.
+// backward), HPW slots per wave = HH heads x SEG time segments, L steps per
+// wave and segment (AffL), NW waves per workgroup (as many as the LDS budget
+// allows), chunks of SEG * NW * L steps.
 inline AffPlan make_plan(int64_t B, int64_t T, int64_t n, int k, int v, bool bwd, int CPL, bool VIO) {
     AffPlan pl;
     pl.KP = next_pow2_16(k);
@@ -1036,10 +1074,16 @@ inline AffPlan make_plan(int64_t B, int64_t T, int64_t n, int k, int v, bool bwd
     pl.G = (ncols + CPL - 1) / CPL;
     if (pl.G > 64) {  // a head must fit one wave: this tiling is not usable
         pl.HPW = 0; pl.NCP = 0; pl.n_groups = 0; pl.n_chunks = 0; pl.LC = 0; pl.NW = 0;
+        pl.HH = 0; pl.SEG = 0;
         pl.n_slots = 0; pl.payload = 0; pl.lds_bytes = 0; pl.ok = false;
         return pl;
     }
     pl.HPW = 64 / pl.G;
+    pl.SEG = 1;  // the backward holds HPW heads per wave (one segment)
+    if (!bwd)
+        for (int sgc = 1; sgc <= pl.HPW && sgc <= MISCAN_AFF_SEGMAX; ++sgc)
+            if (pl.HPW % sgc == 0) pl.SEG = sgc;
+    pl.HH = pl.HPW / pl.SEG;
     pl.NCP = (int)round_up((size_t)pl.G * CPL, 4);
     const int L = aff_L(pl.KP, CPL, bwd);
     const size_t a_ld = (size_t)pad_bank(pl.KP * pl.KP);  // LDS strides (see pad_bank)
@@ -1049,30 +1093,31 @@ inline AffPlan make_plan(int64_t B, int64_t T, int64_t n, int k, int v, bool bwd
     const size_t limit = bwd ? BWD_LDS_MAX : FWD_LDS_MAX;
     auto lds_floats = [&](int nw) {
         const size_t common = round_up((size_t)nw * L * pl.HPW * a_ld, 4) + (size_t)nw * pl.HPW * x_ld;
-        return bwd ? common + (size_t)pl.HPW * x_ld + (size_t)nw * part : common + 2 * (size_t)pl.HPW * x_ld;
+        return bwd ? common + (size_t)pl.HH * x_ld + (size_t)nw * part : common + (size_t)pl.HH * x_ld;
     };
     pl.NW = 1;
-    for (int nw = bwd ? MISCAN_AFF_BWD_NWMAX : MISCAN_AFF_NWMAX; nw >= 1; nw /= 2)
+    const int nwmax = bwd ? MISCAN_AFF_BWD_NWMAX : pl.KP >= 8 ? MISCAN_AFF_NWMAX_K8 : MISCAN_AFF_NWMAX;
+    for (int nw = nwmax; nw >= 1; nw /= 2)
         if (lds_floats(nw) * sizeof(float) <= limit) { pl.NW = nw; break; }
-    pl.LC = pl.NW * L;
+    pl.LC = pl.SEG * pl.NW * L;
     pl.lds_bytes = lds_floats(pl.NW) * sizeof(float);
     const int64_t heads = B * n;
-    const int64_t ng = (heads + pl.HPW - 1) / pl.HPW;
+    const int64_t ng = (heads + pl.HH - 1) / pl.HH;
     const int64_t nc = (T + pl.LC - 1) / pl.LC;
     pl.ok = ng <= INT32_MAX && nc <= INT32_MAX && ng * nc <= (int64_t)INT32_MAX &&
             pl.lds_bytes <= LDS_DEVICE_MAX;
     pl.n_groups = (int)ng;
     pl.n_chunks = (int)nc;
     pl.n_slots = pl.ok ? (size_t)ng * (size_t)nc : 0;
-    pl.payload = (size_t)pl.HPW * pl.KP * pl.NCP;
+    pl.payload = (size_t)pl.HH * pl.KP * pl.NCP;
     return pl;
 }
 
 // Column tiling: of the vector tilings the alignment allows (k a power of two
 // so that rows load as vectors, k and v multiples of CPL so that column groups
-// never straddle tensors, 16-byte aligned pointers), the one with the longest
-// chunk (fewer look-back steps and payload bytes per step of data), four
-// columns per lane on a tie; otherwise four columns with element accesses.
+// never straddle tensors, 16-byte aligned pointers), the one whose waves cover
+// the most steps (fewer look-back steps and payload bytes per step of data),
+// four columns per lane on a tie; otherwise four columns with element accesses.
 inline AffPlan choose_plan(int64_t B, int64_t T, int64_t n, int k, int v, bool bwd, bool ptrs16) {
     const bool kpow2 = next_pow2_16(k) == k;
     AffPlan best;
@@ -1082,7 +1127,9 @@ inline AffPlan choose_plan(int64_t B, int64_t T, int64_t n, int k, int v, bool b
         if (!(ptrs16 && kpow2 && k % cpl == 0 && v % cpl == 0)) continue;
         AffPlan pl = make_plan(B, T, n, k, v, bwd, cpl, true);
         if (!pl.ok) continue;
-        if (!have || pl.LC > best.LC) { best = pl; have = true; }
+        // compare the time each wave covers (NW * L): segments lengthen chunks
+        // of either width alike, while the wider tiling costs registers
+        if (!have || pl.LC / pl.SEG > best.LC / best.SEG) { best = pl; have = true; }
     }
     if (!have) best = make_plan(B, T, n, k, v, bwd, 4, false);
     return best;
@@ -1100,7 +1147,8 @@ inline mi_status allow_lds(K kernel, size_t bytes) {
 
 template <typename TS, int KP, int CPL, bool VIO, bool H0>
 mi_status fwd_launch_h(const AffPlan &pl, FwdArgs &a, hipStream_t s) {
-    if (pl.LC != pl.NW * AffL<KP, CPL>::L) return MI_ERR_UNSUPPORTED;  // host and kernel tilings agree
+    if (pl.LC != pl.SEG * pl.NW * AffL<KP, CPL>::L || pl.HH * pl.SEG != pl.HPW)  // host and kernel tilings agree
+        return MI_ERR_UNSUPPORTED;
     if (allow_lds(&affine_fwd_kernel<TS, KP, CPL, VIO, H0>, pl.lds_bytes) != MI_OK) return MI_ERR_LAUNCH;
     hipLaunchKernelGGL((affine_fwd_kernel<TS, KP, CPL, VIO, H0>), dim3((unsigned)pl.n_slots), dim3(64 * pl.NW),
                        pl.lds_bytes, s, a);
@@ -1116,7 +1164,7 @@ mi_status fwd_launch(const AffPlan &pl, FwdArgs &a, hipStream_t s) {
 }
 template <typename TS, int KP, int CPL, bool VIO, bool H0>
 mi_status bwd_launch_h(const AffPlan &pl, BwdArgs &a, hipStream_t s) {
-    if (pl.LC != pl.NW * AffL<KP, CPL, true>::L) return MI_ERR_UNSUPPORTED;
+    if (pl.LC != pl.SEG * pl.NW * AffL<KP, CPL, true>::L || pl.HH * pl.SEG != pl.HPW) return MI_ERR_UNSUPPORTED;
     if (allow_lds(&affine_bwd_kernel<TS, KP, CPL, VIO, H0>, pl.lds_bytes) != MI_OK) return MI_ERR_LAUNCH;
     hipLaunchKernelGGL((affine_bwd_kernel<TS, KP, CPL, VIO, H0>), dim3((unsigned)pl.n_slots), dim3(64 * pl.NW),
                        pl.lds_bytes, s, a);
@@ -1186,7 +1234,7 @@ mi_status launch_affine_fwd(const void *A, const void *Bm, void *Abar, void *Bba
     a.A = A; a.Bm = Bm; a.Abar = Abar; a.Bbar = Bbar; a.H0 = H0;
     a.T = T; a.heads = B * n; a.n = (int)n; a.k = (int)k; a.v = (int)v;
     a.G = pl.G; a.HPW = pl.HPW; a.NCP = pl.NCP; a.n_groups = pl.n_groups;
-    a.n_chunks = pl.n_chunks; a.NW = pl.NW;
+    a.n_chunks = pl.n_chunks; a.NW = pl.NW; a.HH = pl.HH;
     a.ws = ws_ptrs(ws, lay);
     mi_status st = clear_workspace(a.ws, pl.n_slots, s);
     if (st != MI_OK) return st;
@@ -1211,7 +1259,7 @@ mi_status launch_affine_bwd(const void *A, const void *Abar, const void *Bbar,
     a.A = A; a.Abar = Abar; a.Bbar = Bbar; a.gAbar = gAbar; a.gBbar = gBbar; a.dA = dA; a.dB = dB;
     a.T = T; a.heads = B * n; a.n = (int)n; a.k = (int)k; a.v = (int)v;
     a.G = pl.G; a.HPW = pl.HPW; a.NCP = pl.NCP; a.n_groups = pl.n_groups;
-    a.n_chunks = pl.n_chunks; a.NW = pl.NW;
+    a.n_chunks = pl.n_chunks; a.NW = pl.NW; a.HH = pl.HH;
     a.ws = ws_ptrs(ws, lay);
     mi_status st = clear_workspace(a.ws, pl.n_slots, s);
     if (st != MI_OK) return st;
