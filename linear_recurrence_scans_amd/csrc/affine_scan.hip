@@ -134,6 +134,7 @@ struct FwdArgs {
     int n, k, v;
     int G, HPW, NCP, n_groups, n_chunks, NW;
     int HH;  // heads per workgroup; SEG = HPW / HH time segments per chunk
+    int DB;  // payload blocks the look-back stages in LDS per round trip
     WsPtrs ws;
 };
 
@@ -146,6 +147,7 @@ struct BwdArgs {
     int n, k, v;
     int G, HPW, NCP, n_groups, n_chunks, NW;
     int HH;  // heads per workgroup; SEG = HPW / HH time segments per chunk
+    int DB;  // payload blocks the look-back stages in LDS per round trip
     WsPtrs ws;
 };
 
@@ -392,37 +394,39 @@ __device__ __forceinline__ void block_apply(float (&S)[KP][CPL], const float *bl
     }, k, is_h);
 }
 
-// N consecutive payload floats at byte offset voff, coherent vector loads.
-template <int N>
-__device__ __forceinline__ void carry_row(float *dst, rsrc_t r, uint32_t voff) {
-    if constexpr (N % 4 == 0) {
-#pragma unroll
-        for (int i = 0; i < N; i += 4) carry_load_vec<4>(dst + i, r, voff + 4u * i);
-    } else if constexpr (N % 2 == 0) {
-#pragma unroll
-        for (int i = 0; i < N; i += 2) carry_load_vec<2>(dst + i, r, voff + 4u * i);
-    } else {
-#pragma unroll
-        for (int i = 0; i < N; ++i) carry_load_vec<1>(dst + i, r, voff + 4u * i);
+// Look-back payloads into LDS, cooperatively: one round trip for a batch of
+// up to DB published blocks instead of one per block.  Fold index q = 0 is the
+// inclusive state of slot j0 (the `inc` array), q >= 1 the transform of slot
+// j0 + dir * q (the `agg` array); the batch holds indices b0 .. b0 + nb - 1,
+// index q at s_stage + (q - b0) * slot_sz.  Slot j of the workgroup's group
+// lives at (row0 + j) * slot_sz of either array.  The transforms of a batch
+// are consecutive slots, so each array is read through one descriptor.
+__device__ __forceinline__ void stage_payloads(float *s_stage, const WsPtrs &ws, int64_t row0, int j0, int dir,
+                                               int b0, int nb, int slot_sz) {
+    const int tid = threadIdx.x, nt = blockDim.x;
+    int first = b0;
+    if (b0 == 0) {
+        const rsrc_t r = make_rows(ws.inc + (row0 + j0) * slot_sz, (int64_t)slot_sz * 4);
+        for (int e = tid * 4; e < slot_sz; e += nt * 4) {
+            float q[4];
+            carry_load_vec<4>(q, r, 4u * (uint32_t)e);
+            *reinterpret_cast<f32x4 *>(s_stage + e) = f32x4{q[0], q[1], q[2], q[3]};
+        }
+        first = 1;
     }
-}
-
-// The block of a published payload: slot descriptor r, the head's block at
-// byte offset hb.
-template <int KP, int CPL>
-__device__ __forceinline__ void payload_apply(float (&S)[KP][CPL], rsrc_t r, uint32_t hb, int NCP, int k, int c0,
-                                              const bool (&is_h)[CPL]) {
-    apply_rows<KP, CPL>(S, [&](int i, float (&m)[KP], float (&h)[CPL]) {
-        carry_row<KP>(m, r, hb + 4u * (uint32_t)(i * NCP));
-        carry_row<CPL>(h, r, hb + 4u * (uint32_t)(i * NCP + c0));
-    }, k, is_h);
-}
-
-// The lane's columns of a published payload block.
-template <int KP, int CPL>
-__device__ __forceinline__ void payload_cols(float (&x)[KP][CPL], rsrc_t r, uint32_t hb, int NCP, int c0) {
-#pragma unroll
-    for (int i = 0; i < KP; ++i) carry_row<CPL>(x[i], r, hb + 4u * (uint32_t)(i * NCP + c0));
+    const int last = b0 + nb - 1;
+    const int na = last - first + 1;  // transforms in this batch
+    if (na > 0) {
+        const int lo = dir > 0 ? j0 + first : j0 - last;  // lowest slot of the batch
+        const rsrc_t r = make_rows(ws.agg + (row0 + lo) * slot_sz, (int64_t)na * slot_sz * 4);
+        for (int e = tid * 4; e < na * slot_sz; e += nt * 4) {
+            const int a = e / slot_sz, off = e - a * slot_sz;  // slot lo + a
+            const int q = dir > 0 ? first + a : last - a;      // its fold index
+            float v[4];
+            carry_load_vec<4>(v, r, 4u * (uint32_t)e);
+            *reinterpret_cast<f32x4 *>(s_stage + (q - b0) * slot_sz + off) = f32x4{v[0], v[1], v[2], v[3]};
+        }
+    }
 }
 
 // One workgroup = NW waves; each wave holds HPW slots = HH heads x SEG
@@ -457,6 +461,8 @@ __global__ __launch_bounds__(512) void affine_fwd_kernel(FwdArgs p) {
     float *s_A = s_dyn;                     // [CHW][HPW][AS]
     float *s_X = s_A + (CHW * HPW * AS + 3) / 4 * 4;  // [NW][HPW][bs]: wave transforms (16-byte aligned)
     float *s_S = s_X + NW * HPW * bs;       // [HH][bs]: state entering the chunk, per head
+    float *s_stage = s_S + HH * bs;         // [DB][HH * blk]: predecessor payloads
+    __shared__ int s_dist;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -538,59 +544,68 @@ __global__ __launch_bounds__(512) void affine_fwd_kernel(FwdArgs p) {
         lds_barrier();
     }
 
-    // 4. Look-back and publication (wave 0).  The chunk transform of head hh
-    //    is the prefix through its last piece.
-    if (wave == 0) {
-        const float *s_C = piece(E - 1);
-        // Every segment's lanes of a head hold the same look-back values (same
-        // loads, same operations) and store them to the same addresses.
-        const bool lb_lane = slot_lane;
-
-        const int64_t slot_sz = (int64_t)HH * blk;
-        const int64_t hoff = (int64_t)hh * blk;
-        const int64_t slot = (int64_t)grp * p.n_chunks + chunk;
-        float S[KP][CPL];
+    // 4. Look-back and publication.  Wave 0 finds how far back the nearest
+    //    inclusive state is; the workgroup stages that state and the
+    //    transforms after it in LDS, a batch per round trip; wave 0 folds them
+    //    and publishes.  The chunk transform of head hh is the prefix through
+    //    its last piece.
+    const float *s_C = piece(E - 1);
+    const int slot_sz = HH * blk;
+    const int hoff = hh * blk;
+    const int64_t slot = (int64_t)grp * p.n_chunks + chunk;
+    float S[KP][CPL];
 #pragma unroll
-        for (int i = 0; i < KP; ++i)
+    for (int i = 0; i < KP; ++i)
 #pragma unroll
-            for (int cc = 0; cc < CPL; ++cc) S[i][cc] = (cl.kind[cc] == C_ABAR && i == cl.col[cc]) ? 1.f : 0.f;
-        if constexpr (H0) {
-            if (chunk == 0 && p.H0 != nullptr && active) {  // H columns of the state: H0
+        for (int cc = 0; cc < CPL; ++cc) S[i][cc] = (cl.kind[cc] == C_ABAR && i == cl.col[cc]) ? 1.f : 0.f;
+    if constexpr (H0) {
+        if (chunk == 0 && p.H0 != nullptr && active) {  // H columns of the state: H0
 #pragma unroll
-                for (int i = 0; i < KP; ++i)
+            for (int i = 0; i < KP; ++i)
 #pragma unroll
-                    for (int cc = 0; cc < CPL; ++cc)
-                        if (i < k && cl.kind[cc] == C_H)
-                            S[i][cc] = ld1(static_cast<const TS *>(p.H0) + gh * k * p.v + i * p.v + cl.col[cc]);
-            }
+                for (int cc = 0; cc < CPL; ++cc)
+                    if (i < k && cl.kind[cc] == C_H)
+                        S[i][cc] = ld1(static_cast<const TS *>(p.H0) + gh * k * p.v + i * p.v + cl.col[cc]);
         }
-        if (chunk > 0) {
-            if (lb_lane) {
+    }
+    // Every segment's lanes of a head hold the same look-back values (same
+    // loads, same operations) and store them to the same addresses.
+    if (chunk > 0) {
+        if (wave == 0) {
+            if (slot_lane) {
                 float C[KP][CPL];
                 get_cols<KP, CPL>(C, s_C, NCP, c0);
                 payload_store<KP, CPL>(p.ws.agg + slot * slot_sz + hoff, NCP, c0, C);
             }
             const int dist = wait_ready(p.ws.flags, slot - 1, -1, chunk, p.ws.hdr + 1, p.ws.flags + slot, FLAG_AGG);
-            const int j0 = chunk - 1 - dist;
-            const uint32_t hb = 4u * (uint32_t)hoff;
-            const int64_t slot_bytes = 4 * slot_sz;
-            // slot j0 holds an inclusive state; chunks j0+1 .. chunk-1 hold transforms
-            payload_cols<KP, CPL>(S, make_rows(p.ws.inc + ((int64_t)grp * p.n_chunks + j0) * slot_sz, slot_bytes), hb,
-                                  NCP, c0);
-            for (int jj = j0 + 1; jj < chunk; ++jj)
-                payload_apply<KP, CPL>(S, make_rows(p.ws.agg + ((int64_t)grp * p.n_chunks + jj) * slot_sz, slot_bytes),
-                                       hb, NCP, k, c0, is_h);
+            if (lane == 0) s_dist = dist;
         }
-        if (lb_lane) put_cols<KP, CPL>(s_S + hh * bs, NCP, c0, S);
+        lds_barrier();
+        // slot j0 holds an inclusive state; chunks j0+1 .. chunk-1 hold transforms
+        const int nfold = (int)__builtin_amdgcn_readfirstlane(s_dist) + 1;
+        const int j0 = chunk - nfold;
+        for (int b0 = 0; b0 < nfold; b0 += p.DB) {
+            const int nb = nfold - b0 < p.DB ? nfold - b0 : p.DB;
+            stage_payloads(s_stage, p.ws, (int64_t)grp * p.n_chunks, j0, +1, b0, nb, slot_sz);
+            lds_barrier();
+            if (wave == 0) {
+                if (b0 == 0) get_cols<KP, CPL>(S, s_stage + hoff, NCP, c0);
+                for (int q = b0 == 0 ? 1 : b0; q < b0 + nb; ++q)
+                    block_apply<KP, CPL>(S, s_stage + (q - b0) * slot_sz + hoff, NCP, k, c0, is_h);
+            }
+            if (b0 + p.DB < nfold) lds_barrier();  // the next batch overwrites the stage
+        }
+    }
+    if (wave == 0) {
+        if (slot_lane) put_cols<KP, CPL>(s_S + hh * bs, NCP, c0, S);
         block_apply<KP, CPL>(S, s_C, NCP, k, c0, is_h);  // S becomes the inclusive state
-        if (lb_lane) payload_store<KP, CPL>(p.ws.inc + slot * slot_sz + hoff, NCP, c0, S);
+        if (slot_lane) payload_store<KP, CPL>(p.ws.inc + slot * slot_sz + hoff, NCP, c0, S);
         publish_flag(p.ws.flags + slot, FLAG_INC);
     }
     lds_barrier();
 
     // 5. State entering this piece (the chunk's, then the prefix of the pieces
     //    before it), rescan, store.
-    float S[KP][CPL];
     get_cols<KP, CPL>(S, s_S + hh * bs, NCP, c0);
     if (e > 0) block_apply<KP, CPL>(S, piece(e - 1), NCP, k, c0, is_h);
 #pragma unroll
@@ -791,7 +806,8 @@ __global__ __launch_bounds__(512) void affine_bwd_kernel(BwdArgs p) {
     float *s_A = s_dyn;                                 // [CH][HPW][AS]: A_{t+1}^T
     float *s_X = s_A + (CH * HPW * AS + 3) / 4 * 4;     // [NW][HPW][bs]: wave transforms / suffixes
     float *s_S = s_X + NW * HPW * bs;                   // [HPW][bs]: Y entering the chunk from later
-    float *s_part = s_S + HPW * bs;                     // [NW][pw]
+    float *s_part = s_S + HPW * bs;                     // [NW][pw]; first the look-back's payload stage
+    __shared__ int s_dist;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -870,19 +886,22 @@ __global__ __launch_bounds__(512) void affine_bwd_kernel(BwdArgs p) {
         lds_barrier();
     }
 
-    // 4. Look-back over later chunks (wave 0): Y entering the chunk from later
-    //    time (zero after the last chunk), then Y at the chunk's first step.
-    if (wave == 0) {
-        const int64_t slot_sz = (int64_t)HPW * blk;
-        const int64_t hoff = (int64_t)hsc * blk;
-        const int64_t slot = (int64_t)grp * p.n_chunks + chunk;
-        const int last = p.n_chunks - 1;
-        float S[KP][CPL];
+    // 4. Look-back over later chunks: Y entering the chunk from later time
+    //    (zero after the last chunk), then Y at the chunk's first step.  Wave 0
+    //    finds the nearest published state; the workgroup stages it and the
+    //    transforms before it in LDS (in the dA buffer, idle until step 5), a
+    //    batch per round trip; wave 0 folds them and publishes.
+    const int slot_sz = HPW * blk;
+    const int hoff = hsc * blk;
+    const int64_t slot = (int64_t)grp * p.n_chunks + chunk;
+    const int last = p.n_chunks - 1;
+    float S[KP][CPL];
 #pragma unroll
-        for (int i = 0; i < KP; ++i)
+    for (int i = 0; i < KP; ++i)
 #pragma unroll
-            for (int cc = 0; cc < CPL; ++cc) S[i][cc] = 0.f;
-        if (chunk < last) {
+        for (int cc = 0; cc < CPL; ++cc) S[i][cc] = 0.f;
+    if (chunk < last) {
+        if (wave == 0) {
             if (slot_lane) {
                 float Z[KP][CPL];
                 get_cols<KP, CPL>(Z, s_X + hs * bs, NCP, c0);
@@ -890,20 +909,31 @@ __global__ __launch_bounds__(512) void affine_bwd_kernel(BwdArgs p) {
             }
             const int dist = wait_ready(p.ws.flags, slot + 1, +1, last - chunk, p.ws.hdr + 1, p.ws.flags + slot,
                                         FLAG_AGG);
-            const int j0 = chunk + 1 + dist;
-            const uint32_t hb = 4u * (uint32_t)hoff;
-            const int64_t slot_bytes = 4 * slot_sz;
-            // slot j0 holds a state; chunks j0-1 .. chunk+1 hold transforms
-            payload_cols<KP, CPL>(S, make_rows(p.ws.inc + ((int64_t)grp * p.n_chunks + j0) * slot_sz, slot_bytes),
-                                  hb, NCP, c0);
-#pragma unroll
-            for (int i = 0; i < KP; ++i)
-#pragma unroll
-                for (int cc = 0; cc < CPL; ++cc) S[i][cc] = is_y[cc] ? S[i][cc] : 0.f;
-            for (int jj = j0 - 1; jj > chunk; --jj)
-                payload_apply<KP, CPL>(S, make_rows(p.ws.agg + ((int64_t)grp * p.n_chunks + jj) * slot_sz, slot_bytes),
-                                       hb, NCP, k, c0, is_y);
+            if (lane == 0) s_dist = dist;
         }
+        lds_barrier();
+        // slot j0 holds a state; chunks j0-1 .. chunk+1 hold transforms
+        const int nfold = (int)__builtin_amdgcn_readfirstlane(s_dist) + 1;
+        const int j0 = chunk + nfold;
+        for (int b0 = 0; b0 < nfold; b0 += p.DB) {
+            const int nb = nfold - b0 < p.DB ? nfold - b0 : p.DB;
+            stage_payloads(s_part, p.ws, (int64_t)grp * p.n_chunks, j0, -1, b0, nb, slot_sz);
+            lds_barrier();
+            if (wave == 0) {
+                if (b0 == 0) {
+                    get_cols<KP, CPL>(S, s_part + hoff, NCP, c0);
+#pragma unroll
+                    for (int i = 0; i < KP; ++i)
+#pragma unroll
+                        for (int cc = 0; cc < CPL; ++cc) S[i][cc] = is_y[cc] ? S[i][cc] : 0.f;
+                }
+                for (int q = b0 == 0 ? 1 : b0; q < b0 + nb; ++q)
+                    block_apply<KP, CPL>(S, s_part + (q - b0) * slot_sz + hoff, NCP, k, c0, is_y);
+            }
+            if (b0 + p.DB < nfold) lds_barrier();  // the next batch overwrites the stage
+        }
+    }
+    if (wave == 0) {
         if (slot_lane) put_cols<KP, CPL>(s_S + hs * bs, NCP, c0, S);
         block_apply<KP, CPL>(S, s_X + hsc * bs, NCP, k, c0, is_y);  // through the whole chunk
         if (slot_lane) payload_store<KP, CPL>(p.ws.inc + slot * slot_sz + hoff, NCP, c0, S);
@@ -912,7 +942,6 @@ __global__ __launch_bounds__(512) void affine_bwd_kernel(BwdArgs p) {
     lds_barrier();
 
     // 5. Y entering this wave from later time, reverse rescan, outputs.
-    float S[KP][CPL];
     get_cols<KP, CPL>(S, s_S + hsc * bs, NCP, c0);
     if (wave + 1 < NW) block_apply<KP, CPL>(S, s_X + ((wave + 1) * HPW + hsc) * bs, NCP, k, c0, is_y);
     float *part = s_part + wave * pw;
@@ -1030,6 +1059,7 @@ struct AffPlan {
     bool bf16;  // bf16 storage (fp32 otherwise)
     int G, HPW, NCP, n_groups, n_chunks, LC, NW;
     int HH, SEG;  // heads per workgroup, time segments per chunk (HH * SEG = HPW)
+    int DB;       // look-back payload blocks staged per round trip
     size_t n_slots, payload, lds_bytes;
     bool ok;  // the work-item count fits the int32 ticket space, the LDS the workgroup
 };
@@ -1047,6 +1077,16 @@ constexpr size_t BWD_LDS_MAX = MISCAN_AFF_BWD_LDS;
 // Shapes that need more than the budget even with one wave (large padded k
 // with element-wise IO) take up to the device's 160 KiB per workgroup.
 constexpr size_t LDS_DEVICE_MAX = 163840;
+
+// Look-back: payload blocks staged in LDS per round trip, at most this many
+// and (forward) within this many floats of LDS.  The backward stages them in
+// its dA buffer.
+#ifndef MISCAN_AFF_DBMAX
+#define MISCAN_AFF_DBMAX 16
+#endif
+#ifndef MISCAN_AFF_STAGE_FLOATS
+#define MISCAN_AFF_STAGE_FLOATS 4096
+#endif
 
 // Time segments per forward chunk: the largest divisor of HPW up to this
 // bound.
@@ -1074,7 +1114,7 @@ inline AffPlan make_plan(int64_t B, int64_t T, int64_t n, int k, int v, bool bwd
     pl.G = (ncols + CPL - 1) / CPL;
     if (pl.G > 64) {  // a head must fit one wave: this tiling is not usable
         pl.HPW = 0; pl.NCP = 0; pl.n_groups = 0; pl.n_chunks = 0; pl.LC = 0; pl.NW = 0;
-        pl.HH = 0; pl.SEG = 0;
+        pl.HH = 0; pl.SEG = 0; pl.DB = 0;
         pl.n_slots = 0; pl.payload = 0; pl.lds_bytes = 0; pl.ok = false;
         return pl;
     }
@@ -1091,9 +1131,14 @@ inline AffPlan make_plan(int64_t B, int64_t T, int64_t n, int k, int v, bool bwd
     const int rb = pl.KP < MISCAN_AFF_RBMAX ? pl.KP : MISCAN_AFF_RBMAX;  // AffRB
     const size_t part = round_up((size_t)pl.HPW * pl.G * rb * pl.KP, 4);
     const size_t limit = bwd ? BWD_LDS_MAX : FWD_LDS_MAX;
+    const size_t payload = (size_t)pl.HH * pl.KP * pl.NCP;  // floats of one look-back slot
+    const size_t fwd_db = MISCAN_AFF_STAGE_FLOATS / payload;
+    const int fdb = fwd_db < 1 ? 1 : fwd_db > MISCAN_AFF_DBMAX ? MISCAN_AFF_DBMAX : (int)fwd_db;
     auto lds_floats = [&](int nw) {
         const size_t common = round_up((size_t)nw * L * pl.HPW * a_ld, 4) + (size_t)nw * pl.HPW * x_ld;
-        return bwd ? common + (size_t)pl.HH * x_ld + (size_t)nw * part : common + (size_t)pl.HH * x_ld;
+        // the backward's dA buffer also holds at least one staged payload
+        const size_t dab = (size_t)nw * part > payload ? (size_t)nw * part : payload;
+        return bwd ? common + (size_t)pl.HH * x_ld + dab : common + (size_t)pl.HH * x_ld + (size_t)fdb * payload;
     };
     pl.NW = 1;
     const int nwmax = bwd ? MISCAN_AFF_BWD_NWMAX : pl.KP >= 8 ? MISCAN_AFF_NWMAX_K8 : MISCAN_AFF_NWMAX;
@@ -1109,7 +1154,13 @@ inline AffPlan make_plan(int64_t B, int64_t T, int64_t n, int k, int v, bool bwd
     pl.n_groups = (int)ng;
     pl.n_chunks = (int)nc;
     pl.n_slots = pl.ok ? (size_t)ng * (size_t)nc : 0;
-    pl.payload = (size_t)pl.HH * pl.KP * pl.NCP;
+    pl.payload = payload;
+    if (bwd) {
+        const size_t db = ((size_t)pl.NW * part > payload ? (size_t)pl.NW * part : payload) / payload;
+        pl.DB = db > MISCAN_AFF_DBMAX ? MISCAN_AFF_DBMAX : (int)db;
+    } else {
+        pl.DB = fdb;
+    }
     return pl;
 }
 
@@ -1234,7 +1285,7 @@ mi_status launch_affine_fwd(const void *A, const void *Bm, void *Abar, void *Bba
     a.A = A; a.Bm = Bm; a.Abar = Abar; a.Bbar = Bbar; a.H0 = H0;
     a.T = T; a.heads = B * n; a.n = (int)n; a.k = (int)k; a.v = (int)v;
     a.G = pl.G; a.HPW = pl.HPW; a.NCP = pl.NCP; a.n_groups = pl.n_groups;
-    a.n_chunks = pl.n_chunks; a.NW = pl.NW; a.HH = pl.HH;
+    a.n_chunks = pl.n_chunks; a.NW = pl.NW; a.HH = pl.HH; a.DB = pl.DB;
     a.ws = ws_ptrs(ws, lay);
     mi_status st = clear_workspace(a.ws, pl.n_slots, s);
     if (st != MI_OK) return st;
@@ -1259,7 +1310,7 @@ mi_status launch_affine_bwd(const void *A, const void *Abar, const void *Bbar,
     a.A = A; a.Abar = Abar; a.Bbar = Bbar; a.gAbar = gAbar; a.gBbar = gBbar; a.dA = dA; a.dB = dB;
     a.T = T; a.heads = B * n; a.n = (int)n; a.k = (int)k; a.v = (int)v;
     a.G = pl.G; a.HPW = pl.HPW; a.NCP = pl.NCP; a.n_groups = pl.n_groups;
-    a.n_chunks = pl.n_chunks; a.NW = pl.NW; a.HH = pl.HH;
+    a.n_chunks = pl.n_chunks; a.NW = pl.NW; a.HH = pl.HH; a.DB = pl.DB;
     a.ws = ws_ptrs(ws, lay);
     mi_status st = clear_workspace(a.ws, pl.n_slots, s);
     if (st != MI_OK) return st;
