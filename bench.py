@@ -37,12 +37,22 @@ def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
-def source_digest() -> str:
-    """Hash of the kernel sources: stored counter readings are only valid for
-    the exact kernels they were taken on."""
+# The source file of each kernel family; every kernel also includes the shared
+# headers and is launched through api.hip.
+KERNEL_SOURCES = {"linear": "linear_scan.hip", "log": "log_scan.hip", "affine": "affine_scan.hip"}
+SHARED_SOURCES = ("common.hpp", "internal.hpp", "api.hip")
+
+
+def kernel_family(kernel_name: str) -> str:
+    return "log" if "log" in kernel_name else "affine" if kernel_name.startswith("affine") else "linear"
+
+
+def source_digest(family: str) -> str:
+    """Hash of one kernel family's sources: stored counter readings are only
+    valid for the exact kernels they were taken on."""
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "linear_recurrence_scans_amd", "csrc")
-    for f in sorted(os.listdir(csrc)):
+    for f in (KERNEL_SOURCES[family],) + SHARED_SOURCES:
         with open(os.path.join(csrc, f), "rb") as fh:
             h.update(f.encode())
             h.update(fh.read())
@@ -275,9 +285,11 @@ def traffic_key(kernel_name, desc):
     return "%s@%s" % (kernel_name, desc["workload"])
 
 
-def stored_traffic(key, digest):
+def stored_traffic(kernel_name, desc):
     """HBM bytes per launch from committed rocprofv3 counter runs, if they were
-    taken on the current kernel sources."""
+    taken on the current sources of that kernel."""
+    key = traffic_key(kernel_name, desc)
+    digest = source_digest(kernel_family(kernel_name))
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
@@ -392,13 +404,13 @@ def main():
     value = total_bytes / (ms_per_step * 1e-3) / 1e9
     dom = max(per_kernel, key=lambda n: per_kernel[n]["avg_ms"])
     dk = per_kernel[dom]
-    digest = source_digest()
+    digest = source_digest(kernel_family(dom))
     for name in per_kernel:
-        per_kernel[name]["hbm_traffic"] = stored_traffic(traffic_key(name, desc), digest)
+        per_kernel[name]["hbm_traffic"] = stored_traffic(name, desc)
     achieved = dk["GB/s"]
     roofline = {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": stored_traffic(traffic_key(dom, desc), digest),
+                "traffic": stored_traffic(dom, desc),
                 "algorithmic_bytes_per_launch": dk["bytes"], "avg_launch_ms": dk["avg_ms"]}
 
     cpu = None

@@ -507,6 +507,21 @@ def test_affine_bf16_workload_shapes():
     assert max(errs.values()) <= TOL[torch.bfloat16], errs
 
 
+# Forward chunks hold SEG time segments of NW * L steps: (k, v) = (4, 16)
+# gives 12 segments of 16 steps (192-step chunks), (8, 32) 3 segments of 16
+# steps (48-step chunks).  T just below, at and past a chunk or segment
+# boundary, and head counts that leave slots idle, exercise the segment map.
+@pytest.mark.parametrize("case", [(4, 16, 191), (4, 16, 192), (4, 16, 193), (4, 16, 17), (4, 16, 385),
+                                  (8, 32, 47), (8, 32, 48), (8, 32, 49), (8, 32, 97), (8, 32, 16)])
+def test_affine_chunk_boundaries(case):
+    k, v, T = case
+    for (Bn, n) in ((1, 1), (2, 3)):
+        say("affine fwd+bwd B,T,n,k,v =", (Bn, T, n, k, v))
+        x = affine_inputs_diag(Bn, T, n, k, v, seed=T + k, grads=True)
+        errs = run_affine(x, with_bwd=True, metric="abs")
+        assert max(errs.values()) <= TOL[torch.float32], ((Bn, T, n, k, v), errs)
+
+
 def test_affine_rotation_long():
     """Rotations (non-commuting products) over a long sequence."""
     say("affine fwd fp32 rotation B=1 T=5000 n=3 k=4 v=3")
