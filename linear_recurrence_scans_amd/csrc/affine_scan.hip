@@ -621,9 +621,10 @@ __global__ __launch_bounds__(512) void affine_fwd_kernel(FwdArgs p) {
 // Backward
 // ---------------------------------------------------------------------------
 
-// Rows of dA partial sums exchanged through LDS per round.
+// Rows of dA partial sums exchanged through LDS per round.  Four keep the
+// buffer small enough for three backward workgroups per CU at k = 8.
 #ifndef MISCAN_AFF_RBMAX
-#define MISCAN_AFF_RBMAX 8
+#define MISCAN_AFF_RBMAX 4
 #endif
 template <int KP> struct AffRB {
     static constexpr int RB = KP < MISCAN_AFF_RBMAX ? KP : MISCAN_AFF_RBMAX;
@@ -784,13 +785,13 @@ __device__ __forceinline__ void stage_at(float *s_A, const BwdArgs &p, int grp, 
 //     stages the chunk's A_{t+1}^T in LDS;
 //  2. each wave composes its steps' reverse transform from [I | 0 | 0];
 //  3. an inclusive suffix over the waves (reverse Hillis-Steele) through LDS;
-//     meanwhile the X_{t-1} columns for dA arrive;
-//  4. wave 0 runs the look-back over later chunks and publishes the state at
-//     the chunk's first step;
+//  4. the look-back over later chunks; wave 0 publishes the state at the
+//     chunk's first step;
 //  5. each wave applies the suffix of the waves after it to the state from
 //     later time, rescans its steps backwards, stores dB_t = Lam_t and forms
-//     dA_t = Y_t X_{t-1}^T: per-lane partial sums over its columns, added
-//     across the head's lanes through a per-wave LDS buffer (RB rows a round).
+//     dA_t = Y_t X_{t-1}^T from the X_{t-1} columns it loads step by step:
+//     per-lane partial sums over its columns, added across the head's lanes
+//     through a per-wave LDS buffer (RB rows a round).
 // H0: the forward started from [I | H0]: X_{-1} = [I | H0] in dA at the first
 // step, and dH0 = A_1^T Lam_1 is written as well.
 template <typename TS, int KP, int CPL, bool VIO, bool H0 = false>
@@ -869,11 +870,6 @@ __global__ __launch_bounds__(512) void affine_bwd_kernel(BwdArgs p) {
     }
     lds_barrier();
 
-    // X_{t-1} columns for dA; loaded here so that they arrive during steps 3-4.
-    float rx[L][KP][CPL];
-#pragma unroll
-    for (int r = 0; r < L; ++r)
-        load_xprev<TS, KP, CPL, VIO, H0>(rx[r], p, cl, m0 + (t_w + r) * p.n, t_w + r, active && t_w + r < p.T, gh);
 
     // 3. Inclusive suffix: after the round with offset o, wave w holds
     //    T_w o T_{w+1} o ... (T of later waves applied first).
@@ -950,6 +946,10 @@ __global__ __launch_bounds__(512) void affine_bwd_kernel(BwdArgs p) {
 #pragma unroll
     for (int r = L - 1; r >= 0; --r) {
         const int64_t t = t_w + r;
+        // X_{t-1} columns for dA, loaded per step: holding all L steps would
+        // cost L * KP * CPL registers and a workgroup per CU.
+        float rxr[KP][CPL];
+        load_xprev<TS, KP, CPL, VIO, H0>(rxr, p, cl, m0 + (t_w + r) * p.n, t_w + r, active && t_w + r < p.T, gh);
         step_lds<KP, CPL>(S, s_A + ((wave * L + r) * HPW + hsc) * AS, rg[r]);  // S = Y_t
         if (t >= p.T) continue;  // wave-uniform
         const int64_t m = m0 + t * p.n;
@@ -1006,7 +1006,7 @@ __global__ __launch_bounds__(512) void affine_bwd_kernel(BwdArgs p) {
                     for (int cc = 0; cc < CPL; ++cc) {
                         const float y = is_y[cc] ? S[ib + ii][cc] : 0.f;
 #pragma unroll
-                        for (int j = 0; j < KP; ++j) row[j] = fmaf(y, rx[r][j][cc], row[j]);
+                        for (int j = 0; j < KP; ++j) row[j] = fmaf(y, rxr[j][cc], row[j]);
                     }
                     stv<KP, false>(part + ((hs * G + g) * RB + ii) * KP, row);
                 }
