@@ -166,9 +166,12 @@ struct Cols {
 // ---------------------------------------------------------------------------
 
 // Time steps a wave holds in registers: L steps of the lane's B columns,
-// L * KP * CPL floats, kept near 64.
+// L * KP * CPL floats, kept near 64 (see aff_breg_floats).  More steps per
+// wave mean fewer pieces for the chunk's prefix rounds, whose block products
+// are overhead on top of the two per step (compose, rescan); measured on the
+// k = 4 and k = 8 forward, 64 beats 32, 48 and 96.
 #ifndef MISCAN_AFF_BREGS
-#define MISCAN_AFF_BREGS 32
+#define MISCAN_AFF_BREGS 64
 #endif
 #ifndef MISCAN_AFF_NWMAX
 #define MISCAN_AFF_NWMAX 8
@@ -179,17 +182,29 @@ struct Cols {
 #ifndef MISCAN_AFF_NWMAX_K8
 #define MISCAN_AFF_NWMAX_K8 4
 #endif
-// The backward holds two such sets (G_t and X_{t-1} columns).
+// The backward holds the G_t columns of its steps and more state per lane
+// (2k + v columns); it runs best with half the forward's budget.
 #ifndef MISCAN_AFF_BWD_BREGS
-#define MISCAN_AFF_BWD_BREGS MISCAN_AFF_BREGS
+#define MISCAN_AFF_BWD_BREGS 32
 #endif
 #ifndef MISCAN_AFF_BWD_NWMAX
 #define MISCAN_AFF_BWD_NWMAX 4
 #endif
+// Floats of B (forward) or G (backward) columns a lane holds over its steps.
+// The forward doubles its budget only at padded k = 8 with two columns a lane
+// (measured faster, 256 VGPRs, no spill); four columns there, or padded
+// k = 16, would spill with it.  The backward doubles it at padded k >= 8.
+__host__ __device__ constexpr int aff_breg_floats(int KP, int CPL, bool bwd) {
+    return bwd ? MISCAN_AFF_BWD_BREGS * (KP >= 8 ? 2 : 1)
+               : MISCAN_AFF_BREGS * (KP >= 8 && KP * CPL <= 16 ? 2 : 1);
+}
+__host__ __device__ constexpr int aff_steps(int KP, int CPL, bool bwd) {
+    return aff_breg_floats(KP, CPL, bwd) / (KP * CPL) < 1 ? 1
+           : aff_breg_floats(KP, CPL, bwd) / (KP * CPL) > 16 ? 16
+           : aff_breg_floats(KP, CPL, bwd) / (KP * CPL);
+}
 template <int KP, int CPL, bool BWD = false> struct AffL {
-    static constexpr int regs = BWD ? MISCAN_AFF_BWD_BREGS : MISCAN_AFF_BREGS;
-    static constexpr int raw = regs * (KP >= 8 ? 2 : 1) / (KP * CPL);
-    static constexpr int L = raw < 1 ? 1 : raw > 16 ? 16 : raw;
+    static constexpr int L = aff_steps(KP, CPL, BWD);
 };
 
 // The lane's columns of B_t (zero for Abar and padding columns, or when !ok).
@@ -1091,15 +1106,13 @@ constexpr size_t LDS_DEVICE_MAX = 163840;
 #endif
 
 // Time segments per forward chunk: the largest divisor of HPW up to this
-// bound.
+// bound.  Segments shorten the look-back chain but add prefix rounds; with
+// the longer per-wave runs above, two segments at most measured fastest.
 #ifndef MISCAN_AFF_SEGMAX
-#define MISCAN_AFF_SEGMAX 64
+#define MISCAN_AFF_SEGMAX 2
 #endif
 
-inline int aff_L(int KP, int CPL, bool bwd) {
-    const int raw = (bwd ? MISCAN_AFF_BWD_BREGS : MISCAN_AFF_BREGS) * (KP >= 8 ? 2 : 1) / (KP * CPL);
-    return raw < 1 ? 1 : raw > 16 ? 16 : raw;
-}
+inline int aff_L(int KP, int CPL, bool bwd) { return aff_steps(KP, CPL, bwd); }
 
 // Tiling: G lanes x CPL columns per head (k + v columns forward, 2k + v
 // backward), HPW slots per wave = HH heads x SEG time segments, L steps per

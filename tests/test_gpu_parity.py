@@ -508,11 +508,13 @@ def test_affine_bf16_workload_shapes():
 
 
 # Forward chunks hold SEG time segments of NW * L steps: (k, v) = (4, 16)
-# gives 12 segments of 16 steps (192-step chunks), (8, 32) 3 segments of 16
-# steps (48-step chunks).  T just below, at and past a chunk or segment
-# boundary, and head counts that leave slots idle, exercise the segment map.
-@pytest.mark.parametrize("case", [(4, 16, 191), (4, 16, 192), (4, 16, 193), (4, 16, 17), (4, 16, 385),
-                                  (8, 32, 47), (8, 32, 48), (8, 32, 49), (8, 32, 97), (8, 32, 16)])
+# gives 2 segments of 32 steps (64-step chunks, 3 heads a workgroup), (8, 32)
+# one segment of 32 steps (32-step chunks, 3 heads).  T just below, at and
+# past a chunk or segment boundary, and head counts that leave slots idle,
+# exercise the segment map.
+@pytest.mark.parametrize("case", [(4, 16, 31), (4, 16, 32), (4, 16, 33), (4, 16, 63), (4, 16, 64),
+                                  (4, 16, 65), (4, 16, 129), (4, 16, 17), (8, 32, 31), (8, 32, 32),
+                                  (8, 32, 33), (8, 32, 65), (8, 32, 16), (8, 32, 97)])
 def test_affine_chunk_boundaries(case):
     k, v, T = case
     for (Bn, n) in ((1, 1), (2, 3)):
