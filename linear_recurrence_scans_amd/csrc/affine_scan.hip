@@ -958,13 +958,22 @@ __global__ __launch_bounds__(512) void affine_bwd_kernel(BwdArgs p) {
     get_cols<KP, CPL>(S, s_S + hsc * bs, NCP, c0);
     if (wave + 1 < NW) block_apply<KP, CPL>(S, s_X + ((wave + 1) * HPW + hsc) * bs, NCP, k, c0, is_y);
     float *part = s_part + wave * pw;
+    // X_{t-1} columns for dA, loaded one step ahead of their use: holding all
+    // L steps would cost L * KP * CPL registers and a workgroup per CU, while
+    // loading each in the step that uses it exposes the load latency.
+    float rxn[KP][CPL];
+    load_xprev<TS, KP, CPL, VIO, H0>(rxn, p, cl, m0 + (t_w + L - 1) * p.n, t_w + L - 1, active && t_w + L - 1 < p.T, gh);
 #pragma unroll
     for (int r = L - 1; r >= 0; --r) {
         const int64_t t = t_w + r;
-        // X_{t-1} columns for dA, loaded per step: holding all L steps would
-        // cost L * KP * CPL registers and a workgroup per CU.
         float rxr[KP][CPL];
-        load_xprev<TS, KP, CPL, VIO, H0>(rxr, p, cl, m0 + (t_w + r) * p.n, t_w + r, active && t_w + r < p.T, gh);
+#pragma unroll
+        for (int i = 0; i < KP; ++i)
+#pragma unroll
+            for (int cc = 0; cc < CPL; ++cc) rxr[i][cc] = rxn[i][cc];
+        if (r > 0)
+            load_xprev<TS, KP, CPL, VIO, H0>(rxn, p, cl, m0 + (t_w + r - 1) * p.n, t_w + r - 1,
+                                             active && t_w + r - 1 < p.T, gh);
         step_lds<KP, CPL>(S, s_A + ((wave * L + r) * HPW + hsc) * AS, rg[r]);  // S = Y_t
         if (t >= p.T) continue;  // wave-uniform
         const int64_t m = m0 + t * p.n;
