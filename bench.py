@@ -280,6 +280,25 @@ def cpu_baseline(wid, torch, workloads, storage=None):
 
 # ---------------------------------------------------------------------------
 
+def copy_bandwidth(torch, nbytes=1 << 30, reps=5):
+    """Device-to-device copy rate (GB/s, read + write bytes) on the current
+    stream: the practical streaming ceiling the scans are compared with."""
+    src = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    stream = torch.cuda.current_stream()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record(stream)
+    for _ in range(reps):
+        dst.copy_(src)
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / reps
+    del src, dst
+    return 2 * nbytes / (ms * 1e-3) / 1e9
+
+
 def traffic_key(kernel_name, desc):
     """Counter readings are stored per kernel and workload shape."""
     return "%s@%s" % (kernel_name, desc["workload"])
@@ -412,6 +431,11 @@ def main():
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": stored_traffic(dom, desc),
                 "algorithmic_bytes_per_launch": dk["bytes"], "avg_launch_ms": dk["avg_ms"]}
+    # Context: the same figure against a plain 1 GiB device-to-device copy
+    # measured now (after the timed region, outside it).
+    copy_gbs = copy_bandwidth(torch)
+    roofline["copy_GBps"] = round(copy_gbs, 1)
+    roofline["frac_of_copy"] = round(achieved / copy_gbs, 4)
 
     cpu = None
     if not args.no_cpu_baseline:
