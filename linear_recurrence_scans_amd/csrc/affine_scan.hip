@@ -644,6 +644,11 @@ __global__ __launch_bounds__(512) void affine_fwd_kernel(FwdArgs p) {
 template <int KP> struct AffRB {
     static constexpr int RB = KP < MISCAN_AFF_RBMAX ? KP : MISCAN_AFF_RBMAX;
 };
+// Floats between two lanes' dA partial sums (RB rows of KP) in LDS.  A stride
+// that is a multiple of 8 floats put the 16-byte writes of every lane of a
+// wave in the same 4 of the 32 banks; 4 more floats spread 8 consecutive
+// lanes over all 32.
+__host__ __device__ constexpr int aff_part_stride(int rbkp) { return rbkp >= 8 ? rbkp + 4 : rbkp; }
 
 // Source of the lane's columns of one of two (k x k | k x v) tensor pairs at
 // matrix index m: the k x k tensor for Z_M columns, the k x v tensor for Z_L
@@ -820,7 +825,8 @@ __global__ __launch_bounds__(512) void affine_bwd_kernel(BwdArgs p) {
     const int CH = NW * L;
     const int blk = KP * NCP;
     const int bs = pad_bank(blk);
-    const int pw = (HPW * G * RB * KP + 3) / 4 * 4;  // one wave's dA partial-sum buffer
+    constexpr int PS = aff_part_stride(RB * KP);      // floats per lane in it
+    const int pw = (HPW * G * PS + 3) / 4 * 4;        // one wave's dA partial-sum buffer
     float *s_A = s_dyn;                                 // [CH][HPW][AS]: A_{t+1}^T
     float *s_X = s_A + (CH * HPW * AS + 3) / 4 * 4;     // [NW][HPW][bs]: wave transforms / suffixes
     float *s_S = s_X + NW * HPW * bs;                   // [HPW][bs]: Y entering the chunk from later
@@ -1032,7 +1038,7 @@ __global__ __launch_bounds__(512) void affine_bwd_kernel(BwdArgs p) {
 #pragma unroll
                         for (int j = 0; j < KP; ++j) row[j] = fmaf(y, rxr[j][cc], row[j]);
                     }
-                    stv<KP, false>(part + ((hs * G + g) * RB + ii) * KP, row);
+                    stv<KP, false>(part + (hs * G + g) * PS + ii * KP, row);
                 }
             }
             // the wave's own partial sums are in LDS before any lane reads them
@@ -1046,7 +1052,7 @@ __global__ __launch_bounds__(512) void affine_bwd_kernel(BwdArgs p) {
                         float acc[4] = {0.f, 0.f, 0.f, 0.f};
                         for (int gg = 0; gg < G; ++gg) {
                             float q[4];
-                            ldv<4>(q, part + ((hs * G + gg) * RB + ii) * KP + j0);
+                            ldv<4>(q, part + (hs * G + gg) * PS + ii * KP + j0);
 #pragma unroll
                             for (int u = 0; u < 4; ++u) acc[u] += q[u];
                         }
@@ -1063,7 +1069,7 @@ __global__ __launch_bounds__(512) void affine_bwd_kernel(BwdArgs p) {
                         const int ii = e / KP, j = e - (e / KP) * KP;
                         const int i = ib + ii;
                         float acc = 0.f;
-                        for (int gg = 0; gg < G; ++gg) acc += part[((hs * G + gg) * RB + ii) * KP + j];
+                        for (int gg = 0; gg < G; ++gg) acc += part[(hs * G + gg) * PS + ii * KP + j];
                         if (i < k && j < k) st1(static_cast<TS *>(p.dA) + m * k * k + (int64_t)i * k + j, acc);
                     }
                 }
@@ -1153,7 +1159,7 @@ inline AffPlan make_plan(int64_t B, int64_t T, int64_t n, int k, int v, bool bwd
     const size_t a_ld = (size_t)pad_bank(pl.KP * pl.KP);  // LDS strides (see pad_bank)
     const size_t x_ld = (size_t)pad_bank(pl.KP * pl.NCP);
     const int rb = pl.KP < MISCAN_AFF_RBMAX ? pl.KP : MISCAN_AFF_RBMAX;  // AffRB
-    const size_t part = round_up((size_t)pl.HPW * pl.G * rb * pl.KP, 4);
+    const size_t part = round_up((size_t)pl.HPW * pl.G * aff_part_stride(rb * pl.KP), 4);
     const size_t limit = bwd ? BWD_LDS_MAX : FWD_LDS_MAX;
     const size_t payload = (size_t)pl.HH * pl.KP * pl.NCP;  // floats of one look-back slot
     const size_t fwd_db = MISCAN_AFF_STAGE_FLOATS / payload;
