@@ -102,6 +102,44 @@ __device__ __forceinline__ Item decode_item(uint32_t ticket, int n_tiles, int n_
 // workgroup runs the look-back (wg_lookback), and each wave rescans its rows
 // from its carry-in and stores A_t, Bc_t.
 // ---------------------------------------------------------------------------
+// LDS slot of channel ch of a tile whose lanes each hold VEC consecutive
+// channels.  With VEC = 8 a lane's two 16-byte halves lie 32 bytes apart, so
+// lanes l and l + 4 would hit the same four banks; swapping the halves of
+// every other group of four lanes (bit 2 of the slot flips when bit 5 of the
+// channel is set) spreads 8 consecutive lanes over all 32 banks and keeps the
+// per-channel accesses of consecutive threads conflict-free.
+template <int VEC>
+__device__ __forceinline__ int lds_ch(int ch) {
+    return VEC == 8 ? ch ^ ((ch >> 3) & 4) : ch;
+}
+// The lane's VEC channels of one LDS row, at their lds_ch slots (16-byte
+// accesses: rows are 16-byte aligned).
+template <int VEC>
+__device__ __forceinline__ void lds_put_lane(float *row, int lane, const float (&x)[VEC]) {
+    if constexpr (VEC == 8) {
+        const int s = lane & 4;
+        const f32x4 lo = {x[0], x[1], x[2], x[3]}, hi = {x[4], x[5], x[6], x[7]};
+        *reinterpret_cast<f32x4 *>(row + lane * 8 + s) = lo;
+        *reinterpret_cast<f32x4 *>(row + lane * 8 + (s ^ 4)) = hi;
+    } else {
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) row[lane * VEC + v] = x[v];
+    }
+}
+template <int VEC>
+__device__ __forceinline__ void lds_get_lane(float (&x)[VEC], const float *row, int lane) {
+    if constexpr (VEC == 8) {
+        const int s = lane & 4;
+        const f32x4 lo = *reinterpret_cast<const f32x4 *>(row + lane * 8 + s);
+        const f32x4 hi = *reinterpret_cast<const f32x4 *>(row + lane * 8 + (s ^ 4));
+        x[0] = lo.x; x[1] = lo.y; x[2] = lo.z; x[3] = lo.w;
+        x[4] = hi.x; x[5] = hi.y; x[6] = hi.z; x[7] = hi.w;
+    } else {
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) x[v] = row[lane * VEC + v];
+    }
+}
+
 // H0: the scan starts from the state p.h0 instead of 0 (Bc then holds the
 // states from h0): the carry entering chunk 0 is (1, h0).
 template <typename T, int VEC, int L, int NW, bool H0 = false>
@@ -110,10 +148,10 @@ __global__ __launch_bounds__(NW * 64) void linear_fwd_kernel(FwdArgs p) {
     using raw_t = typename PK::raw_t;
     constexpr int TILE = 64 * VEC, NT = NW * 64, CPT = (TILE + NT - 1) / NT;
 
-    __shared__ float s_A[NW][TILE];  // wave aggregates
-    __shared__ float s_H[NW][TILE];
-    __shared__ float s_cA[TILE];     // chunk carry-in
-    __shared__ float s_cH[TILE];
+    __shared__ __align__(16) float s_A[NW][TILE];  // wave aggregates (lds_ch slots)
+    __shared__ __align__(16) float s_H[NW][TILE];
+    __shared__ __align__(16) float s_cA[TILE];     // chunk carry-in
+    __shared__ __align__(16) float s_cH[TILE];
     __shared__ uint32_t s_ticket;
     __shared__ int s_k;
 
@@ -163,11 +201,8 @@ __global__ __launch_bounds__(NW * 64) void linear_fwd_kernel(FwdArgs p) {
             gA[v] = fa[v] * gA[v];
         }
     }
-#pragma unroll
-    for (int v = 0; v < VEC; ++v) {
-        s_A[wave][lane * VEC + v] = gA[v];
-        s_H[wave][lane * VEC + v] = gH[v];
-    }
+    lds_put_lane<VEC>(s_A[wave], lane, gA);
+    lds_put_lane<VEC>(s_H[wave], lane, gH);
     lds_barrier();
 
     // 3. Chunk aggregate per channel (waves in time order), look-back, carry.
@@ -181,7 +216,7 @@ __global__ __launch_bounds__(NW * 64) void linear_fwd_kernel(FwdArgs p) {
             in[q][0] = 1.f; in[q][1] = 0.f;
             if (ch < TILE)
                 for (int w = 0; w < NW; ++w) {
-                    const float x[2] = {s_A[w][ch], s_H[w][ch]};
+                    const float x[2] = {s_A[w][lds_ch<VEC>(ch)], s_H[w][lds_ch<VEC>(ch)]};
                     float r[2];
                     FwdOp::then(r, c[q], x);
                     c[q][0] = r[0]; c[q][1] = r[1];
@@ -199,21 +234,23 @@ __global__ __launch_bounds__(NW * 64) void linear_fwd_kernel(FwdArgs p) {
 #pragma unroll
         for (int q = 0; q < CPT; ++q) {
             const int ch = threadIdx.x + q * NT;
-            if (ch < TILE) { s_cA[ch] = in[q][0]; s_cH[ch] = in[q][1]; }
+            if (ch < TILE) { s_cA[lds_ch<VEC>(ch)] = in[q][0]; s_cH[lds_ch<VEC>(ch)] = in[q][1]; }
         }
         wg_publish_inc(p.ws, slot);
     }
 
     // 4. Carry into this wave: chunk carry-in, then waves 0..wave-1.
     float hA[VEC], hH[VEC];
-#pragma unroll
-    for (int v = 0; v < VEC; ++v) { hA[v] = s_cA[lane * VEC + v]; hH[v] = s_cH[lane * VEC + v]; }
+    lds_get_lane<VEC>(hA, s_cA, lane);
+    lds_get_lane<VEC>(hH, s_cH, lane);
     for (int w = 0; w < wave; ++w) {
+        float xA[VEC], xH[VEC];
+        lds_get_lane<VEC>(xA, s_A[w], lane);
+        lds_get_lane<VEC>(xH, s_H[w], lane);
 #pragma unroll
         for (int v = 0; v < VEC; ++v) {
-            const float xA = s_A[w][lane * VEC + v], xH = s_H[w][lane * VEC + v];
-            hH[v] = fmaf(xA, hH[v], xH);
-            hA[v] = xA * hA[v];
+            hH[v] = fmaf(xA[v], hH[v], xH[v]);
+            hA[v] = xA[v] * hA[v];
         }
     }
 
@@ -256,11 +293,11 @@ __global__ __launch_bounds__(NW * 64) void linear_bwd_kernel(BwdArgs p) {
     using raw_t = typename PK::raw_t;
     constexpr int TILE = 64 * VEC, NT = NW * 64, CPT = (TILE + NT - 1) / NT;
 
-    __shared__ float s_P[NW][TILE];
-    __shared__ float s_L[NW][TILE];
-    __shared__ float s_M[NW][TILE];
-    __shared__ float s_cL[TILE];
-    __shared__ float s_cM[TILE];
+    __shared__ __align__(16) float s_P[NW][TILE];  // wave aggregates (lds_ch slots)
+    __shared__ __align__(16) float s_L[NW][TILE];
+    __shared__ __align__(16) float s_M[NW][TILE];
+    __shared__ __align__(16) float s_cL[TILE];     // chunk carry-in
+    __shared__ __align__(16) float s_cM[TILE];
     __shared__ uint32_t s_ticket;
     __shared__ int s_k;
 
@@ -319,12 +356,9 @@ __global__ __launch_bounds__(NW * 64) void linear_bwd_kernel(BwdArgs p) {
             gP[v] = fc[v] * gP[v];
         }
     }
-#pragma unroll
-    for (int v = 0; v < VEC; ++v) {
-        s_P[wave][lane * VEC + v] = gP[v];
-        s_L[wave][lane * VEC + v] = gL[v];
-        s_M[wave][lane * VEC + v] = gM[v];
-    }
+    lds_put_lane<VEC>(s_P[wave], lane, gP);
+    lds_put_lane<VEC>(s_L[wave], lane, gL);
+    lds_put_lane<VEC>(s_M[wave], lane, gM);
     lds_barrier();
     // A_{t-1}, Bc_{t-1} are needed only by the rescan: loaded after the
     // barrier (which the compiler cannot hoist them over), they overlap the
@@ -366,7 +400,8 @@ __global__ __launch_bounds__(NW * 64) void linear_bwd_kernel(BwdArgs p) {
             in[q][0] = 1.f; in[q][1] = 0.f; in[q][2] = 0.f;
             if (ch < TILE)
                 for (int w = NW - 1; w >= 0; --w) {
-                    const float x[3] = {s_P[w][ch], s_L[w][ch], s_M[w][ch]};
+                    const int sl = lds_ch<VEC>(ch);
+                    const float x[3] = {s_P[w][sl], s_L[w][sl], s_M[w][sl]};
                     float r[3];
                     BwdOp::then(r, c[q], x);
                     c[q][0] = r[0]; c[q][1] = r[1]; c[q][2] = r[2];
@@ -376,22 +411,24 @@ __global__ __launch_bounds__(NW * 64) void linear_bwd_kernel(BwdArgs p) {
 #pragma unroll
         for (int q = 0; q < CPT; ++q) {
             const int ch = threadIdx.x + q * NT;
-            if (ch < TILE) { s_cL[ch] = in[q][1]; s_cM[ch] = in[q][2]; }
+            if (ch < TILE) { s_cL[lds_ch<VEC>(ch)] = in[q][1]; s_cM[lds_ch<VEC>(ch)] = in[q][2]; }
         }
         wg_publish_inc(p.ws, slot);
     }
 
     // 4. Adjoint state entering this wave: chunk carry-in, then waves NW-1 .. wave+1.
     float lam[VEC], mu[VEC];
-#pragma unroll
-    for (int v = 0; v < VEC; ++v) { lam[v] = s_cL[lane * VEC + v]; mu[v] = s_cM[lane * VEC + v]; }
+    lds_get_lane<VEC>(lam, s_cL, lane);
+    lds_get_lane<VEC>(mu, s_cM, lane);
     for (int w = NW - 1; w > wave; --w) {
+        float xP[VEC], xL[VEC], xM[VEC];
+        lds_get_lane<VEC>(xP, s_P[w], lane);
+        lds_get_lane<VEC>(xL, s_L[w], lane);
+        lds_get_lane<VEC>(xM, s_M[w], lane);
 #pragma unroll
         for (int v = 0; v < VEC; ++v) {
-            const int i = lane * VEC + v;
-            const float xP = s_P[w][i];
-            lam[v] = fmaf(xP, lam[v], s_L[w][i]);
-            mu[v] = fmaf(xP, mu[v], s_M[w][i]);
+            lam[v] = fmaf(xP[v], lam[v], xL[v]);
+            mu[v] = fmaf(xP[v], mu[v], xM[v]);
         }
     }
 
