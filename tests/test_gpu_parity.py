@@ -82,14 +82,16 @@ def test_linear_fwd_workload1(seed):
 
 
 @pytest.mark.parametrize("shape", [(1, 1, 1), (2, 2, 3), (1, 63, 100), (3, 65, 1), (2, 1000, 3),
-                                   (1, 4097, 100), (2, 130, 520), (1, 64, 256), (2, 129, 257)])
+                                   (1, 4097, 100), (2, 130, 520), (1, 64, 256), (2, 129, 257),
+                                   (1, 31, 260), (2, 32, 256), (1, 33, 516)])
 def test_linear_edge_shapes_f32(shape):
     say("linear fwd+bwd fp32 edge shape", shape)
     errs = run_linear(lin_case(*shape, seed=sum(shape)), torch.float32)
     assert max(errs.values()) <= TOL[torch.float32], (shape, errs)
 
 
-@pytest.mark.parametrize("shape", [(2, 1000, 4104), (1, 77, 37), (3, 33, 6), (1, 300, 12)])
+@pytest.mark.parametrize("shape", [(2, 1000, 4104), (1, 77, 37), (3, 33, 6), (1, 300, 12), (2, 32, 512),
+                                   (1, 97, 1024)])
 def test_linear_bf16_reduced(shape):
     """bf16 storage / fp32 arithmetic on the workload-3 distribution; D values
     pick the 8-, 4-, 2- and 1-wide vector kernels and ragged tiles."""
