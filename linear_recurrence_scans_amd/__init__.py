@@ -13,6 +13,7 @@ provided as aliases with the same argument order and returns.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 
@@ -23,6 +24,7 @@ __all__ = [
     "mi_status_string", "mi_device_check",
     "mi_linear_scan_workspace", "mi_linear_scan_fwd", "mi_linear_scan_bwd",
     "mi_linear_scan_fwd_h0", "mi_linear_scan_bwd_h0",
+    "set_checked", "workspace_timeouts",
     "mi_scan_log_workspace", "mi_scan_log_fwd", "mi_scan_log_bwd",
     "mi_affine_scan_workspace", "mi_affine_scan_fwd", "mi_affine_scan_bwd",
     "mi_affine_scan_fwd_h0", "mi_affine_scan_bwd_h0",
@@ -140,23 +142,88 @@ def _out(t, like: torch.Tensor, name: str) -> torch.Tensor:
     return t
 
 
-def _stream(stream, device) -> int:
-    if stream is None:
-        stream = torch.cuda.current_stream(device)
-    return stream.cuda_stream
+# Checked mode: after every call, wait for the stream and raise if a
+# cross-workgroup wait gave up (word 1 of the workspace, zero after every
+# correct run).  Off by default (it synchronises); the environment variable
+# MISCAN_CHECK=1 or set_checked(True) turns it on.
+_checked = os.environ.get("MISCAN_CHECK", "0") not in ("", "0")
+
+
+def set_checked(on: bool = True):
+    """Turn checked mode (synchronise and verify the workspace after each call) on or off."""
+    global _checked
+    _checked = bool(on)
+
+
+def workspace_timeouts(ws: torch.Tensor) -> int:
+    """Cross-workgroup waits that hit their spin limit during the last call that
+    used workspace `ws` (word 1; synchronises with the device)."""
+    return int(ws[4:8].cpu().view(torch.int32).item())
+
+
+class _Call:
+    """Stream and device context of one library call.
+
+    The kernels run on `stream` (default: torch's current stream).  When it is
+    another stream, it first waits for the current one (so inputs produced
+    there are ready), every tensor the call allocates (contiguous copies,
+    outputs, workspace) is allocated on it, and every caller tensor it touches
+    is recorded on it, so the caching allocator reuses none of that memory
+    before the kernels are done.
+    """
+
+    def __init__(self, stream, device):
+        self.device = device
+        cur = torch.cuda.current_stream(device)
+        self.side = stream is not None and stream != cur
+        self.stream = stream if self.side else cur
+        if self.side:
+            self.stream.wait_stream(cur)
+        self._ctx = contextlib.ExitStack()
+
+    def __enter__(self):
+        self._ctx.enter_context(torch.cuda.device(self.device))
+        if self.side:
+            self._ctx.enter_context(torch.cuda.stream(self.stream))
+        return self
+
+    def __exit__(self, *exc):
+        return self._ctx.__exit__(*exc)
+
+    def keep(self, *ts):
+        """Record caller tensors on a side stream."""
+        if self.side:
+            for t in ts:
+                if t is not None and t.numel():
+                    t.record_stream(self.stream)
+
+    @property
+    def handle(self) -> int:
+        return self.stream.cuda_stream
 
 
 def _workspace(ws, nbytes: int, device):
     if ws is None:
-        return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+        return torch.empty(max(int(nbytes), 8), dtype=torch.uint8, device=device)
     if ws.device != device or ws.numel() * ws.element_size() < nbytes:
         raise ValueError("workspace too small: %d bytes needed" % nbytes)
     return ws
 
 
-def _check(st: int, where: str):
+def _check(st: int, where: str, call=None, ws=None):
     if st != 0:
         raise MiscanError(st, where)
+    # (a call with nothing to scan launches no scan and leaves ws untouched)
+    if _checked and call is not None and ws is not None and ws.numel() >= 8:
+        call.stream.synchronize()
+        n = workspace_timeouts(ws)
+        if n:
+            raise RuntimeError("%s: %d cross-workgroup wait(s) hit the spin limit; the result is not valid"
+                               % (where, n))
+
+
+def _nonempty(t: torch.Tensor) -> bool:
+    return t.numel() > 0
 
 
 def _same(ref: torch.Tensor, *ts):
@@ -169,45 +236,60 @@ def _same(ref: torch.Tensor, *ts):
 # k = 1 channel scan
 # ---------------------------------------------------------------------------
 
+def _device(t, name: str):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if not t.is_cuda:
+        raise ValueError("%s must be a GPU tensor (the scans run only on the GPU)" % name)
+    return t.device
+
+
+def _nbytes(t) -> int:
+    return t.numel() * t.element_size()
+
+
 def mi_linear_scan_workspace(B: int, T: int, D: int, dtype=torch.float32) -> int:
     return int(_load().mi_linear_scan_workspace(B, T, D, _DTYPES[dtype]))
 
 
 def mi_linear_scan_fwd(a, b, A=None, Bc=None, *, ws=None, stream=None):
-    """(A, Bc) = linear_scan_fwd(a, b); a, b (B, T, D) float32 or bfloat16."""
-    a, b = _dev_tensor(a, "a"), _dev_tensor(b, "b")
-    if a.dim() != 3 or b.shape != a.shape:
-        raise ValueError("a and b must both be (B, T, D)")
-    _same(a, b)
-    A, Bc = _out(A, a, "A"), _out(Bc, a, "Bc")
-    Bn, T, D = a.shape
-    dt = _dt(a)
-    nbytes = _load().mi_linear_scan_workspace(Bn, T, D, dt)
-    ws = _workspace(ws, nbytes, a.device)
-    st = _load().mi_linear_scan_fwd(a.data_ptr(), b.data_ptr(), A.data_ptr(), Bc.data_ptr(),
-                                    Bn, T, D, dt, ws.data_ptr(), ws.numel() * ws.element_size(),
-                                    _stream(stream, a.device))
-    _check(st, "mi_linear_scan_fwd")
+    """(A, Bc) = linear_scan_fwd(a, b); a, b (B, T, D) float32 or bfloat16.
+
+    Runs on `stream` (default: torch's current stream); see _Call for how a
+    side stream is ordered against the current one."""
+    with _Call(stream, _device(a, "a")) as c:
+        a, b = _dev_tensor(a, "a"), _dev_tensor(b, "b")
+        if a.dim() != 3 or b.shape != a.shape:
+            raise ValueError("a and b must both be (B, T, D)")
+        _same(a, b)
+        A, Bc = _out(A, a, "A"), _out(Bc, a, "Bc")
+        Bn, T, D = a.shape
+        dt = _dt(a)
+        ws = _workspace(ws, _load().mi_linear_scan_workspace(Bn, T, D, dt), a.device)
+        c.keep(a, b, A, Bc, ws)
+        st = _load().mi_linear_scan_fwd(a.data_ptr(), b.data_ptr(), A.data_ptr(), Bc.data_ptr(),
+                                        Bn, T, D, dt, ws.data_ptr(), _nbytes(ws), c.handle)
+        _check(st, "mi_linear_scan_fwd", c, ws if _nonempty(a) else None)
     return A, Bc
 
 
 def mi_linear_scan_bwd(a, A, Bc, gA, gBc, da=None, db=None, *, ws=None, stream=None):
     """(da, db) = linear_scan_bwd(a, A, Bc, gA, gBc); all (B, T, D)."""
-    a, A, Bc, gA, gBc = (_dev_tensor(t, n) for t, n in
-                         ((a, "a"), (A, "A"), (Bc, "Bc"), (gA, "gA"), (gBc, "gBc")))
-    if a.dim() != 3 or any(t.shape != a.shape for t in (A, Bc, gA, gBc)):
-        raise ValueError("a, A, Bc, gA, gBc must all be (B, T, D)")
-    _same(a, A, Bc, gA, gBc)
-    da, db = _out(da, a, "da"), _out(db, a, "db")
-    Bn, T, D = a.shape
-    dt = _dt(a)
-    nbytes = _load().mi_linear_scan_workspace(Bn, T, D, dt)
-    ws = _workspace(ws, nbytes, a.device)
-    st = _load().mi_linear_scan_bwd(a.data_ptr(), A.data_ptr(), Bc.data_ptr(), gA.data_ptr(),
-                                    gBc.data_ptr(), da.data_ptr(), db.data_ptr(), Bn, T, D, dt,
-                                    ws.data_ptr(), ws.numel() * ws.element_size(),
-                                    _stream(stream, a.device))
-    _check(st, "mi_linear_scan_bwd")
+    with _Call(stream, _device(a, "a")) as c:
+        a, A, Bc, gA, gBc = (_dev_tensor(t, n) for t, n in
+                             ((a, "a"), (A, "A"), (Bc, "Bc"), (gA, "gA"), (gBc, "gBc")))
+        if a.dim() != 3 or any(t.shape != a.shape for t in (A, Bc, gA, gBc)):
+            raise ValueError("a, A, Bc, gA, gBc must all be (B, T, D)")
+        _same(a, A, Bc, gA, gBc)
+        da, db = _out(da, a, "da"), _out(db, a, "db")
+        Bn, T, D = a.shape
+        dt = _dt(a)
+        ws = _workspace(ws, _load().mi_linear_scan_workspace(Bn, T, D, dt), a.device)
+        c.keep(a, A, Bc, gA, gBc, da, db, ws)
+        st = _load().mi_linear_scan_bwd(a.data_ptr(), A.data_ptr(), Bc.data_ptr(), gA.data_ptr(),
+                                        gBc.data_ptr(), da.data_ptr(), db.data_ptr(), Bn, T, D, dt,
+                                        ws.data_ptr(), _nbytes(ws), c.handle)
+        _check(st, "mi_linear_scan_bwd", c, ws if _nonempty(a) else None)
     return da, db
 
 
@@ -228,37 +310,41 @@ def _ptr(t):
 def mi_linear_scan_fwd_h0(a, b, h0=None, A=None, H=None, *, ws=None, stream=None):
     """(A, H): the scan from the initial state h0 (B, D) (None = zero);
     H_t = a_t H_{t-1} + b_t with H_0 = h0.  The final state is (A[:, -1], H[:, -1])."""
-    a, b = _dev_tensor(a, "a"), _dev_tensor(b, "b")
-    if a.dim() != 3 or b.shape != a.shape:
-        raise ValueError("a and b must both be (B, T, D)")
-    _same(a, b)
-    Bn, T, D = a.shape
-    h0 = _state(h0, a, (Bn, D), "h0")
-    A, H = _out(A, a, "A"), _out(H, a, "H")
-    dt = _dt(a)
-    ws = _workspace(ws, _load().mi_linear_scan_workspace(Bn, T, D, dt), a.device)
-    st = _load().mi_linear_scan_fwd_h0(a.data_ptr(), b.data_ptr(), _ptr(h0), A.data_ptr(), H.data_ptr(), Bn, T, D,
-                                       dt, ws.data_ptr(), ws.numel() * ws.element_size(), _stream(stream, a.device))
-    _check(st, "mi_linear_scan_fwd_h0")
+    with _Call(stream, _device(a, "a")) as c:
+        a, b = _dev_tensor(a, "a"), _dev_tensor(b, "b")
+        if a.dim() != 3 or b.shape != a.shape:
+            raise ValueError("a and b must both be (B, T, D)")
+        _same(a, b)
+        Bn, T, D = a.shape
+        h0 = _state(h0, a, (Bn, D), "h0")
+        A, H = _out(A, a, "A"), _out(H, a, "H")
+        dt = _dt(a)
+        ws = _workspace(ws, _load().mi_linear_scan_workspace(Bn, T, D, dt), a.device)
+        c.keep(a, b, h0, A, H, ws)
+        st = _load().mi_linear_scan_fwd_h0(a.data_ptr(), b.data_ptr(), _ptr(h0), A.data_ptr(), H.data_ptr(),
+                                           Bn, T, D, dt, ws.data_ptr(), _nbytes(ws), c.handle)
+        _check(st, "mi_linear_scan_fwd_h0", c, ws if _nonempty(a) else None)
     return A, H
 
 
 def mi_linear_scan_bwd_h0(a, A, H, h0, gA, gH, da=None, db=None, dh0=None, *, ws=None, stream=None):
     """(da, db, dh0): gradient of mi_linear_scan_fwd_h0 for upstream grads gA, gH."""
-    a, A, H, gA, gH = (_dev_tensor(t, n) for t, n in ((a, "a"), (A, "A"), (H, "H"), (gA, "gA"), (gH, "gH")))
-    if a.dim() != 3 or any(t.shape != a.shape for t in (A, H, gA, gH)):
-        raise ValueError("a, A, H, gA, gH must all be (B, T, D)")
-    _same(a, A, H, gA, gH)
-    Bn, T, D = a.shape
-    h0 = _state(h0, a, (Bn, D), "h0")
-    da, db = _out(da, a, "da"), _out(db, a, "db")
-    dh0 = _out(dh0, a.new_empty((Bn, D)), "dh0")
-    dt = _dt(a)
-    ws = _workspace(ws, _load().mi_linear_scan_workspace(Bn, T, D, dt), a.device)
-    st = _load().mi_linear_scan_bwd_h0(a.data_ptr(), A.data_ptr(), H.data_ptr(), _ptr(h0), gA.data_ptr(),
-                                       gH.data_ptr(), da.data_ptr(), db.data_ptr(), dh0.data_ptr(), Bn, T, D, dt,
-                                       ws.data_ptr(), ws.numel() * ws.element_size(), _stream(stream, a.device))
-    _check(st, "mi_linear_scan_bwd_h0")
+    with _Call(stream, _device(a, "a")) as c:
+        a, A, H, gA, gH = (_dev_tensor(t, n) for t, n in ((a, "a"), (A, "A"), (H, "H"), (gA, "gA"), (gH, "gH")))
+        if a.dim() != 3 or any(t.shape != a.shape for t in (A, H, gA, gH)):
+            raise ValueError("a, A, H, gA, gH must all be (B, T, D)")
+        _same(a, A, H, gA, gH)
+        Bn, T, D = a.shape
+        h0 = _state(h0, a, (Bn, D), "h0")
+        da, db = _out(da, a, "da"), _out(db, a, "db")
+        dh0 = _out(dh0, a.new_empty((Bn, D)), "dh0")
+        dt = _dt(a)
+        ws = _workspace(ws, _load().mi_linear_scan_workspace(Bn, T, D, dt), a.device)
+        c.keep(a, A, H, h0, gA, gH, da, db, dh0, ws)
+        st = _load().mi_linear_scan_bwd_h0(a.data_ptr(), A.data_ptr(), H.data_ptr(), _ptr(h0), gA.data_ptr(),
+                                           gH.data_ptr(), da.data_ptr(), db.data_ptr(), dh0.data_ptr(), Bn, T, D,
+                                           dt, ws.data_ptr(), _nbytes(ws), c.handle)
+        _check(st, "mi_linear_scan_bwd_h0", c, ws if _nonempty(a) else None)
     return da, db, dh0
 
 
@@ -272,41 +358,41 @@ def mi_scan_log_workspace(B: int, T: int, D: int, dtype=torch.float32) -> int:
 
 def mi_scan_log_fwd(log_coeffs, log_values, h=None, *, ws=None, stream=None):
     """h (B, T, D) = parallel_scan_log_fwd(log_coeffs (B,T,D), log_values (B,T+1,D))."""
-    lc, lv = _dev_tensor(log_coeffs, "log_coeffs"), _dev_tensor(log_values, "log_values")
-    if lc.dim() != 3 or lv.dim() != 3 or lv.shape != (lc.shape[0], lc.shape[1] + 1, lc.shape[2]):
-        raise ValueError("log_coeffs must be (B, T, D) and log_values (B, T+1, D)")
-    _same(lc, lv)
-    h = _out(h, lc, "h")
-    Bn, T, D = lc.shape
-    dt = _dt(lc)
-    nbytes = _load().mi_scan_log_workspace(Bn, T, D, dt)
-    ws = _workspace(ws, nbytes, lc.device)
-    st = _load().mi_scan_log_fwd(lc.data_ptr(), lv.data_ptr(), h.data_ptr(), Bn, T, D, dt,
-                                 ws.data_ptr(), ws.numel() * ws.element_size(),
-                                 _stream(stream, lc.device))
-    _check(st, "mi_scan_log_fwd")
+    with _Call(stream, _device(log_coeffs, "log_coeffs")) as c:
+        lc, lv = _dev_tensor(log_coeffs, "log_coeffs"), _dev_tensor(log_values, "log_values")
+        if lc.dim() != 3 or lv.dim() != 3 or lv.shape != (lc.shape[0], lc.shape[1] + 1, lc.shape[2]):
+            raise ValueError("log_coeffs must be (B, T, D) and log_values (B, T+1, D)")
+        _same(lc, lv)
+        h = _out(h, lc, "h")
+        Bn, T, D = lc.shape
+        dt = _dt(lc)
+        ws = _workspace(ws, _load().mi_scan_log_workspace(Bn, T, D, dt), lc.device)
+        c.keep(lc, lv, h, ws)
+        st = _load().mi_scan_log_fwd(lc.data_ptr(), lv.data_ptr(), h.data_ptr(), Bn, T, D, dt,
+                                     ws.data_ptr(), _nbytes(ws), c.handle)
+        _check(st, "mi_scan_log_fwd", c, ws if _nonempty(lc) else None)
     return h
 
 
 def mi_scan_log_bwd(log_coeffs, log_values, h, g, dlog_coeffs=None, dlog_values=None, *, ws=None, stream=None):
     """(dlog_coeffs (B,T,D), dlog_values (B,T+1,D)): gradient of parallel_scan_log_fwd
     given its output h (B,T,D) and the upstream gradient g = dL/dh (B,T,D)."""
-    lc, lv = _dev_tensor(log_coeffs, "log_coeffs"), _dev_tensor(log_values, "log_values")
-    h, g = _dev_tensor(h, "h"), _dev_tensor(g, "g")
-    if lc.dim() != 3 or lv.dim() != 3 or lv.shape != (lc.shape[0], lc.shape[1] + 1, lc.shape[2]):
-        raise ValueError("log_coeffs must be (B, T, D) and log_values (B, T+1, D)")
-    if h.shape != lc.shape or g.shape != lc.shape:
-        raise ValueError("h and g must be (B, T, D)")
-    _same(lc, lv, h, g)
-    dlc, dlv = _out(dlog_coeffs, lc, "dlog_coeffs"), _out(dlog_values, lv, "dlog_values")
-    Bn, T, D = lc.shape
-    dt = _dt(lc)
-    nbytes = _load().mi_scan_log_workspace(Bn, T, D, dt)
-    ws = _workspace(ws, nbytes, lc.device)
-    st = _load().mi_scan_log_bwd(lc.data_ptr(), lv.data_ptr(), h.data_ptr(), g.data_ptr(), dlc.data_ptr(),
-                                 dlv.data_ptr(), Bn, T, D, dt, ws.data_ptr(), ws.numel() * ws.element_size(),
-                                 _stream(stream, lc.device))
-    _check(st, "mi_scan_log_bwd")
+    with _Call(stream, _device(log_coeffs, "log_coeffs")) as c:
+        lc, lv = _dev_tensor(log_coeffs, "log_coeffs"), _dev_tensor(log_values, "log_values")
+        h, g = _dev_tensor(h, "h"), _dev_tensor(g, "g")
+        if lc.dim() != 3 or lv.dim() != 3 or lv.shape != (lc.shape[0], lc.shape[1] + 1, lc.shape[2]):
+            raise ValueError("log_coeffs must be (B, T, D) and log_values (B, T+1, D)")
+        if h.shape != lc.shape or g.shape != lc.shape:
+            raise ValueError("h and g must be (B, T, D)")
+        _same(lc, lv, h, g)
+        dlc, dlv = _out(dlog_coeffs, lc, "dlog_coeffs"), _out(dlog_values, lv, "dlog_values")
+        Bn, T, D = lc.shape
+        dt = _dt(lc)
+        ws = _workspace(ws, _load().mi_scan_log_workspace(Bn, T, D, dt), lc.device)
+        c.keep(lc, lv, h, g, dlc, dlv, ws)
+        st = _load().mi_scan_log_bwd(lc.data_ptr(), lv.data_ptr(), h.data_ptr(), g.data_ptr(), dlc.data_ptr(),
+                                     dlv.data_ptr(), Bn, T, D, dt, ws.data_ptr(), _nbytes(ws), c.handle)
+        _check(st, "mi_scan_log_bwd", c, ws if _nonempty(lc) else None)
     return dlc, dlv
 
 
@@ -328,75 +414,80 @@ def _affine_shapes(A, Bm):
 
 
 def mi_affine_scan_fwd(A, Bm, Abar=None, Bbar=None, *, ws=None, stream=None):
-    """(Abar, Bbar) = affine_scan_fwd(A (B,T,n,k,k), Bm (B,T,n,k,v)); float32 or bfloat16 storage."""
-    A, Bm = _dev_tensor(A, "A"), _dev_tensor(Bm, "Bm")
-    _same(A, Bm)
-    Bn, T, n, k, v = _affine_shapes(A, Bm)
-    Abar, Bbar = _out(Abar, A, "Abar"), _out(Bbar, Bm, "Bbar")
-    dt = _dt(A)
-    nbytes = _load().mi_affine_scan_workspace(Bn, T, n, k, v, dt)
-    ws = _workspace(ws, nbytes, A.device)
-    st = _load().mi_affine_scan_fwd(A.data_ptr(), Bm.data_ptr(), Abar.data_ptr(), Bbar.data_ptr(),
-                                    Bn, T, n, k, v, dt, ws.data_ptr(),
-                                    ws.numel() * ws.element_size(), _stream(stream, A.device))
-    _check(st, "mi_affine_scan_fwd")
+    """(Abar, Bbar) = affine_scan_fwd(A (B,T,n,k,k), Bm (B,T,n,k,v))."""
+    with _Call(stream, _device(A, "A")) as c:
+        A, Bm = _dev_tensor(A, "A"), _dev_tensor(Bm, "Bm")
+        _same(A, Bm)
+        Bn, T, n, k, v = _affine_shapes(A, Bm)
+        Abar, Bbar = _out(Abar, A, "Abar"), _out(Bbar, Bm, "Bbar")
+        dt = _dt(A)
+        ws = _workspace(ws, _load().mi_affine_scan_workspace(Bn, T, n, k, v, dt), A.device)
+        c.keep(A, Bm, Abar, Bbar, ws)
+        st = _load().mi_affine_scan_fwd(A.data_ptr(), Bm.data_ptr(), Abar.data_ptr(), Bbar.data_ptr(),
+                                        Bn, T, n, k, v, dt, ws.data_ptr(), _nbytes(ws), c.handle)
+        _check(st, "mi_affine_scan_fwd", c, ws if _nonempty(A) else None)
     return Abar, Bbar
 
 
 def mi_affine_scan_bwd(A, Abar, Bbar, gAbar, gBbar, dA=None, dB=None, *, ws=None, stream=None):
-    """(dA, dB) = affine_scan_bwd(A, Abar, Bbar, gAbar, gBbar); float32 or bfloat16 storage."""
-    A, Abar, Bbar, gAbar, gBbar = (_dev_tensor(t, nm) for t, nm in
-                                   ((A, "A"), (Abar, "Abar"), (Bbar, "Bbar"),
-                                    (gAbar, "gAbar"), (gBbar, "gBbar")))
-    _same(A, Abar, Bbar, gAbar, gBbar)
-    Bn, T, n, k, v = _affine_shapes(A, Bbar)
-    if Abar.shape != A.shape or gAbar.shape != A.shape or gBbar.shape != Bbar.shape:
-        raise ValueError("Abar, gAbar must match A; gBbar must match Bbar")
-    dA, dB = _out(dA, A, "dA"), _out(dB, Bbar, "dB")
-    dt = _dt(A)
-    nbytes = _load().mi_affine_scan_workspace(Bn, T, n, k, v, dt)
-    ws = _workspace(ws, nbytes, A.device)
-    st = _load().mi_affine_scan_bwd(A.data_ptr(), Abar.data_ptr(), Bbar.data_ptr(),
-                                    gAbar.data_ptr(), gBbar.data_ptr(), dA.data_ptr(),
-                                    dB.data_ptr(), Bn, T, n, k, v, dt, ws.data_ptr(),
-                                    ws.numel() * ws.element_size(), _stream(stream, A.device))
-    _check(st, "mi_affine_scan_bwd")
+    """(dA, dB) = affine_scan_bwd(A, Abar, Bbar, gAbar, gBbar)."""
+    with _Call(stream, _device(A, "A")) as c:
+        A, Abar, Bbar, gAbar, gBbar = (_dev_tensor(t, nm) for t, nm in
+                                       ((A, "A"), (Abar, "Abar"), (Bbar, "Bbar"),
+                                        (gAbar, "gAbar"), (gBbar, "gBbar")))
+        _same(A, Abar, Bbar, gAbar, gBbar)
+        Bn, T, n, k, v = _affine_shapes(A, Bbar)
+        if Abar.shape != A.shape or gAbar.shape != A.shape or gBbar.shape != Bbar.shape:
+            raise ValueError("Abar, gAbar must match A; gBbar must match Bbar")
+        dA, dB = _out(dA, A, "dA"), _out(dB, Bbar, "dB")
+        dt = _dt(A)
+        ws = _workspace(ws, _load().mi_affine_scan_workspace(Bn, T, n, k, v, dt), A.device)
+        c.keep(A, Abar, Bbar, gAbar, gBbar, dA, dB, ws)
+        st = _load().mi_affine_scan_bwd(A.data_ptr(), Abar.data_ptr(), Bbar.data_ptr(),
+                                        gAbar.data_ptr(), gBbar.data_ptr(), dA.data_ptr(),
+                                        dB.data_ptr(), Bn, T, n, k, v, dt, ws.data_ptr(),
+                                        _nbytes(ws), c.handle)
+        _check(st, "mi_affine_scan_bwd", c, ws if _nonempty(A) else None)
     return dA, dB
 
 
 def mi_affine_scan_fwd_h0(A, Bm, H0=None, Abar=None, H=None, *, ws=None, stream=None):
     """(Abar, H): the k x k scan from X_0 = [I | H0], H0 (B, n, k, v) (None = zero)."""
-    A, Bm = _dev_tensor(A, "A"), _dev_tensor(Bm, "Bm")
-    _same(A, Bm)
-    Bn, T, n, k, v = _affine_shapes(A, Bm)
-    H0 = _state(H0, A, (Bn, n, k, v), "H0")
-    Abar, H = _out(Abar, A, "Abar"), _out(H, Bm, "H")
-    dt = _dt(A)
-    ws = _workspace(ws, _load().mi_affine_scan_workspace(Bn, T, n, k, v, dt), A.device)
-    st = _load().mi_affine_scan_fwd_h0(A.data_ptr(), Bm.data_ptr(), _ptr(H0), Abar.data_ptr(), H.data_ptr(),
-                                       Bn, T, n, k, v, dt, ws.data_ptr(), ws.numel() * ws.element_size(),
-                                       _stream(stream, A.device))
-    _check(st, "mi_affine_scan_fwd_h0")
+    with _Call(stream, _device(A, "A")) as c:
+        A, Bm = _dev_tensor(A, "A"), _dev_tensor(Bm, "Bm")
+        _same(A, Bm)
+        Bn, T, n, k, v = _affine_shapes(A, Bm)
+        H0 = _state(H0, A, (Bn, n, k, v), "H0")
+        Abar, H = _out(Abar, A, "Abar"), _out(H, Bm, "H")
+        dt = _dt(A)
+        ws = _workspace(ws, _load().mi_affine_scan_workspace(Bn, T, n, k, v, dt), A.device)
+        c.keep(A, Bm, H0, Abar, H, ws)
+        st = _load().mi_affine_scan_fwd_h0(A.data_ptr(), Bm.data_ptr(), _ptr(H0), Abar.data_ptr(), H.data_ptr(),
+                                           Bn, T, n, k, v, dt, ws.data_ptr(), _nbytes(ws), c.handle)
+        _check(st, "mi_affine_scan_fwd_h0", c, ws if _nonempty(A) else None)
     return Abar, H
 
 
 def mi_affine_scan_bwd_h0(A, Abar, H, H0, gAbar, gH, dA=None, dB=None, dH0=None, *, ws=None, stream=None):
     """(dA, dB, dH0): gradient of mi_affine_scan_fwd_h0."""
-    A, Abar, H, gAbar, gH = (_dev_tensor(t, nm) for t, nm in
-                             ((A, "A"), (Abar, "Abar"), (H, "H"), (gAbar, "gAbar"), (gH, "gH")))
-    _same(A, Abar, H, gAbar, gH)
-    Bn, T, n, k, v = _affine_shapes(A, H)
-    if Abar.shape != A.shape or gAbar.shape != A.shape or gH.shape != H.shape:
-        raise ValueError("Abar, gAbar must match A; gH must match H")
-    H0 = _state(H0, A, (Bn, n, k, v), "H0")
-    dA, dB = _out(dA, A, "dA"), _out(dB, H, "dB")
-    dH0 = _out(dH0, A.new_empty((Bn, n, k, v)), "dH0")
-    dt = _dt(A)
-    ws = _workspace(ws, _load().mi_affine_scan_workspace(Bn, T, n, k, v, dt), A.device)
-    st = _load().mi_affine_scan_bwd_h0(A.data_ptr(), Abar.data_ptr(), H.data_ptr(), _ptr(H0), gAbar.data_ptr(),
-                                       gH.data_ptr(), dA.data_ptr(), dB.data_ptr(), dH0.data_ptr(), Bn, T, n, k, v,
-                                       dt, ws.data_ptr(), ws.numel() * ws.element_size(), _stream(stream, A.device))
-    _check(st, "mi_affine_scan_bwd_h0")
+    with _Call(stream, _device(A, "A")) as c:
+        A, Abar, H, gAbar, gH = (_dev_tensor(t, nm) for t, nm in
+                                 ((A, "A"), (Abar, "Abar"), (H, "H"), (gAbar, "gAbar"), (gH, "gH")))
+        _same(A, Abar, H, gAbar, gH)
+        Bn, T, n, k, v = _affine_shapes(A, H)
+        if Abar.shape != A.shape or gAbar.shape != A.shape or gH.shape != H.shape:
+            raise ValueError("Abar, gAbar must match A; gH must match H")
+        H0 = _state(H0, A, (Bn, n, k, v), "H0")
+        dA, dB = _out(dA, A, "dA"), _out(dB, H, "dB")
+        dH0 = _out(dH0, A.new_empty((Bn, n, k, v)), "dH0")
+        dt = _dt(A)
+        ws = _workspace(ws, _load().mi_affine_scan_workspace(Bn, T, n, k, v, dt), A.device)
+        c.keep(A, Abar, H, H0, gAbar, gH, dA, dB, dH0, ws)
+        st = _load().mi_affine_scan_bwd_h0(A.data_ptr(), Abar.data_ptr(), H.data_ptr(), _ptr(H0),
+                                           gAbar.data_ptr(), gH.data_ptr(), dA.data_ptr(), dB.data_ptr(),
+                                           dH0.data_ptr(), Bn, T, n, k, v, dt, ws.data_ptr(), _nbytes(ws),
+                                           c.handle)
+        _check(st, "mi_affine_scan_bwd_h0", c, ws if _nonempty(A) else None)
     return dA, dB, dH0
 
 

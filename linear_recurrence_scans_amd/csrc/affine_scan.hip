@@ -137,6 +137,7 @@ struct FwdArgs {
     int G, HPW, NCP, n_groups, n_chunks, NW;
     int HH;  // heads per workgroup; SEG = HPW / HH time segments per chunk
     int DB;  // payload blocks the look-back stages in LDS per round trip
+    int lb_window;  // look-back window W (a power of two)
     WsPtrs ws;
 };
 
@@ -150,6 +151,7 @@ struct BwdArgs {
     int G, HPW, NCP, n_groups, n_chunks, NW;
     int HH;  // heads per workgroup; SEG = HPW / HH time segments per chunk
     int DB;  // payload blocks the look-back stages in LDS per round trip
+    int lb_window;  // look-back window W (a power of two)
     WsPtrs ws;
 };
 
@@ -412,37 +414,27 @@ __device__ __forceinline__ void block_apply(float (&S)[KP][CPL], const float *bl
 }
 
 // Look-back payloads into LDS, cooperatively: one round trip for a batch of
-// up to DB published blocks instead of one per block.  Fold index q = 0 is the
-// inclusive state of slot j0 (the `inc` array), q >= 1 the transform of slot
-// j0 + dir * q (the `agg` array); the batch holds indices b0 .. b0 + nb - 1,
-// index q at s_stage + (q - b0) * slot_sz.  Slot j of the workgroup's group
-// lives at (row0 + j) * slot_sz of either array.  The transforms of a batch
-// are consecutive slots, so each array is read through one descriptor.
-__device__ __forceinline__ void stage_payloads(float *s_stage, const WsPtrs &ws, int64_t row0, int j0, int dir,
-                                               int b0, int nb, int slot_sz) {
+// up to DB published blocks instead of one per block.  A chunk folds n_wait
+// predecessors; fold index q = 0 is the farthest (slot + n_wait dir) and, if
+// q.has_inc, contributes its inclusive state (the `inc` array), the others
+// their aggregates (the `agg` array); q = n_wait - 1 is the nearest (slot +
+// dir).  That is time order for the forward (dir = -1) and reverse time
+// order for the adjoint (dir = +1).  The batch holds fold indices b0 .. b0 +
+// nb - 1, index q at s_stage + (q - b0) * slot_sz.  Its slots are
+// consecutive, so each array is read through one descriptor.
+__device__ __forceinline__ void stage_payloads(float *s_stage, const WsPtrs &ws, int64_t slot, int dir,
+                                               const LbPos &lq, int b0, int nb, int slot_sz) {
     const int tid = threadIdx.x, nt = blockDim.x;
-    int first = b0;
-    if (b0 == 0) {
-        const rsrc_t r = make_rows(ws.inc + (row0 + j0) * slot_sz, (int64_t)slot_sz * 4);
-        for (int e = tid * 4; e < slot_sz; e += nt * 4) {
-            float q[4];
-            carry_load_vec<4>(q, r, 4u * (uint32_t)e);
-            *reinterpret_cast<f32x4 *>(s_stage + e) = f32x4{q[0], q[1], q[2], q[3]};
-        }
-        first = 1;
-    }
-    const int last = b0 + nb - 1;
-    const int na = last - first + 1;  // transforms in this batch
-    if (na > 0) {
-        const int lo = dir > 0 ? j0 + first : j0 - last;  // lowest slot of the batch
-        const rsrc_t r = make_rows(ws.agg + (row0 + lo) * slot_sz, (int64_t)na * slot_sz * 4);
-        for (int e = tid * 4; e < na * slot_sz; e += nt * 4) {
-            const int a = e / slot_sz, off = e - a * slot_sz;  // slot lo + a
-            const int q = dir > 0 ? first + a : last - a;      // its fold index
-            float v[4];
-            carry_load_vec<4>(v, r, 4u * (uint32_t)e);
-            *reinterpret_cast<f32x4 *>(s_stage + (q - b0) * slot_sz + off) = f32x4{v[0], v[1], v[2], v[3]};
-        }
+    const int n_wait = lq.n_wait;
+    const int64_t lo = dir < 0 ? slot - n_wait + b0 : slot + n_wait - (b0 + nb - 1);  // lowest slot
+    const rsrc_t ra = make_rows(ws.agg + lo * slot_sz, (int64_t)nb * slot_sz * 4);
+    const rsrc_t ri = make_rows(ws.inc + lo * slot_sz, (int64_t)nb * slot_sz * 4);
+    for (int e = tid * 4; e < nb * slot_sz; e += nt * 4) {
+        const int a = e / slot_sz, off = e - a * slot_sz;  // slot lo + a
+        const int q = dir < 0 ? b0 + a : b0 + nb - 1 - a;   // its fold index
+        float v[4];
+        carry_load_vec<4>(v, (q == 0 && lq.has_inc) ? ri : ra, 4u * (uint32_t)e);
+        *reinterpret_cast<f32x4 *>(s_stage + (q - b0) * slot_sz + off) = f32x4{v[0], v[1], v[2], v[3]};
     }
 }
 
@@ -479,7 +471,6 @@ __global__ __launch_bounds__(512) void affine_fwd_kernel(FwdArgs p) {
     float *s_X = s_A + (CHW * HPW * AS + 3) / 4 * 4;  // [NW][HPW][bs]: wave transforms (16-byte aligned)
     float *s_S = s_X + NW * HPW * bs;       // [HH][bs]: state entering the chunk, per head
     float *s_stage = s_S + HH * bs;         // [DB][HH * blk]: predecessor payloads
-    __shared__ int s_dist;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -561,22 +552,25 @@ __global__ __launch_bounds__(512) void affine_fwd_kernel(FwdArgs p) {
         lds_barrier();
     }
 
-    // 4. Look-back and publication.  Wave 0 finds how far back the nearest
-    //    inclusive state is; the workgroup stages that state and the
-    //    transforms after it in LDS, a batch per round trip; wave 0 folds them
-    //    and publishes.  The chunk transform of head hh is the prefix through
-    //    its last piece.
+    // 4. Look-back and publication (windowed look-back, common.hpp).  Wave 0
+    //    publishes the chunk's transform and waits for the chunk's look-back
+    //    window; the workgroup stages the window's payloads in LDS, a batch
+    //    per round trip; wave 0 folds them in time order onto the initial
+    //    state (or the inclusive state of chunk - W) and publishes the
+    //    chunk's inclusive state.  The chunk transform of head hh is the
+    //    prefix through its last piece.
     const float *s_C = piece(E - 1);
     const int slot_sz = HH * blk;
     const int hoff = hh * blk;
     const int64_t slot = (int64_t)grp * p.n_chunks + chunk;
+    const LbPos lq = lb_pos(chunk, p.lb_window);
     float S[KP][CPL];
 #pragma unroll
     for (int i = 0; i < KP; ++i)
 #pragma unroll
         for (int cc = 0; cc < CPL; ++cc) S[i][cc] = (cl.kind[cc] == C_ABAR && i == cl.col[cc]) ? 1.f : 0.f;
     if constexpr (H0) {
-        if (chunk == 0 && p.H0 != nullptr && active) {  // H columns of the state: H0
+        if (!lq.has_inc && p.H0 != nullptr && active) {  // H columns of the initial state: H0
 #pragma unroll
             for (int i = 0; i < KP; ++i)
 #pragma unroll
@@ -587,30 +581,28 @@ __global__ __launch_bounds__(512) void affine_fwd_kernel(FwdArgs p) {
     }
     // Every segment's lanes of a head hold the same look-back values (same
     // loads, same operations) and store them to the same addresses.
-    if (chunk > 0) {
-        if (wave == 0) {
-            if (slot_lane) {
-                float C[KP][CPL];
-                get_cols<KP, CPL>(C, s_C, NCP, c0);
-                payload_store<KP, CPL>(p.ws.agg + slot * slot_sz + hoff, NCP, c0, C);
-            }
-            const int dist = wait_ready(p.ws.flags, slot - 1, -1, chunk, p.ws.hdr + 1, p.ws.flags + slot, FLAG_AGG);
-            if (lane == 0) s_dist = dist;
+    if (wave == 0) {
+        if (slot_lane) {
+            float C[KP][CPL];
+            get_cols<KP, CPL>(C, s_C, NCP, c0);
+            payload_store<KP, CPL>(p.ws.agg + slot * slot_sz + hoff, NCP, c0, C);
         }
+        wait_window(p.ws.flags, slot, -1, lq, p.ws.hdr + 1, p.ws.flags + slot);
+    }
+    if (lq.n_wait > 0) {
         lds_barrier();
-        // slot j0 holds an inclusive state; chunks j0+1 .. chunk-1 hold transforms
-        const int nfold = (int)__builtin_amdgcn_readfirstlane(s_dist) + 1;
-        const int j0 = chunk - nfold;
-        for (int b0 = 0; b0 < nfold; b0 += p.DB) {
-            const int nb = nfold - b0 < p.DB ? nfold - b0 : p.DB;
-            stage_payloads(s_stage, p.ws, (int64_t)grp * p.n_chunks, j0, +1, b0, nb, slot_sz);
+        for (int b0 = 0; b0 < lq.n_wait; b0 += p.DB) {
+            const int nb = lq.n_wait - b0 < p.DB ? lq.n_wait - b0 : p.DB;
+            stage_payloads(s_stage, p.ws, slot, -1, lq, b0, nb, slot_sz);
             lds_barrier();
             if (wave == 0) {
-                if (b0 == 0) get_cols<KP, CPL>(S, s_stage + hoff, NCP, c0);
-                for (int q = b0 == 0 ? 1 : b0; q < b0 + nb; ++q)
-                    block_apply<KP, CPL>(S, s_stage + (q - b0) * slot_sz + hoff, NCP, k, c0, is_h);
+                for (int q = b0; q < b0 + nb; ++q) {
+                    const float *blk_q = s_stage + (q - b0) * slot_sz + hoff;
+                    if (q == 0 && lq.has_inc) get_cols<KP, CPL>(S, blk_q, NCP, c0);  // chunk - W's state
+                    else block_apply<KP, CPL>(S, blk_q, NCP, k, c0, is_h);
+                }
             }
-            if (b0 + p.DB < nfold) lds_barrier();  // the next batch overwrites the stage
+            if (b0 + p.DB < lq.n_wait) lds_barrier();  // the next batch overwrites the stage
         }
     }
     if (wave == 0) {
@@ -831,7 +823,6 @@ __global__ __launch_bounds__(512) void affine_bwd_kernel(BwdArgs p) {
     float *s_X = s_A + (CH * HPW * AS + 3) / 4 * 4;     // [NW][HPW][bs]: wave transforms / suffixes
     float *s_S = s_X + NW * HPW * bs;                   // [HPW][bs]: Y entering the chunk from later
     float *s_part = s_S + HPW * bs;                     // [NW][pw]; first the look-back's payload stage
-    __shared__ int s_dist;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -905,51 +896,52 @@ __global__ __launch_bounds__(512) void affine_bwd_kernel(BwdArgs p) {
         lds_barrier();
     }
 
-    // 4. Look-back over later chunks: Y entering the chunk from later time
-    //    (zero after the last chunk), then Y at the chunk's first step.  Wave 0
-    //    finds the nearest published state; the workgroup stages it and the
-    //    transforms before it in LDS (in the dA buffer, idle until step 5), a
-    //    batch per round trip; wave 0 folds them and publishes.
+    // 4. Look-back over later chunks (windowed look-back, common.hpp): Y
+    //    entering the chunk from later time (zero after the last chunk), then
+    //    Y at the chunk's first step.  Wave 0 publishes the chunk's reverse
+    //    transform and waits for the chunk's look-back window; the workgroup
+    //    stages the window's payloads in LDS (in the dA buffer, idle until
+    //    step 5), a batch per round trip; wave 0 folds them in reverse time
+    //    order onto zero (or the state of chunk + W) and publishes the state
+    //    at the chunk's first step.
     const int slot_sz = HPW * blk;
     const int hoff = hsc * blk;
     const int64_t slot = (int64_t)grp * p.n_chunks + chunk;
-    const int last = p.n_chunks - 1;
+    const LbPos lq = lb_pos(rchunk, p.lb_window);
     float S[KP][CPL];
 #pragma unroll
     for (int i = 0; i < KP; ++i)
 #pragma unroll
         for (int cc = 0; cc < CPL; ++cc) S[i][cc] = 0.f;
-    if (chunk < last) {
-        if (wave == 0) {
-            if (slot_lane) {
-                float Z[KP][CPL];
-                get_cols<KP, CPL>(Z, s_X + hs * bs, NCP, c0);
-                payload_store<KP, CPL>(p.ws.agg + slot * slot_sz + hoff, NCP, c0, Z);
-            }
-            const int dist = wait_ready(p.ws.flags, slot + 1, +1, last - chunk, p.ws.hdr + 1, p.ws.flags + slot,
-                                        FLAG_AGG);
-            if (lane == 0) s_dist = dist;
+    if (wave == 0) {
+        if (slot_lane) {
+            float Z[KP][CPL];
+            get_cols<KP, CPL>(Z, s_X + hs * bs, NCP, c0);
+            payload_store<KP, CPL>(p.ws.agg + slot * slot_sz + hoff, NCP, c0, Z);
         }
+        wait_window(p.ws.flags, slot, +1, lq, p.ws.hdr + 1, p.ws.flags + slot);
+    }
+    if (lq.n_wait > 0) {
         lds_barrier();
-        // slot j0 holds a state; chunks j0-1 .. chunk+1 hold transforms
-        const int nfold = (int)__builtin_amdgcn_readfirstlane(s_dist) + 1;
-        const int j0 = chunk + nfold;
-        for (int b0 = 0; b0 < nfold; b0 += p.DB) {
-            const int nb = nfold - b0 < p.DB ? nfold - b0 : p.DB;
-            stage_payloads(s_part, p.ws, (int64_t)grp * p.n_chunks, j0, -1, b0, nb, slot_sz);
+        for (int b0 = 0; b0 < lq.n_wait; b0 += p.DB) {
+            const int nb = lq.n_wait - b0 < p.DB ? lq.n_wait - b0 : p.DB;
+            stage_payloads(s_part, p.ws, slot, +1, lq, b0, nb, slot_sz);
             lds_barrier();
             if (wave == 0) {
-                if (b0 == 0) {
-                    get_cols<KP, CPL>(S, s_part + hoff, NCP, c0);
+                for (int q = b0; q < b0 + nb; ++q) {
+                    const float *blk_q = s_part + (q - b0) * slot_sz + hoff;
+                    if (q == 0 && lq.has_inc) {  // the state of chunk + W (its Y columns)
+                        get_cols<KP, CPL>(S, blk_q, NCP, c0);
 #pragma unroll
-                    for (int i = 0; i < KP; ++i)
+                        for (int i = 0; i < KP; ++i)
 #pragma unroll
-                        for (int cc = 0; cc < CPL; ++cc) S[i][cc] = is_y[cc] ? S[i][cc] : 0.f;
+                            for (int cc = 0; cc < CPL; ++cc) S[i][cc] = is_y[cc] ? S[i][cc] : 0.f;
+                    } else {
+                        block_apply<KP, CPL>(S, blk_q, NCP, k, c0, is_y);
+                    }
                 }
-                for (int q = b0 == 0 ? 1 : b0; q < b0 + nb; ++q)
-                    block_apply<KP, CPL>(S, s_part + (q - b0) * slot_sz + hoff, NCP, k, c0, is_y);
             }
-            if (b0 + p.DB < nfold) lds_barrier();  // the next batch overwrites the stage
+            if (b0 + p.DB < lq.n_wait) lds_barrier();  // the next batch overwrites the stage
         }
     }
     if (wave == 0) {
@@ -1316,6 +1308,7 @@ mi_status launch_affine_fwd(const void *A, const void *Bm, void *Abar, void *Bba
     a.T = T; a.heads = B * n; a.n = (int)n; a.k = (int)k; a.v = (int)v;
     a.G = pl.G; a.HPW = pl.HPW; a.NCP = pl.NCP; a.n_groups = pl.n_groups;
     a.n_chunks = pl.n_chunks; a.NW = pl.NW; a.HH = pl.HH; a.DB = pl.DB;
+    a.lb_window = lb_window(pl.n_groups);
     a.ws = ws_ptrs(ws, lay);
     mi_status st = clear_workspace(a.ws, pl.n_slots, s);
     if (st != MI_OK) return st;
@@ -1341,6 +1334,7 @@ mi_status launch_affine_bwd(const void *A, const void *Abar, const void *Bbar,
     a.T = T; a.heads = B * n; a.n = (int)n; a.k = (int)k; a.v = (int)v;
     a.G = pl.G; a.HPW = pl.HPW; a.NCP = pl.NCP; a.n_groups = pl.n_groups;
     a.n_chunks = pl.n_chunks; a.NW = pl.NW; a.HH = pl.HH; a.DB = pl.DB;
+    a.lb_window = lb_window(pl.n_groups);
     a.ws = ws_ptrs(ws, lay);
     mi_status st = clear_workspace(a.ws, pl.n_slots, s);
     if (st != MI_OK) return st;

@@ -194,36 +194,76 @@ __device__ __forceinline__ typename Pack<T, VEC>::raw_t splat(float x) {
 }
 
 // ---------------------------------------------------------------------------
-// Cross-workgroup carry protocol.
+// Cross-workgroup carry protocol: a windowed look-back with a fixed
+// association, so that every run rounds identically.
 //
-// Work items (a channel tile x a time chunk) take a ticket from a global
-// counter when they start, and the ticket -- not blockIdx -- decides which
-// chunk they scan.  Tickets are handed out chunk-major in scan order, so an
-// item only ever waits on items that already hold a ticket and are running:
-// forward progress does not depend on the hardware's dispatch order.
+// Work items (a channel tile or head group x a time chunk) take a ticket from
+// a global counter when they start, and the ticket -- not blockIdx -- decides
+// which chunk they scan.  Tickets are handed out chunk-major in scan order, so
+// an item only ever waits on items that already hold a ticket and are
+// running: forward progress does not depend on the hardware's dispatch order.
 //
-// Each item publishes, per channel, first its local aggregate (flag AGG),
-// then its inclusive prefix (flag INC).  A successor walks back over its
-// predecessors' slots, folding aggregates until it meets an inclusive prefix
-// (decoupled look-back).
+// The chunks of one tile are numbered in scan order ord = 0, 1, ... (time
+// order for a forward scan, reverse time for an adjoint).  Every chunk
+// publishes two payloads in its slot: first its aggregate (the transform of
+// its own rows), before it waits for anything, then its inclusive state.
+// Chunk ord takes as its carry-in
+//     the inclusive state of chunk ord - W (the scan's initial state if
+//     ord < W), followed by the aggregates of the chunks after it, up to
+//     ord - 1, applied in time order,
+// with W a power of two that the host derives from the shape alone.  That
+// expression depends on ord alone, never on which predecessor happened to
+// publish first, so results are bitwise reproducible.  The inclusive states
+// form W interleaved chains along time, each link W chunks long: the chunk a
+// link waits for started W chunk rows earlier, so it has usually published.
 //
 // Visibility across the XCDs (each has its own L2) uses device-scope memory
 // operations only, never cache maintenance: payload words and flags are
 // written and read with agent-scope relaxed atomics, which gfx950 performs at
 // the device coherence point (the sc1 bit).  The writer waits until its
 // payload stores are acknowledged (s_waitcnt vmcnt(0)) before it stores the
-// flag; the reader's payload loads are issued only after its flag load has
-// returned a non-empty value (the branch on that value waits for it).  An
-// agent-scope release/acquire pair would add an L2 writeback on every publish
-// and an L2 invalidate on every poll, which the streaming kernels around it
-// cannot afford.
+// flag; the reader's payload loads are issued only after its flag loads have
+// returned (the branch on their values waits for them).  An agent-scope
+// release/acquire pair would add an L2 writeback on every publish and an L2
+// invalidate on every poll, which the streaming kernels around it cannot
+// afford.
 // ---------------------------------------------------------------------------
 enum : uint32_t { FLAG_EMPTY = 0, FLAG_AGG = 1, FLAG_INC = 2 };
 
-// About 2^22 polls of >= 64 cycles each (~0.1 s): only a broken protocol gets
-// here.  The wait then gives up, counts the event in the workspace header and
-// lets the kernel finish, so a bug shows up as a wrong result plus a non-zero
-// counter instead of a hung GPU.
+// Position of a chunk in the look-back.
+struct LbPos {
+    int n_wait;    // predecessors folded: min(ord, W)
+    bool has_inc;  // the farthest of them (ord - W) contributes its inclusive state
+};
+__host__ __device__ inline LbPos lb_pos(int ord, int W) {
+    LbPos q;
+    q.has_inc = ord >= W;
+    q.n_wait = q.has_inc ? W : ord;
+    return q;
+}
+
+// Window from the shape: about RESIDENT work items run at once, i.e.
+// RESIDENT / tiles consecutive chunks of every tile.  A power of two in
+// [2, 16].  It depends on the shape only, so equal shapes always fold in the
+// same order.
+#ifndef MISCAN_LB_RESIDENT
+#define MISCAN_LB_RESIDENT 256
+#endif
+#ifndef MISCAN_LB_WMAX
+#define MISCAN_LB_WMAX 16
+#endif
+inline int lb_window(int64_t tiles, int64_t resident = MISCAN_LB_RESIDENT) {
+    const int64_t want = tiles > 0 ? (resident + tiles - 1) / tiles : 1;
+    int W = 2;
+    while (W < want && W < MISCAN_LB_WMAX) W *= 2;
+    return W;
+}
+
+// About 2^22 polls, each a device-coherent load (a round trip to the memory
+// side, about a microsecond under load) plus a short sleep: seconds, so only a
+// broken protocol gets here.  The wait then gives up, counts the event in the
+// workspace header and lets the kernel finish, so a bug shows up as a wrong
+// result plus a non-zero counter instead of a hung GPU.
 constexpr uint32_t SPIN_LIMIT = 1u << 22;
 
 __device__ __forceinline__ uint32_t take_ticket(uint32_t *ctr) {
@@ -236,17 +276,6 @@ __device__ __forceinline__ void carry_store(float *p, float v) {
 }
 __device__ __forceinline__ float carry_load(const float *p) {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-template <int N>
-__device__ __forceinline__ void carry_store_n(float *dst, const float *src) {
-#pragma unroll
-    for (int i = 0; i < N; ++i) carry_store(dst + i, src[i]);
-}
-template <int N>
-__device__ __forceinline__ void carry_load_n(float *dst, const float *src) {
-#pragma unroll
-    for (int i = 0; i < N; ++i) dst[i] = carry_load(src + i);
 }
 
 // Vector form of carry_load for N = 1, 2 or 4 consecutive floats at byte
@@ -268,57 +297,48 @@ __device__ __forceinline__ void carry_load_vec(float *dst, __amdgpu_buffer_rsrc_
     }
 }
 
+// One payload word at byte offset voff + soff of a buffer resource, with the
+// device-coherent policy of carry_load (soff wave-uniform).
+__device__ __forceinline__ float carry_load_buf(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, CPOL_SC1));
+}
+
 // Store the flag once this lane's earlier payload stores are acknowledged.
 __device__ __forceinline__ void publish_flag(uint32_t *flag, uint32_t v) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __hip_atomic_store(flag, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Wave-cooperative look-back wait.  Predecessor d (d = 0 is the nearest) owns
-// slot slot0 + dir*d, for d < n_pred; the farthest predecessor always
-// publishes an inclusive prefix without waiting on anyone.  Lane l polls
-// predecessor base + l, so one coalesced load reads 64 flags.  Returns the
-// distance k of the nearest predecessor whose inclusive prefix is published
-// with every nearer one at least aggregate-ready: the caller then folds
-// aggregates 0..k-1 and the inclusive prefix k.
-//
-// If `pending` is non-null the caller's own flag is stored (value
-// `pending_val`) right after the first poll returns: the wait for the
-// caller's payload acknowledgements then overlaps that first round trip.
-// Every lane of the wave must call this.
-__device__ __forceinline__ int wait_ready(const uint32_t *flags, int64_t slot0, int dir, int n_pred,
-                                          uint32_t *timeouts, uint32_t *pending = nullptr,
-                                          uint32_t pending_val = 0) {
+// Wave-cooperative wait for a chunk's look-back window: the n_wait (<= 64)
+// slots slot + dir, ..., slot + n_wait dir must have published their
+// aggregate, and the farthest one its inclusive state if q.has_inc.  Lane d
+// polls slot + (d + 1) dir, so one coalesced load reads every flag.  If `own`
+// is non-null the caller's aggregate flag is stored right after the first
+// poll returns: the wait for the caller's payload acknowledgements then
+// overlaps that first round trip.  Every lane of the wave must call this.
+__device__ __forceinline__ void wait_window(const uint32_t *flags, int64_t slot, int dir, const LbPos &q,
+                                            uint32_t *timeouts, uint32_t *own) {
     const int lane = threadIdx.x & 63;
-    int base = 0;
+    const bool valid = lane < q.n_wait;
+    const uint32_t need = (q.has_inc && lane == q.n_wait - 1) ? FLAG_INC : FLAG_AGG;
+    const uint32_t *f_lane = flags + slot + (int64_t)dir * (lane + 1);
     uint32_t spins = 0;
     while (true) {
-        const int d = base + lane;
-        const bool valid = d < n_pred;
-        uint32_t f = FLAG_EMPTY;
-        if (valid)
-            f = __hip_atomic_load(flags + slot0 + (int64_t)dir * d, __ATOMIC_RELAXED,
-                                  __HIP_MEMORY_SCOPE_AGENT);
-        const uint64_t incm = __ballot(valid && f == FLAG_INC);
-        const uint64_t empm = __ballot(valid && f == FLAG_EMPTY);
-        if (pending) {
-            publish_flag(pending, pending_val);
-            pending = nullptr;
+        uint32_t f = FLAG_INC;
+        if (valid) f = __hip_atomic_load(f_lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const uint64_t empty = __ballot(f < need);
+        if (own) {
+            publish_flag(own, FLAG_AGG);
+            own = nullptr;
         }
-        const int first_inc = incm ? __builtin_ctzll(incm) : 64;
-        const int first_emp = empm ? __builtin_ctzll(empm) : 64;
-        if (first_inc < first_emp) {
+        if (empty == 0) {
             asm volatile("" ::: "memory");  // payload loads stay after the flag loads
-            return base + first_inc;
-        }
-        if (first_emp == 64 && base + 64 < n_pred) {  // whole window ready, none inclusive
-            base += 64;
-            continue;
+            return;
         }
         __builtin_amdgcn_s_sleep(1);
         if (++spins >= SPIN_LIMIT) {
             if (lane == 0) __hip_atomic_fetch_add(timeouts, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            return n_pred - 1;
+            return;
         }
     }
 }
@@ -328,7 +348,7 @@ __device__ __forceinline__ int wait_ready(const uint32_t *flags, int64_t slot0, 
 //   [0, 256)                 header: u32 ticket counter, u32 timeout counter
 //   [256, 256 + F)           u32 flag per slot, F rounded up to 256
 //   [.., + P)                fp32 aggregate payload, `payload` floats per slot
-//   [.., + P)                fp32 inclusive-prefix payload, same size
+//   [.., + P)                fp32 inclusive-state payload, same size
 // ---------------------------------------------------------------------------
 constexpr size_t WS_HEADER = 256;
 
@@ -339,7 +359,7 @@ struct WsLayout {
     __host__ WsLayout(size_t n_slots, size_t payload_floats) {
         flags_off = WS_HEADER;
         agg_off = flags_off + round_up(n_slots * sizeof(uint32_t), 256);
-        size_t pbytes = round_up(n_slots * payload_floats * sizeof(float), 256);
+        const size_t pbytes = round_up(n_slots * payload_floats * sizeof(float), 256);
         inc_off = agg_off + pbytes;
         total = inc_off + pbytes;
     }
@@ -348,8 +368,8 @@ struct WsLayout {
 struct WsPtrs {
     uint32_t *hdr;    // [0] ticket, [1] timeouts
     uint32_t *flags;  // one per slot
-    float *agg;
-    float *inc;
+    float *agg;       // per slot: the chunk's aggregate
+    float *inc;       // per slot: the inclusive state after the chunk
 };
 
 inline WsPtrs ws_ptrs(void *ws, const WsLayout &l) {
@@ -366,23 +386,6 @@ inline WsPtrs ws_ptrs(void *ws, const WsLayout &l) {
 // (a plain kernel rather than a memset node, so the pair stays capturable).
 mi_status clear_workspace(const WsPtrs &w, size_t n_slots, hipStream_t stream);
 
-// Workgroups of a persistent kernel: as many as can be resident on the
-// current device at once (they loop over tickets), never more than the work
-// items.  Residency changes nothing for correctness -- a workgroup that is not
-// yet running holds no ticket -- it only sizes the loop.
-inline size_t persistent_grid(const void *kernel, int block, size_t n_items) {
-    int dev = 0, n_cu = 0, per_cu = 0;
-    if (hipGetDevice(&dev) != hipSuccess ||
-        hipDeviceGetAttribute(&n_cu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, block, 0) != hipSuccess ||
-        n_cu <= 0 || per_cu <= 0) {
-        n_cu = 256;
-        per_cu = 1;
-    }
-    const size_t cap = (size_t)n_cu * (size_t)per_cu;
-    return n_items < cap ? n_items : cap;
-}
-
 inline mi_status launch_status() {
     hipError_t e = hipGetLastError();
     return e == hipSuccess ? MI_OK : MI_ERR_LAUNCH;
@@ -392,156 +395,110 @@ inline mi_status launch_status() {
 // Workgroup-wide look-back for the channel scans.  A work item is a tile of
 // TILE channels x one time chunk, run by NT threads.  Thread t owns channels
 // t, t + NT, ... (< TILE); `c` holds this chunk's aggregate for them and `in`
-// enters as the state before the first chunk (the identity unless the scan
-// starts from a given state) and leaves as the carry-in of this chunk.
+// enters as the scan's initial state (the identity unless the scan starts
+// from a given state) and leaves as the carry-in of this chunk.
 //
 //  1. every thread stores its channels' aggregate (component-major payload,
-//     so the stores and the loads below coalesce);
-//  2. wave 0 finds the nearest predecessor with a published inclusive prefix
-//     (wait_ready), publishing this chunk's aggregate flag on the way;
-//  3. every thread folds the k aggregates and the inclusive prefix of its
-//     channels, issuing up to BATCH predecessors' loads at a time -- so the walk
-//     costs one round trip per BATCH predecessors rather than one each.  When
-//     the workgroup has G >= 2 threads per channel, G groups fold disjoint
-//     runs of predecessors at once and combine their partials through LDS;
-//  4. every thread stores its channels' inclusive prefix in (+) c.
-// The caller then stages `in` in LDS and calls wg_publish_inc.
+//     so the stores and the loads below coalesce); wave 0 publishes it;
+//  2. wave 0 waits for the chunk's look-back window (wait_window);
+//  3. every thread folds, in time order, the inclusive state of chunk
+//     ord - W (which replaces `in`) or, for ord < W, nothing, then the
+//     aggregates of the window, issuing up to BATCH predecessors' loads at a
+//     time: one round trip per BATCH payloads;
+//  4. every thread stores its channels' inclusive state in (+) c; the caller
+//     then stages `in` in LDS and calls wg_publish.
 //
 // Op describes the carry algebra: NC floats per channel, and
 // then(r, x, y): r = x followed by y (x is applied to the state first).
 // ---------------------------------------------------------------------------
 template <class Op, int TILE, int NT, int BATCH = 8>
-__device__ __forceinline__ void wg_lookback(const WsPtrs &ws, int64_t slot, int dir, int n_pred,
+__device__ __forceinline__ void wg_lookback(const WsPtrs &ws, int64_t slot, int dir, const LbPos &q,
                                             const float (&c)[(TILE + NT - 1) / NT][Op::NC],
-                                            float (&in)[(TILE + NT - 1) / NT][Op::NC], int *s_k) {
+                                            float (&in)[(TILE + NT - 1) / NT][Op::NC]) {
     constexpr int NC = Op::NC, CPT = (TILE + NT - 1) / NT;
-    constexpr int G = NT >= 2 * TILE ? NT / TILE : 1;  // predecessor-folding groups
     const int tid = threadIdx.x;
     const int64_t pay = (int64_t)NC * TILE;  // payload floats per slot
-    if (n_pred > 0) {
 #pragma unroll
-        for (int q = 0; q < CPT; ++q) {
-            const int ch = tid + q * NT;
-            if (ch < TILE)
+    for (int u = 0; u < CPT; ++u) {
+        const int ch = tid + u * NT;
+        if (ch < TILE)
 #pragma unroll
-                for (int m = 0; m < NC; ++m) carry_store(ws.agg + slot * pay + m * TILE + ch, c[q][m]);
-        }
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // every wave's aggregate is acknowledged
-        lds_barrier();
-        if (tid < 64) {
-            const int k = wait_ready(ws.flags, slot + dir, dir, n_pred, ws.hdr + 1, ws.flags + slot, FLAG_AGG);
-            if (tid == 0) *s_k = k;
-        }
-        lds_barrier();
-        const int k = *s_k;
-        if constexpr (G == 1) {
-            for (int j0 = 0; j0 <= k; j0 += BATCH) {
-                float x[BATCH][CPT][NC];
+            for (int m = 0; m < NC; ++m) carry_store(ws.agg + slot * pay + m * TILE + ch, c[u][m]);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // every wave's aggregate is acknowledged
+    lds_barrier();
+    if (tid < 64) wait_window(ws.flags, slot, dir, q, ws.hdr + 1, ws.flags + slot);
+    if (q.n_wait == 0) return;  // wave 0 has published; no carry to fold
+    lds_barrier();
+    // Fold index j = 0 is the farthest predecessor (slot + n_wait dir), j =
+    // n_wait - 1 the nearest.  The predecessors' slots are consecutive: one
+    // descriptor per payload array covers them, each lane keeps one offset
+    // (its channel) and each predecessor and component is a wave-uniform
+    // offset.
+    const int64_t lo = dir < 0 ? slot - q.n_wait : slot + 1;  // lowest slot of the window
+    const rsrc_t ra = make_rows(ws.agg + lo * pay, (int64_t)q.n_wait * pay * 4);
+    const rsrc_t ri = make_rows(ws.inc + lo * pay, (int64_t)q.n_wait * pay * 4);
+    for (int j0 = 0; j0 < q.n_wait; j0 += BATCH) {
+        float x[BATCH][CPT][NC];
 #pragma unroll
-                for (int u = 0; u < BATCH; ++u) {
-                    const int j = j0 + u;
-                    if (j <= k) {
-                        const float *src = (j == k ? ws.inc : ws.agg) + (slot + (int64_t)dir * (j + 1)) * pay;
+        for (int u = 0; u < BATCH; ++u) {
+            const int j = j0 + u;
+            if (j < q.n_wait) {
+                const int a = dir < 0 ? j : q.n_wait - 1 - j;  // slot lo + a
+                const bool from_inc = j == 0 && q.has_inc;
 #pragma unroll
-                        for (int q = 0; q < CPT; ++q) {
-                            const int ch = tid + q * NT;
+                for (int v = 0; v < CPT; ++v) {
+                    const int ch = tid + v * NT;
+                    const uint32_t voff = 4u * (uint32_t)(ch < TILE ? ch : 0);
 #pragma unroll
-                            for (int m = 0; m < NC; ++m)
-                                x[u][q][m] = ch < TILE ? carry_load(src + m * TILE + ch) : 0.f;
-                        }
-                    }
-                }
-#pragma unroll
-                for (int u = 0; u < BATCH; ++u) {
-                    if (j0 + u <= k) {
-#pragma unroll
-                        for (int q = 0; q < CPT; ++q) {
-                            float r[NC];
-                            Op::then(r, x[u][q], in[q]);  // predecessor j comes before all folded so far
-#pragma unroll
-                            for (int m = 0; m < NC; ++m) in[q][m] = r[m];
-                        }
-                    }
+                    for (int m = 0; m < NC; ++m)
+                        x[u][v][m] = carry_load_buf(from_inc ? ri : ra, voff, 4u * (uint32_t)(a * pay + m * TILE));
                 }
             }
-        } else {
-            // G groups of TILE threads (CPT == 1).  Group g folds predecessors
-            // [g * per, (g + 1) * per) into a partial transform, nearest
-            // first; group 0 then applies the partials of the later groups,
-            // which lie further back in time.
-            __shared__ float s_part[G - 1][NC][TILE];
-            const int grp = tid / TILE, ch = tid - grp * TILE;
-            const int per = (k + 1 + G - 1) / G;
-            const int lo = grp * per;
-            const int hi = lo + per < k + 1 ? lo + per : k + 1;
-            float part[NC];
-            bool have = false;
-            if (grp < G) {
-                for (int j0 = lo; j0 < hi; j0 += BATCH) {
-                    float x[BATCH][NC];
+        }
 #pragma unroll
-                    for (int u = 0; u < BATCH; ++u) {
-                        const int j = j0 + u;
-                        if (j < hi) {
-                            const float *src = (j == k ? ws.inc : ws.agg) + (slot + (int64_t)dir * (j + 1)) * pay;
+        for (int u = 0; u < BATCH; ++u) {
+            const int j = j0 + u;
+            if (j < q.n_wait) {
 #pragma unroll
-                            for (int m = 0; m < NC; ++m) x[u][m] = carry_load(src + m * TILE + ch);
-                        }
+                for (int v = 0; v < CPT; ++v) {
+                    if (j == 0 && q.has_inc) {
+#pragma unroll
+                        for (int m = 0; m < NC; ++m) in[v][m] = x[u][v][m];  // chunk ord - W's inclusive state
+                    } else {
+                        float r[NC];
+                        Op::then(r, in[v], x[u][v]);  // the state so far, then predecessor j's rows
+#pragma unroll
+                        for (int m = 0; m < NC; ++m) in[v][m] = r[m];
                     }
-#pragma unroll
-                    for (int u = 0; u < BATCH; ++u) {
-                        if (j0 + u < hi) {
-                            if (!have) {
-#pragma unroll
-                                for (int m = 0; m < NC; ++m) part[m] = x[u][m];
-                                have = true;
-                            } else {
-                                float r[NC];
-                                Op::then(r, x[u], part);
-#pragma unroll
-                                for (int m = 0; m < NC; ++m) part[m] = r[m];
-                            }
-                        }
-                    }
-                }
-                if (grp > 0 && have)
-#pragma unroll
-                    for (int m = 0; m < NC; ++m) s_part[grp - 1][m][ch] = part[m];
-            }
-            lds_barrier();
-            if (grp == 0) {
-                if (have) {
-                    float r[NC];
-                    Op::then(r, part, in[0]);
-#pragma unroll
-                    for (int m = 0; m < NC; ++m) in[0][m] = r[m];
-                }
-                for (int g = 1; g < G && g * per < k + 1; ++g) {
-                    float x[NC], r[NC];
-#pragma unroll
-                    for (int m = 0; m < NC; ++m) x[m] = s_part[g - 1][m][ch];
-                    Op::then(r, x, in[0]);
-#pragma unroll
-                    for (int m = 0; m < NC; ++m) in[0][m] = r[m];
                 }
             }
         }
     }
+}
+
+// Every chunk stores its inclusive state (in followed by c) for its channels.
+template <class Op, int TILE, int NT>
+__device__ __forceinline__ void wg_store_inclusive(const WsPtrs &ws, int64_t slot,
+                                                   const float (&c)[(TILE + NT - 1) / NT][Op::NC],
+                                                   const float (&in)[(TILE + NT - 1) / NT][Op::NC]) {
+    constexpr int NC = Op::NC, CPT = (TILE + NT - 1) / NT;
+    const int64_t pay = (int64_t)NC * TILE;
 #pragma unroll
-    for (int q = 0; q < CPT; ++q) {
-        const int ch = tid + q * NT;
+    for (int u = 0; u < CPT; ++u) {
+        const int ch = threadIdx.x + u * NT;
         if (ch < TILE) {
             float r[NC];
-            Op::then(r, in[q], c[q]);
+            Op::then(r, in[u], c[u]);
 #pragma unroll
             for (int m = 0; m < NC; ++m) carry_store(ws.inc + slot * pay + m * TILE + ch, r[m]);
         }
     }
 }
 
-// Publish the chunk's inclusive prefix once every wave's payload stores are
-// acknowledged; the barrier also makes the caller's staged LDS carry visible.
-__device__ __forceinline__ void wg_publish_inc(const WsPtrs &ws, int64_t slot) {
+// The barrier after the caller has staged its carry in LDS; the inclusive
+// state is published once every wave's payload stores are acknowledged.
+__device__ __forceinline__ void wg_publish(const WsPtrs &ws, int64_t slot) {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     lds_barrier();
     if (threadIdx.x < 64)

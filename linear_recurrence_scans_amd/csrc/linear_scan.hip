@@ -31,6 +31,7 @@ struct FwdArgs {
     const void *h0;  // initial state (B, D), used by the H0 kernels; NULL = zero
     int64_t T, D;
     int n_dtiles, n_tiles, n_chunks;
+    int lb_window;  // look-back window W (a power of two)
     WsPtrs ws;
 };
 
@@ -41,6 +42,7 @@ struct BwdArgs {
     void *dh0;       // its gradient (B, D), written by the H0 kernels
     int64_t T, D;
     int n_dtiles, n_tiles, n_chunks;
+    int lb_window;  // look-back window W (a power of two)
     WsPtrs ws;
 };
 
@@ -156,7 +158,6 @@ __global__ __launch_bounds__(NW * 64, 4) void linear_fwd_kernel(FwdArgs p) {
     __shared__ __align__(16) float s_cA[TILE];     // chunk carry-in
     __shared__ __align__(16) float s_cH[TILE];
     __shared__ uint32_t s_ticket;
-    __shared__ int s_k;
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -189,13 +190,17 @@ __global__ __launch_bounds__(NW * 64, 4) void linear_fwd_kernel(FwdArgs p) {
         }
     }
 
-    // 2. Serial scan of the wave's rows from (1, 0): the wave aggregate.
+    // 2. Serial scan of the wave's rows from (1, 0): the wave aggregate.  Each
+    //    row is widened only when its step runs (opaque): widening rows ahead
+    //    of their step kept fp32 copies of several rows live at once and
+    //    spilled 9 VGPRs of the bf16 kernel to scratch.
     float gA[VEC], gH[VEC];
 #pragma unroll
     for (int v = 0; v < VEC; ++v) { gA[v] = 1.f; gH[v] = 0.f; }
 #pragma unroll
     for (int r = 0; r < L; ++r) {
         float fa[VEC], fb[VEC];
+        opaque(ra[r]); opaque(rb[r]);
         PK::unpack(ra[r], fa);
         PK::unpack(rb[r], fb);
 #pragma unroll
@@ -210,6 +215,7 @@ __global__ __launch_bounds__(NW * 64, 4) void linear_fwd_kernel(FwdArgs p) {
 
     // 3. Chunk aggregate per channel (waves in time order), look-back, carry.
     const int64_t slot = (int64_t)it.tile * p.n_chunks + it.chunk;
+    const LbPos lq = lb_pos(it.chunk, p.lb_window);
     {
         float c[CPT][2], in[CPT][2];
 #pragma unroll
@@ -224,22 +230,23 @@ __global__ __launch_bounds__(NW * 64, 4) void linear_fwd_kernel(FwdArgs p) {
                     FwdOp::then(r, c[q], x);
                     c[q][0] = r[0]; c[q][1] = r[1];
                 }
-            if constexpr (H0) {
+            if constexpr (H0) {  // the initial state (1, h0) of the first group's fold
                 const int64_t dch = (int64_t)(it.tile - it.bidx * p.n_dtiles) * TILE + ch;
-                if (it.chunk == 0 && ch < TILE && dch < p.D && p.h0 != nullptr) {
+                if (!lq.has_inc && ch < TILE && dch < p.D && p.h0 != nullptr) {
                     float f0[1];
                     Pack<T, 1>::unpack(load_vec<T, 1>(static_cast<const T *>(p.h0) + (int64_t)it.bidx * p.D + dch), f0);
                     in[q][1] = f0[0];
                 }
             }
         }
-        wg_lookback<FwdOp, TILE, NT>(p.ws, slot, -1, it.chunk, c, in, &s_k);
+        wg_lookback<FwdOp, TILE, NT>(p.ws, slot, -1, lq, c, in);
+        wg_store_inclusive<FwdOp, TILE, NT>(p.ws, slot, c, in);
 #pragma unroll
         for (int q = 0; q < CPT; ++q) {
             const int ch = threadIdx.x + q * NT;
             if (ch < TILE) { s_cA[lds_ch<VEC>(ch)] = in[q][0]; s_cH[lds_ch<VEC>(ch)] = in[q][1]; }
         }
-        wg_publish_inc(p.ws, slot);
+        wg_publish(p.ws, slot);
     }
 
     // 4. Carry into this wave: chunk carry-in, then waves 0..wave-1.
@@ -302,7 +309,6 @@ __global__ __launch_bounds__(NW * 64, 4) void linear_bwd_kernel(BwdArgs p) {
     __shared__ __align__(16) float s_cL[TILE];     // chunk carry-in
     __shared__ __align__(16) float s_cM[TILE];
     __shared__ uint32_t s_ticket;
-    __shared__ int s_k;
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -394,6 +400,7 @@ __global__ __launch_bounds__(NW * 64, 4) void linear_bwd_kernel(BwdArgs p) {
     // 3. Chunk aggregate per channel (waves NW-1 .. 0), look-back over later
     //    chunks, carry.
     const int64_t slot = (int64_t)it.tile * p.n_chunks + it.chunk;
+    const LbPos lq = lb_pos(p.n_chunks - 1 - it.chunk, p.lb_window);
     {
         float c[CPT][3], in[CPT][3];
 #pragma unroll
@@ -410,13 +417,14 @@ __global__ __launch_bounds__(NW * 64, 4) void linear_bwd_kernel(BwdArgs p) {
                     c[q][0] = r[0]; c[q][1] = r[1]; c[q][2] = r[2];
                 }
         }
-        wg_lookback<BwdOp, TILE, NT, 4>(p.ws, slot, +1, p.n_chunks - 1 - it.chunk, c, in, &s_k);
+        wg_lookback<BwdOp, TILE, NT, 4>(p.ws, slot, +1, lq, c, in);
+        wg_store_inclusive<BwdOp, TILE, NT>(p.ws, slot, c, in);
 #pragma unroll
         for (int q = 0; q < CPT; ++q) {
             const int ch = threadIdx.x + q * NT;
             if (ch < TILE) { s_cL[lds_ch<VEC>(ch)] = in[q][1]; s_cM[lds_ch<VEC>(ch)] = in[q][2]; }
         }
-        wg_publish_inc(p.ws, slot);
+        wg_publish(p.ws, slot);
     }
 
     // 4. Adjoint state entering this wave: chunk carry-in, then waves NW-1 .. wave+1.
@@ -554,6 +562,7 @@ mi_status run_fwd(const void *a, const void *b, void *A, void *Bc, int64_t B, in
     FwdArgs p;
     p.a = a; p.b = b; p.A = A; p.Bc = Bc; p.h0 = h0; p.T = T; p.D = D;
     p.n_dtiles = g.n_dtiles; p.n_tiles = g.n_tiles; p.n_chunks = g.n_chunks;
+    p.lb_window = lb_window(g.n_tiles);
     p.ws = ws_ptrs(ws, lay);
     mi_status st = clear_workspace(p.ws, g.n_slots, s);
     if (st != MI_OK) return st;
@@ -574,6 +583,7 @@ mi_status run_bwd(const void *a, const void *A, const void *Bc, const void *gA,
     p.a = a; p.A = A; p.Bc = Bc; p.gA = gA; p.gBc = gBc; p.da = da; p.db = db; p.h0 = h0; p.dh0 = dh0;
     p.T = T; p.D = D;
     p.n_dtiles = g.n_dtiles; p.n_tiles = g.n_tiles; p.n_chunks = g.n_chunks;
+    p.lb_window = lb_window(g.n_tiles);
     p.ws = ws_ptrs(ws, lay);
     mi_status st = clear_workspace(p.ws, g.n_slots, s);
     if (st != MI_OK) return st;

@@ -43,6 +43,7 @@ struct LogArgs {
     void *h;
     int64_t T, D;
     int n_dtiles, n_tiles, n_chunks;
+    int lb_window;  // look-back window W (a power of two)
     WsPtrs ws;
 };
 
@@ -73,7 +74,6 @@ __global__ __launch_bounds__(NW * 64) void log_fwd_kernel(LogArgs p) {
     __shared__ float s_lh[NW][TILE];
     __shared__ float s_c[TILE];
     __shared__ uint32_t s_ticket;
-    __shared__ int s_k;
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -137,9 +137,11 @@ __global__ __launch_bounds__(NW * 64) void log_fwd_kernel(LogArgs p) {
     }
     lds_barrier();
 
-    // 3. Chunk aggregate per channel, look-back, carry.  Before the first
-    //    chunk the state is log h_0 (log_values slot 0).
+    // 3. Chunk aggregate per channel, look-back, carry.  The scan's initial
+    //    state is log h_0 (log_values slot 0): the first look-back group folds
+    //    from it.
     const int64_t slot = (int64_t)tile * p.n_chunks + chunk;
+    const LbPos lq = lb_pos(chunk, p.lb_window);
     {
         float c[CPT][2], in[CPT][2];
         const int64_t d_tile = (int64_t)dtile * TILE;
@@ -155,7 +157,7 @@ __global__ __launch_bounds__(NW * 64) void log_fwd_kernel(LogArgs p) {
                     LogOp::then(r, c[q], x);
                     c[q][0] = r[0]; c[q][1] = r[1];
                 }
-                if (chunk == 0 && d_tile + ch < p.D) {
+                if (!lq.has_inc && d_tile + ch < p.D) {
                     const T *lv0 = static_cast<const T *>(p.lv) + (int64_t)bidx * (p.T + 1) * p.D + d_tile + ch;
                     float f0[1];
                     Pack<T, 1>::unpack(load_vec<T, 1>(lv0), f0);
@@ -163,13 +165,14 @@ __global__ __launch_bounds__(NW * 64) void log_fwd_kernel(LogArgs p) {
                 }
             }
         }
-        wg_lookback<LogOp, TILE, NT, MISCAN_LOG_BATCH>(p.ws, slot, -1, chunk, c, in, &s_k);
+        wg_lookback<LogOp, TILE, NT, MISCAN_LOG_BATCH>(p.ws, slot, -1, lq, c, in);
+        wg_store_inclusive<LogOp, TILE, NT>(p.ws, slot, c, in);
 #pragma unroll
         for (int q = 0; q < CPT; ++q) {
             const int ch = threadIdx.x + q * NT;
             if (ch < TILE) s_c[ch] = in[q][1];
         }
-        wg_publish_inc(p.ws, slot);
+        wg_publish(p.ws, slot);
     }
 
     // 4. State entering this wave: chunk carry-in, then waves 0..wave-1.
@@ -221,6 +224,7 @@ struct LogBwdArgs {
     void *dlc, *dlv;
     int64_t T, D;
     int n_dtiles, n_tiles, n_chunks;
+    int lb_window;  // look-back window W (a power of two)
     WsPtrs ws;
 };
 
@@ -245,7 +249,6 @@ __global__ __launch_bounds__(NW * 64) void log_bwd_kernel(LogBwdArgs p) {
     __shared__ float s_L[NW][TILE];
     __shared__ float s_cL[TILE];
     __shared__ uint32_t s_ticket;
-    __shared__ int s_k;
 
     const int lane = threadIdx.x & 63;
     const int wave = threadIdx.x >> 6;
@@ -334,6 +337,7 @@ __global__ __launch_bounds__(NW * 64) void log_bwd_kernel(LogBwdArgs p) {
 
     // 3. Chunk aggregate (waves NW-1 .. 0), look-back over later chunks, carry.
     const int64_t slot = (int64_t)tile * p.n_chunks + chunk;
+    const LbPos lq = lb_pos(ord, p.lb_window);
     {
         float c[CPT][2], in[CPT][2];
 #pragma unroll
@@ -349,13 +353,14 @@ __global__ __launch_bounds__(NW * 64) void log_bwd_kernel(LogBwdArgs p) {
                     c[q][0] = r[0]; c[q][1] = r[1];
                 }
         }
-        wg_lookback<LogBwdOp, TILE, NT, MISCAN_LOG_BATCH>(p.ws, slot, +1, p.n_chunks - 1 - chunk, c, in, &s_k);
+        wg_lookback<LogBwdOp, TILE, NT, MISCAN_LOG_BATCH>(p.ws, slot, +1, lq, c, in);
+        wg_store_inclusive<LogBwdOp, TILE, NT>(p.ws, slot, c, in);
 #pragma unroll
         for (int q = 0; q < CPT; ++q) {
             const int ch = threadIdx.x + q * NT;
             if (ch < TILE) s_cL[ch] = in[q][1];
         }
-        wg_publish_inc(p.ws, slot);
+        wg_publish(p.ws, slot);
     }
 
     // 4. lam entering this wave: chunk carry-in, then waves NW-1 .. wave+1.
@@ -461,6 +466,7 @@ mi_status run_log_bwd(const void *lc, const void *lv, const void *h, const void 
     WsLayout lay(n_slots, 64 * 2 * VEC);
     if (ws == nullptr || ws_bytes < lay.total) return MI_ERR_WORKSPACE;
     p.lc = lc; p.lv = lv; p.h = h; p.g = g; p.dlc = dlc; p.dlv = dlv; p.T = T; p.D = D;
+    p.lb_window = lb_window(p.n_tiles);
     p.ws = ws_ptrs(ws, lay);
     mi_status st = clear_workspace(p.ws, n_slots, s);
     if (st != MI_OK) return st;
@@ -492,6 +498,7 @@ mi_status run_log(const void *lc, const void *lv, void *h, int64_t B, int64_t T,
     WsLayout lay(n_slots, 64 * 2 * VEC);
     if (ws == nullptr || ws_bytes < lay.total) return MI_ERR_WORKSPACE;
     p.lc = lc; p.lv = lv; p.h = h; p.T = T; p.D = D;
+    p.lb_window = lb_window(p.n_tiles);
     p.ws = ws_ptrs(ws, lay);
     mi_status st = clear_workspace(p.ws, n_slots, s);
     if (st != MI_OK) return st;
