@@ -8,10 +8,19 @@ workloads.py): one linear_scan_fwd followed by one linear_scan_bwd that
 consumes the forward's A and Bc.  Inputs are resident in HBM before the
 timed region starts.
 
-Printed: one JSON line with the whole-job throughput (algorithmic bytes --
-every input read once and every output written once -- per second), the
-roofline of the dominant kernel (HIP events on the stream the kernels run on)
-and the fp64 CPU oracle timed on a bounded sample of the same workload.
+Printed: one JSON line with
+  * value: whole-job throughput (algorithmic bytes -- every input read once
+    and every output written once -- per second) over the K timed steps;
+  * kernels: per kernel, HIP-event times on the stream the kernels run on
+    (mean, median and minimum over the K steps), the same kernel timed cold
+    (median and minimum over --cold-iters launches, each after a 1 GiB write
+    that evicts the L2s and the Infinity Cache), and the streaming ceiling of
+    its access shape (libmiscan_bench.so: the same tiles and accesses with no
+    carry), warm and cold;
+  * roofline: the dominant kernel against the published 8 TB/s and against
+    that ceiling;
+  * cpu_baseline: the fp64 CPU oracle on a bounded sample of the same
+    workload, at all host threads and at one thread, with the CPU model.
 
   python bench.py [--steps K] [--warmup W] [--workload {1..6}] [--no-cpu-baseline]
 """
@@ -28,6 +37,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0  # MI355X published HBM3E bandwidth
+FLUSH_BYTES = 1 << 30  # written before each cold timing: more than the L2s plus the 256 MB Infinity Cache
 METRIC = "scan GB/s and % HBM peak, linear_scan fwd+bwd B=8,T=8192,D=4096"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 CPU_SECONDS = 10.0  # CPU work spent on the oracle baseline
@@ -206,7 +216,21 @@ def build_workload(wid, torch, lrs, workloads, on_device=False, initial_state=Fa
 # CPU baseline: the fp64 oracle, as it stands, on a bounded sample
 # ---------------------------------------------------------------------------
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(wid, torch, workloads, storage=None):
+    """The oracle on a bounded sample of the workload, timed with every host
+    thread it uses and with one thread (each leg runs about CPU_SECONDS, at
+    least once)."""
     import numpy as np
     import oracle
     w = dict(workloads.WORKLOADS[wid])
@@ -266,37 +290,128 @@ def cpu_baseline(wid, torch, workloads, storage=None):
         if wid == 5:
             nbytes += es * (4 * S * k * k + 3 * S * k * v)
         sample = "B=1 of %d batch rows: %d head-steps" % (w["B"], S)
-    # The sample is run repeatedly until about CPU_SECONDS of work is done.
-    reps, t0 = 0, time.perf_counter()
-    while True:
-        run()
-        reps += 1
-        dt = time.perf_counter() - t0
-        if dt >= CPU_SECONDS or reps >= 10000:
-            break
-    return {"value": round(reps * nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": oracle.num_threads(),
-            "kind": "oracle", "sample": "%s; run %d times" % (sample, reps), "seconds": round(dt, 3)}
+
+    def timed(seconds):
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            run()
+            reps += 1
+            dt = time.perf_counter() - t0
+            if dt >= seconds or reps >= 10000:
+                return reps, dt
+
+    threads = oracle.num_threads()
+    reps, dt = timed(CPU_SECONDS)
+    oracle.set_threads(1)
+    reps1, dt1 = timed(CPU_SECONDS)
+    oracle.set_threads(threads)
+    return {"value": round(reps * nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle", "sample": "%s; run %d times" % (sample, reps), "seconds": round(dt, 3),
+            "one_thread": {"value": round(reps1 * nbytes / dt1 / 1e9, 4), "unit": "GB/s", "cores": 1,
+                           "runs": reps1, "seconds": round(dt1, 3)},
+            "cpu_model": cpu_model(), "host_threads": os.cpu_count()}
 
 
 # ---------------------------------------------------------------------------
+# streaming ceiling and cold timing (libmiscan_bench.so)
+# ---------------------------------------------------------------------------
 
-def copy_bandwidth(torch, nbytes=1 << 30, reps=5):
-    """Device-to-device copy rate (GB/s, read + write bytes) on the current
-    stream: the practical streaming ceiling the scans are compared with."""
-    src = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
-    dst = torch.empty_like(src)
-    dst.copy_(src)
-    stream = torch.cuda.current_stream()
-    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+_BENCH_LIB = None
+
+
+def bench_lib():
+    global _BENCH_LIB
+    if _BENCH_LIB is None:
+        import ctypes
+        path = os.path.join(ROOT, "linear_recurrence_scans_amd", "libmiscan_bench.so")
+        if not os.path.exists(path):
+            raise SystemExit("bench.py: %s is not built (python -m linear_recurrence_scans_amd.build)" % path)
+        lib = ctypes.CDLL(path)
+        V, I, I64, SZ = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t
+        lib.mi_bench_stream.argtypes = [ctypes.POINTER(V), I, ctypes.POINTER(V), I, I64, I64, I64, I, V]
+        lib.mi_bench_stream.restype = I
+        lib.mi_bench_flush.argtypes = [V, SZ, V]
+        lib.mi_bench_flush.restype = I
+        _BENCH_LIB = lib
+    return _BENCH_LIB
+
+
+# Streams read and written by each kernel (its algorithmic tensors).
+STREAMS = {"linear_scan_fwd": (2, 2), "linear_scan_bwd": (5, 2), "scan_log_fwd": (2, 1),
+           "scan_log_bwd": (4, 2), "affine_scan_fwd": (2, 2), "affine_scan_bwd": (5, 2)}
+
+
+def stream_shape(name, desc, nbytes):
+    """(n_in, n_out, B, T, D) of the streaming probe for kernel `name`: the
+    channel scans' own (B, T, D); for the k x k scans, equal (1, T', 1024)
+    tensors whose total is the kernel's algorithmic bytes."""
+    nin, nout = STREAMS[name.replace("_h0", "")]
+    es = 2 if desc["storage"] == "bf16" else 4
+    if "D" in desc:
+        return nin, nout, desc["B"], desc["T"], desc["D"]
+    D = 1024
+    rows = max(1, int(round(nbytes / (nin + nout) / es / D)))
+    return nin, nout, 1, rows, D
+
+
+def flush_caches(torch, buf, stream):
+    st = bench_lib().mi_bench_flush(buf.data_ptr(), buf.numel(), stream.cuda_stream)
+    if st != 0:
+        raise RuntimeError("mi_bench_flush failed (%d)" % st)
+
+
+def time_cold(torch, fn, stream, flush, iters):
+    """Median and minimum (ms) of `fn` over `iters` launches, each after the
+    caches were flushed (the flush itself is not timed)."""
+    times = []
+    for _ in range(iters):
+        flush_caches(torch, flush, stream)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        fn()
+        b.record(stream)
+        b.synchronize()
+        times.append(a.elapsed_time(b))
+    times.sort()
+    return times[len(times) // 2], times[0]
+
+
+def stream_ceiling(torch, name, desc, nbytes, stream, flush, reps):
+    """Rate (GB/s) of the streaming probe with kernel `name`'s access shape:
+    warm (median over reps back-to-back launches) and cold (median, each after
+    a flush)."""
+    import ctypes
+    nin, nout, Bn, T, D = stream_shape(name, desc, nbytes)
+    dt = torch.bfloat16 if desc["storage"] == "bf16" else torch.float32
+    ins = [torch.ones(Bn, T, D, dtype=dt, device="cuda") for _ in range(nin)]
+    outs = [torch.empty(Bn, T, D, dtype=dt, device="cuda") for _ in range(nout)]
+    pin = (ctypes.c_void_p * nin)(*[t.data_ptr() for t in ins])
+    pout = (ctypes.c_void_p * nout)(*[t.data_ptr() for t in outs])
+    code = 1 if dt == torch.bfloat16 else 0
+
+    def fn():
+        st = bench_lib().mi_bench_stream(pin, nin, pout, nout, Bn, T, D, code, stream.cuda_stream)
+        if st != 0:
+            raise RuntimeError("mi_bench_stream failed (%d)" % st)
+
+    moved = (nin + nout) * Bn * T * D * ins[0].element_size()
+    for _ in range(3):
+        fn()
     torch.cuda.synchronize()
-    a.record(stream)
+    warm = []
     for _ in range(reps):
-        dst.copy_(src)
-    b.record(stream)
-    torch.cuda.synchronize()
-    ms = a.elapsed_time(b) / reps
-    del src, dst
-    return 2 * nbytes / (ms * 1e-3) / 1e9
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        fn()
+        b.record(stream)
+        b.synchronize()
+        warm.append(a.elapsed_time(b))
+    warm.sort()
+    cold_med, _ = time_cold(torch, fn, stream, flush, reps)
+    del ins, outs
+    return {"shape": "%d reads + %d writes of (%d, %d, %d) %s" % (nin, nout, Bn, T, D, desc["storage"]),
+            "GBps": round(moved / (warm[len(warm) // 2] * 1e-3) / 1e9, 1),
+            "cold_GBps": round(moved / (cold_med * 1e-3) / 1e9, 1)}
 
 
 def traffic_key(kernel_name, desc):
@@ -320,15 +435,20 @@ def stored_traffic(kernel_name, desc):
     return e.get("hbm_bytes_per_launch")
 
 
+def gbps(nbytes, ms):
+    return round(nbytes / (ms * 1e-3) / 1e9, 1)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", type=int, default=3, choices=[1, 2, 3, 4, 5, 6])
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cold", action="store_true",
-                    help="also time each kernel alone after writing 1 GiB to evict the caches")
+    ap.add_argument("--cold-iters", type=int, default=50,
+                    help="cold-cache launches per kernel (each after a 1 GiB write); 0 skips them")
+    ap.add_argument("--no-ceiling", action="store_true", help="skip the streaming-ceiling probe")
     ap.add_argument("--initial-state", action="store_true",
                     help="time the scans from a given initial state (the *_h0 entry points); "
                          "linear and k x k workloads")
@@ -398,26 +518,33 @@ def main():
 
     per_kernel = {}
     for i, (name, _, nbytes) in enumerate(kernels):
-        ms = sum(ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(args.steps)) / args.steps
-        per_kernel[name] = {"avg_ms": round(ms, 4), "bytes": nbytes,
-                            "GB/s": round(nbytes / (ms * 1e-3) / 1e9, 1),
-                            "frac_hbm_peak": round(nbytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        ms = sorted(ev[s][i][0].elapsed_time(ev[s][i][1]) for s in range(args.steps))
+        mean = sum(ms) / len(ms)
+        per_kernel[name] = {"avg_ms": round(mean, 4), "median_ms": round(ms[len(ms) // 2], 4),
+                            "min_ms": round(ms[0], 4), "bytes": nbytes, "GB/s": gbps(nbytes, mean),
+                            "median_GB/s": gbps(nbytes, ms[len(ms) // 2]),
+                            "frac_hbm_peak": round(nbytes / (mean * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
 
-    if args.cold:
-        flush = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
-        for i, (name, fn, nbytes) in enumerate(kernels):
-            times = []
-            for _ in range(5):
-                flush.fill_(1)
-                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                a.record(stream)
-                fn()
-                b.record(stream)
-                torch.cuda.synchronize()
-                times.append(a.elapsed_time(b))
-            times.sort()
-            per_kernel[name]["cold_median_ms"] = round(times[len(times) // 2], 4)
-        del flush
+    flush = None
+    if args.cold_iters > 0 or not args.no_ceiling:
+        flush = torch.empty(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+    if args.cold_iters > 0:
+        log("cold timing", args.cold_iters, "launches per kernel")
+        for name, fn, nbytes in kernels:
+            med, mn = time_cold(torch, fn, stream, flush, args.cold_iters)
+            per_kernel[name].update({"cold_median_ms": round(med, 4), "cold_min_ms": round(mn, 4),
+                                     "cold_median_GB/s": gbps(nbytes, med),
+                                     "cold_frac_hbm_peak": round(nbytes / (med * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)})
+    if not args.no_ceiling:
+        log("streaming ceiling per kernel")
+        for name, _, nbytes in kernels:
+            c = stream_ceiling(torch, name, desc, nbytes, stream, flush, max(10, min(args.steps, 50)))
+            per_kernel[name]["ceiling"] = c
+            per_kernel[name]["frac_of_ceiling"] = round(per_kernel[name]["GB/s"] / c["GBps"], 4)
+            if "cold_median_GB/s" in per_kernel[name]:
+                per_kernel[name]["cold_frac_of_ceiling"] = round(per_kernel[name]["cold_median_GB/s"]
+                                                                 / c["cold_GBps"], 4)
+    del flush
 
     total_bytes = sum(k[2] for k in kernels)
     value = total_bytes / (ms_per_step * 1e-3) / 1e9
@@ -430,12 +557,17 @@ def main():
     roofline = {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                 "traffic": stored_traffic(dom, desc),
-                "algorithmic_bytes_per_launch": dk["bytes"], "avg_launch_ms": dk["avg_ms"]}
-    # Context: the same figure against a plain 1 GiB device-to-device copy
-    # measured now (after the timed region, outside it).
-    copy_gbs = copy_bandwidth(torch)
-    roofline["copy_GBps"] = round(copy_gbs, 1)
-    roofline["frac_of_copy"] = round(achieved / copy_gbs, 4)
+                "algorithmic_bytes_per_launch": dk["bytes"], "avg_launch_ms": dk["avg_ms"],
+                "median_launch_ms": dk["median_ms"], "min_launch_ms": dk["min_ms"]}
+    if "ceiling" in dk:
+        roofline["ceiling_GBps"] = dk["ceiling"]["GBps"]
+        roofline["frac_of_ceiling"] = dk["frac_of_ceiling"]
+    if "cold_median_ms" in dk:
+        roofline["cold"] = {"median_launch_ms": dk["cold_median_ms"], "achieved": dk["cold_median_GB/s"],
+                            "frac": dk["cold_frac_hbm_peak"]}
+        if "ceiling" in dk:
+            roofline["cold"]["ceiling_GBps"] = dk["ceiling"]["cold_GBps"]
+            roofline["cold"]["frac_of_ceiling"] = dk["cold_frac_of_ceiling"]
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -456,6 +588,7 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f32",
+        "storage_dtype": desc["storage"],
         "data": "synthetic",
         "elements_per_s": round(units / (ms_per_step * 1e-3), 1),
         "config": desc,

@@ -18,6 +18,10 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libmiscan.so")
 SOURCES = ["api.hip", "linear_scan.hip", "log_scan.hip", "affine_scan.hip"]
+# The benchmark's probe kernels (streaming ceiling, cache flush): a library of
+# their own, not part of libmiscan.so.
+BENCH_LIB = os.path.join(PKG, "libmiscan_bench.so")
+BENCH_SOURCES = ["bench_kernels.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
@@ -42,21 +46,31 @@ def _compile(src: str, build_dir: str = BUILD, defines=()) -> str:
     return obj
 
 
-def build(verbose: bool = False, out: str = LIB, defines=(), build_dir: str = BUILD) -> str:
-    """Compile and link.  `defines` (NAME=VALUE) override the compile-time tile
-    shapes; `out` and `build_dir` keep such variants apart from the default."""
-    os.makedirs(build_dir, exist_ok=True)
-    workers = min(len(SOURCES), max(1, (os.cpu_count() or 2)))
-    with cf.ThreadPoolExecutor(max_workers=workers) as ex:
-        objs = list(ex.map(lambda s: _compile(s, build_dir, defines), SOURCES))
+def _link(objs, out: str):
     tmp = out + ".tmp%d" % os.getpid()
     cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n" + r.stderr)
     os.replace(tmp, out)
+
+
+def build(verbose: bool = False, out: str = LIB, defines=(), build_dir: str = BUILD, bench: bool = True) -> str:
+    """Compile and link libmiscan.so (and, with `bench`, libmiscan_bench.so).
+    `defines` (NAME=VALUE) override the compile-time tile shapes; `out` and
+    `build_dir` keep such variants apart from the default."""
+    os.makedirs(build_dir, exist_ok=True)
+    srcs = SOURCES + (BENCH_SOURCES if bench else [])
+    workers = min(len(srcs), max(1, (os.cpu_count() or 2)))
+    with cf.ThreadPoolExecutor(max_workers=workers) as ex:
+        objs = list(ex.map(lambda s: _compile(s, build_dir, defines), srcs))
+    _link(objs[:len(SOURCES)], out)
     if verbose:
         print("built", out)
+    if bench:
+        _link(objs[len(SOURCES):], BENCH_LIB)
+        if verbose:
+            print("built", BENCH_LIB)
     return out
 
 

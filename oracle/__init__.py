@@ -47,6 +47,8 @@ def _load():
         i64 = ctypes.c_int64
         p = ctypes.c_void_p
         lib.lrs_oracle_num_threads.restype = ctypes.c_int
+        lib.lrs_oracle_set_threads.argtypes = [ctypes.c_int]
+        lib.lrs_oracle_set_threads.restype = None
         lib.lrs_oracle_linear_fwd.argtypes = [i64, i64, i64, p, p, p, p]
         lib.lrs_oracle_linear_bwd.argtypes = [i64, i64, i64] + [p] * 7
         lib.lrs_oracle_scan_log_fwd.argtypes = [i64, i64, i64, p, p, p]
@@ -71,6 +73,11 @@ def _load():
 def num_threads() -> int:
     """OpenMP threads the oracle uses for independent channels/heads."""
     return int(_load().lrs_oracle_num_threads())
+
+
+def set_threads(n: int) -> None:
+    """Threads for the independent channels/heads of later calls."""
+    _load().lrs_oracle_set_threads(int(n))
 
 
 def _f64(x) -> np.ndarray:

@@ -36,6 +36,13 @@ int lrs_oracle_num_threads(void) {
 #endif
 }
 
+/* Threads for the independent channels or heads of later calls (timing of the
+ * oracle at one thread and at all host threads; the arithmetic per channel is
+ * the same either way). */
+void lrs_oracle_set_threads(int n) {
+    if (n > 0) omp_set_num_threads(n);
+}
+
 /* Flat index of element (b, t, d) of a contiguous (B, T, D) array. */
 static int64_t idx3(int64_t b, int64_t t, int64_t d, int64_t T, int64_t D) {
     return (b * T + t) * D + d;

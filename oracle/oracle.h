@@ -33,6 +33,7 @@ extern "C" {
 
 /* Number of OpenMP threads the oracle will use (1 when built without OpenMP). */
 int lrs_oracle_num_threads(void);
+void lrs_oracle_set_threads(int n);
 
 /* linear_scan_fwd: a, b are (B,T,D).  A_t is the running product of a, Bc_t is
  * the h_0 = 0 solution of h_t = a_t*h_{t-1} + b_t.  Outputs (B,T,D). */

@@ -26,10 +26,32 @@ def lib():
     return lrs._load()
 
 
-def declared_functions():
-    text = open(HEADER).read()
+def declared_functions(header=HEADER):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(mi_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_bench_header_symbols_exported():
+    """include/miscan_bench.h is the ABI of the benchmark's probe library."""
+    from linear_recurrence_scans_amd import build as B
+    names = declared_functions(os.path.join(ROOT, "include", "miscan_bench.h"))
+    assert names == ["mi_bench_flush", "mi_bench_stream"], names
+    so = ctypes.CDLL(B.BENCH_LIB)
+    for n in names:
+        assert hasattr(so, n), "libmiscan_bench.so does not export %s" % n
+    # every header under include/ is covered by one of the two checks
+    headers = sorted(f for f in os.listdir(os.path.join(ROOT, "include")) if f.endswith(".h"))
+    assert headers == ["miscan.h", "miscan_bench.h"], headers
+    # argument errors are reported before anything is enqueued
+    V = ctypes.c_void_p
+    arr = (V * 5)(*[P + i * STEP for i in range(5)])
+    so.mi_bench_stream.argtypes = [ctypes.POINTER(V), ctypes.c_int, ctypes.POINTER(V), ctypes.c_int,
+                                   ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, ctypes.c_int, V]
+    assert so.mi_bench_stream(arr, 3, arr, 2, 1, 4, 64, F32, None) == MI_ERR_UNSUPPORTED  # (3, 2) not built
+    assert so.mi_bench_stream(arr, 2, arr, 2, 0, 4, 64, F32, None) == MI_ERR_INVALID_ARG
+    so.mi_bench_flush.argtypes = [V, ctypes.c_size_t, V]
+    assert so.mi_bench_flush(None, 1 << 20, None) == MI_ERR_INVALID_ARG
 
 
 def test_header_symbols_exported():
@@ -213,3 +235,4 @@ def test_product_path_does_not_import_oracle():
                 text = open(os.path.join(dirpath, f)).read()
                 assert "import oracle" not in text and "from oracle" not in text, f
                 assert "lrs_oracle" not in text and "liboracle" not in text, f
+

@@ -21,7 +21,7 @@ import pytest
 from linear_recurrence_scans_amd import build as B
 
 HIPCC = B.HIPCC
-KERNEL_SOURCES = [s for s in B.SOURCES if s != "api.hip"]
+KERNEL_SOURCES = [s for s in B.SOURCES + B.BENCH_SOURCES if s != "api.hip"]
 
 pytestmark = pytest.mark.skipif(shutil.which(HIPCC) is None and not os.path.exists(HIPCC),
                                 reason="hipcc not available")
