@@ -53,7 +53,9 @@ typedef enum {
                                [1,128], or a dtype not built for the op */
     MI_ERR_WORKSPACE = 3,   /* workspace NULL or smaller than the query says */
     MI_ERR_LAUNCH = 4,      /* the HIP runtime reported an error at launch */
-    MI_ERR_DEVICE = 5       /* no usable gfx950 device */
+    MI_ERR_DEVICE = 5,      /* no usable gfx950 device */
+    MI_ERR_CAPACITY = 6     /* the problem needs more than the fixed scratch of
+                               mi_linear_scan_fwd_noalloc */
 } mi_status;
 
 typedef enum {
@@ -93,6 +95,27 @@ mi_status mi_linear_scan_bwd(const void *a, const void *A, const void *Bc,
                              const void *gA, const void *gBc, void *da, void *db,
                              int64_t B, int64_t T, int64_t D, mi_dtype dt,
                              void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* The same forward as mi_linear_scan_fwd, through an entry point that
+ * allocates nothing and takes no workspace.  For callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  The look-back workspace is a file-scope device array
+ * of MI_NOALLOC_SCRATCH_BYTES inside the library, one per GPU, held until the
+ * process ends; the call makes no hipMalloc/hipFree and no allocating library
+ * call.  Its device address is looked up (hipGetSymbolAddress) on the first
+ * call on each device, which must be the current device and the stream's.
+ * The array keeps the last call's contents; each call clears what must start
+ * at zero, on `stream`, before its scan kernel.  Every call on one GPU uses
+ * the same array: calls that may overlap on one GPU (other streams, other
+ * threads) race and must be serialised by the caller.  Same dtypes, layouts,
+ * results and argument checks as mi_linear_scan_fwd; a problem whose
+ * workspace exceeds the array returns MI_ERR_CAPACITY before anything is
+ * enqueued.  72 MiB covers the forward of 2^28 channel-steps in either dtype
+ * (e.g. B=8, T=8192, D=4096), about 4.2 bytes of scratch per 16 channel-steps. */
+#define MI_NOALLOC_SCRATCH_BYTES (72u << 20)
+mi_status mi_linear_scan_fwd_noalloc(const void *a, const void *b, void *A, void *Bc,
+                                     int64_t B, int64_t T, int64_t D, mi_dtype dt,
+                                     hipStream_t stream);
 
 /* Scans from a given initial state.  The page's linear_scan_fwd returns Bc,
  * the solution from h_0 = 0, and leaves the initial state to the caller

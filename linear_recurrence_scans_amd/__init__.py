@@ -24,6 +24,7 @@ __all__ = [
     "mi_status_string", "mi_device_check",
     "mi_linear_scan_workspace", "mi_linear_scan_fwd", "mi_linear_scan_bwd",
     "mi_linear_scan_fwd_h0", "mi_linear_scan_bwd_h0",
+    "mi_linear_scan_fwd_noalloc", "NOALLOC_SCRATCH_BYTES",
     "set_checked", "workspace_timeouts",
     "mi_scan_log_workspace", "mi_scan_log_fwd", "mi_scan_log_bwd",
     "mi_affine_scan_workspace", "mi_affine_scan_fwd", "mi_affine_scan_bwd",
@@ -36,6 +37,9 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libmiscan.so")
 
 MI_F32, MI_BF16 = 0, 1
+# Bytes of the per-device scratch array behind mi_linear_scan_fwd_noalloc
+# (MI_NOALLOC_SCRATCH_BYTES in include/miscan.h).
+NOALLOC_SCRATCH_BYTES = 72 << 20
 _DTYPES = {torch.float32: MI_F32, torch.bfloat16: MI_BF16}
 
 # C ABI entry points and their argument types.
@@ -47,6 +51,7 @@ _SIGS = {
     "mi_linear_scan_workspace": ([_I64, _I64, _I64, _I], _SZ),
     "mi_linear_scan_fwd": ([_V] * 4 + [_I64] * 3 + [_I, _V, _SZ, _V], _I),
     "mi_linear_scan_bwd": ([_V] * 7 + [_I64] * 3 + [_I, _V, _SZ, _V], _I),
+    "mi_linear_scan_fwd_noalloc": ([_V] * 4 + [_I64] * 3 + [_I, _V], _I),
     "mi_linear_scan_fwd_h0": ([_V] * 5 + [_I64] * 3 + [_I, _V, _SZ, _V], _I),
     "mi_linear_scan_bwd_h0": ([_V] * 9 + [_I64] * 3 + [_I, _V, _SZ, _V], _I),
     "mi_scan_log_workspace": ([_I64, _I64, _I64, _I], _SZ),
@@ -291,6 +296,25 @@ def mi_linear_scan_bwd(a, A, Bc, gA, gBc, da=None, db=None, *, ws=None, stream=N
                                         ws.data_ptr(), _nbytes(ws), c.handle)
         _check(st, "mi_linear_scan_bwd", c, ws if _nonempty(a) else None)
     return da, db
+
+
+def mi_linear_scan_fwd_noalloc(a, b, A=None, Bc=None, *, stream=None):
+    """(A, Bc) = linear_scan_fwd(a, b) through the entry point that allocates
+    nothing: its look-back state lives in the library's fixed per-device
+    scratch array (NOALLOC_SCRATCH_BYTES).  Calls that overlap on one GPU
+    share that array and must not run concurrently."""
+    with _Call(stream, _device(a, "a")) as c:
+        a, b = _dev_tensor(a, "a"), _dev_tensor(b, "b")
+        if a.dim() != 3 or b.shape != a.shape:
+            raise ValueError("a and b must both be (B, T, D)")
+        _same(a, b)
+        A, Bc = _out(A, a, "A"), _out(Bc, a, "Bc")
+        Bn, T, D = a.shape
+        c.keep(a, b, A, Bc)
+        st = _load().mi_linear_scan_fwd_noalloc(a.data_ptr(), b.data_ptr(), A.data_ptr(), Bc.data_ptr(),
+                                                Bn, T, D, _dt(a), c.handle)
+        _check(st, "mi_linear_scan_fwd_noalloc")
+    return A, Bc
 
 
 def _state(t, like: torch.Tensor, shape, name: str):

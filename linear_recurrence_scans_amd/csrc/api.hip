@@ -9,6 +9,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "common.hpp"
 #include "internal.hpp"
@@ -131,6 +132,8 @@ const char *mi_status_string(mi_status s) {
         case MI_ERR_WORKSPACE: return "MI_ERR_WORKSPACE: workspace missing or smaller than the size query";
         case MI_ERR_LAUNCH: return "MI_ERR_LAUNCH: the HIP runtime rejected a kernel launch";
         case MI_ERR_DEVICE: return "MI_ERR_DEVICE: no usable gfx950 device";
+        case MI_ERR_CAPACITY:
+            return "MI_ERR_CAPACITY: the problem needs more than the fixed scratch of the no-allocation entry point";
     }
     return "unknown mi_status";
 }
@@ -394,3 +397,59 @@ mi_status mi_affine_scan_bwd_h0(const void *A, const void *Abar, const void *H, 
 }
 
 }  // extern "C"
+
+// ---------------------------------------------------------------------------
+// The entry point that allocates nothing, for callers that cannot call
+// hipMalloc (code under graph capture, tight serving loops, harnesses that
+// forbid allocation).  Its look-back workspace is `scratch`, a file-scope
+// device array of MI_NOALLOC_SCRATCH_BYTES that every GPU the library runs on
+// holds until the process ends.  Host code never passes the array's name to a
+// kernel (on the host it only stands in for the symbol): the first call on a
+// device, with that device current, looks up the array's device address with
+// hipGetSymbolAddress and keeps it per device.  Every call on a GPU shares
+// that GPU's array, which keeps the last call's contents; the scan clears
+// what must start at zero (ticket, timeout counter, flags) on the stream
+// before its kernel, as the other entry points do with their workspace.
+// ---------------------------------------------------------------------------
+namespace miscan {
+namespace {
+
+static __device__ __align__(256) uint8_t scratch[MI_NOALLOC_SCRATCH_BYTES];
+
+constexpr int SCRATCH_MAX_DEVICES = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[SCRATCH_MAX_DEVICES];
+
+// Device address of the current device's scratch array.
+mi_status scratch_address(void **out) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= SCRATCH_MAX_DEVICES) return MI_ERR_DEVICE;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) return MI_ERR_DEVICE;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return MI_OK;
+}
+
+}  // namespace
+}  // namespace miscan
+
+extern "C" mi_status mi_linear_scan_fwd_noalloc(const void *a, const void *b, void *A, void *Bc, int64_t B,
+                                                int64_t T, int64_t D, mi_dtype dt, hipStream_t stream) {
+    int64_t bytes;
+    bool empty;
+    mi_status st = check_btd(B, T, D, dt, &bytes, &empty);
+    if (st != MI_OK || empty) return st;
+    const Buf bufs[4] = {{a, bytes}, {b, bytes}, {A, bytes}, {Bc, bytes}};
+    if ((st = check_buffers(bufs, 4, 2, elem_size(dt))) != MI_OK) return st;
+    const int vec = pick_vec(D, elem_size(dt), bufs, 4);
+    const size_t need = linear_fwd_workspace_bytes(B, T, D, dt, vec);
+    if (need == 0) return MI_ERR_UNSUPPORTED;  // the grid does not fit the ticket space
+    if (need > (size_t)MI_NOALLOC_SCRATCH_BYTES) return MI_ERR_CAPACITY;
+    void *ws = nullptr;
+    if ((st = scratch_address(&ws)) != MI_OK) return st;
+    return launch_linear_fwd(a, b, A, Bc, B, T, D, dt, vec, ws, need, stream);
+}

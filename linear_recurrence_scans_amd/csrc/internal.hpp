@@ -11,6 +11,7 @@ namespace miscan {
 
 // k = 1 channel scan and its adjoint (B, T, D).
 size_t linear_workspace_bytes(int64_t B, int64_t T, int64_t D, mi_dtype dt);
+size_t linear_fwd_workspace_bytes(int64_t B, int64_t T, int64_t D, mi_dtype dt, int vec);
 // h0_kernels selects the initial-state kernels (h0 in, dh0 out; h0 may be NULL).
 mi_status launch_linear_fwd(const void *a, const void *b, void *A, void *Bc,
                             int64_t B, int64_t T, int64_t D, mi_dtype dt, int vec,

@@ -594,6 +594,25 @@ mi_status run_bwd(const void *a, const void *A, const void *Bc, const void *gA,
 
 }  // namespace
 
+// Workspace of the forward alone at one vector width (the width the call
+// picks from D and the pointer alignment).
+size_t linear_fwd_workspace_bytes(int64_t B, int64_t T, int64_t D, mi_dtype dt, int vec) {
+    if (dt == MI_F32) {
+        switch (vec) {
+            case 4: return fwd_ws<float, 4>(B, T, D);
+            case 2: return fwd_ws<float, 2>(B, T, D);
+            default: return fwd_ws<float, 1>(B, T, D);
+        }
+    }
+    if (vec > MISCAN_LIN_FWD_BF16_VMAX) vec = MISCAN_LIN_FWD_BF16_VMAX;
+    switch (vec) {
+        case 8: return fwd_ws<bf16_t, 8>(B, T, D);
+        case 4: return fwd_ws<bf16_t, 4>(B, T, D);
+        case 2: return fwd_ws<bf16_t, 2>(B, T, D);
+        default: return fwd_ws<bf16_t, 1>(B, T, D);
+    }
+}
+
 size_t linear_workspace_bytes(int64_t B, int64_t T, int64_t D, mi_dtype dt) {
     // The vector width is chosen per call from pointer alignment, so size for
     // the largest requirement over every width the dtype may use.

@@ -16,7 +16,8 @@ import linear_recurrence_scans_amd as lrs
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "miscan.h")
 
-MI_OK, MI_ERR_INVALID_ARG, MI_ERR_UNSUPPORTED, MI_ERR_WORKSPACE, MI_ERR_LAUNCH, MI_ERR_DEVICE = range(6)
+(MI_OK, MI_ERR_INVALID_ARG, MI_ERR_UNSUPPORTED, MI_ERR_WORKSPACE, MI_ERR_LAUNCH, MI_ERR_DEVICE,
+ MI_ERR_CAPACITY) = range(7)
 F32, BF16 = 0, 1
 P = 1 << 20        # fake, 256-byte aligned "device" addresses; never dereferenced
 STEP = 1 << 30     # far apart: no overlap unless a test wants one
@@ -66,7 +67,7 @@ def test_header_symbols_exported():
 
 
 def test_status_strings():
-    for code in range(6):
+    for code in range(7):
         s = lrs.mi_status_string(code)
         assert s.startswith("MI_"), s
     assert "unknown" in lrs.mi_status_string(99)
@@ -236,3 +237,31 @@ def test_product_path_does_not_import_oracle():
                 assert "import oracle" not in text and "from oracle" not in text, f
                 assert "lrs_oracle" not in text and "liboracle" not in text, f
 
+
+def test_noalloc_checks_before_any_device_call():
+    """The no-allocation forward validates like mi_linear_scan_fwd and rejects a
+    problem larger than its fixed scratch with MI_ERR_CAPACITY, all before it
+    touches a device (no GPU here)."""
+    L = lib()
+    a, b, A, Bc = ptrs(4)
+    call = lambda *args: L.mi_linear_scan_fwd_noalloc(*args, None)
+    assert call(None, None, None, None, 0, 5, 5, F32) == MI_OK          # zero-sized: nothing to do
+    assert call(a, b, A, Bc, -1, 4, 4, F32) == MI_ERR_INVALID_ARG
+    assert call(None, b, A, Bc, 1, 4, 4, F32) == MI_ERR_INVALID_ARG
+    assert call(a, b, a + 8, Bc, 1, 4, 4, F32) == MI_ERR_INVALID_ARG  # output overlaps input
+    assert call(a, b, A, Bc, 1, 4, 4, 7) == MI_ERR_UNSUPPORTED
+    # 2^31 channel-steps need far more than the scratch holds (buffers 1 TiB apart)
+    a, b, A, Bc = [P + i * (1 << 40) for i in range(4)]
+    assert call(a, b, A, Bc, 64, 8192, 4096, BF16) == MI_ERR_CAPACITY
+    assert call(a, b, A, Bc, 64, 8192, 4096, F32) == MI_ERR_CAPACITY
+
+
+def test_noalloc_capacity_constant_matches_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define\s+MI_NOALLOC_SCRATCH_BYTES\s+\((\d+)u\s*<<\s*(\d+)\)", text)
+    assert m, "MI_NOALLOC_SCRATCH_BYTES not found"
+    assert lrs.NOALLOC_SCRATCH_BYTES == int(m.group(1)) << int(m.group(2))
+    # the documented workload (B=8, T=8192, D=4096) fits: its forward workspace
+    # at the widest vectors is at most the scratch
+    for dt in (F32, BF16):
+        assert lib().mi_linear_scan_workspace(8, 8192, 4096, dt) > 0
