@@ -14,8 +14,9 @@
  *    second axis: (B, T, D) for the channel scans, (B, T, n, r, c) for the k x k
  *    scan.  Step t = 1..T of the recurrence is row t-1.
  *  - Outputs have the shape and dtype of the corresponding input.  With bf16
- *    storage all arithmetic is fp32; results are rounded to bf16 (nearest-even)
- *    once, on store.  Every output element is written.
+ *    or fp16 storage all arithmetic is fp32; results are rounded to the
+ *    storage type (nearest-even) once, on store.  Every output element is
+ *    written.
  *  - Ownership: the caller allocates every input, output and the workspace.  The
  *    library keeps no device memory and no state between calls, and never
  *    synchronises: a call enqueues its kernels on `stream` and returns.
@@ -60,7 +61,8 @@ typedef enum {
 
 typedef enum {
     MI_F32 = 0,  /* IEEE binary32 storage */
-    MI_BF16 = 1  /* bfloat16 storage, fp32 arithmetic */
+    MI_BF16 = 1, /* bfloat16 storage, fp32 arithmetic */
+    MI_F16 = 2   /* IEEE binary16 storage, fp32 arithmetic */
 } mi_dtype;
 
 /* Human-readable name of a status code (static storage, never NULL). */
@@ -73,7 +75,7 @@ mi_status mi_device_check(int device, char *reason, size_t reason_len);
 
 /* ------------------------------------------------------------------------ */
 /* k = 1 channel scan ("Triton kernels", Kernel entry points:               */
-/* linear_scan_fwd, linear_scan_bwd).  Dtypes: MI_F32, MI_BF16.             */
+/* linear_scan_fwd, linear_scan_bwd).  Dtypes: MI_F32, MI_BF16, MI_F16.     */
 /* ------------------------------------------------------------------------ */
 
 /* Workspace bytes for mi_linear_scan_fwd / mi_linear_scan_bwd on (B, T, D). */
@@ -143,7 +145,7 @@ mi_status mi_linear_scan_bwd_h0(const void *a, const void *A, const void *H, con
 
 /* ------------------------------------------------------------------------ */
 /* Log-space scan ("Triton kernels", Kernel entry points:                   */
-/* parallel_scan_log_fwd).  Dtypes: MI_F32, MI_BF16.                        */
+/* parallel_scan_log_fwd).  Dtypes: MI_F32, MI_BF16, MI_F16.                */
 /* ------------------------------------------------------------------------ */
 
 /* Workspace bytes for mi_scan_log_fwd and mi_scan_log_bwd on (B, T, D). */
@@ -178,8 +180,8 @@ mi_status mi_scan_log_bwd(const void *log_coeffs, const void *log_values, const 
 
 /* ------------------------------------------------------------------------ */
 /* k x k matrix-affine scan ("Triton kernels", Kernel entry points:         */
-/* affine_scan_fwd, affine_scan_bwd).  Dtypes: MI_F32, MI_BF16 (storage;   */
-/* arithmetic fp32).  1 <= k <= 16,                                          */
+/* affine_scan_fwd, affine_scan_bwd).  Dtypes: MI_F32, MI_BF16, MI_F16     */
+/* (storage; arithmetic fp32).  1 <= k <= 16,                               */
 /* 1 <= v <= 128.                                                           */
 /* ------------------------------------------------------------------------ */
 

@@ -36,11 +36,11 @@ __all__ = [
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _LIB_PATH = os.path.join(_HERE, "libmiscan.so")
 
-MI_F32, MI_BF16 = 0, 1
+MI_F32, MI_BF16, MI_F16 = 0, 1, 2
 # Bytes of the per-device scratch array behind mi_linear_scan_fwd_noalloc
 # (MI_NOALLOC_SCRATCH_BYTES in include/miscan.h).
 NOALLOC_SCRATCH_BYTES = 72 << 20
-_DTYPES = {torch.float32: MI_F32, torch.bfloat16: MI_BF16}
+_DTYPES = {torch.float32: MI_F32, torch.bfloat16: MI_BF16, torch.float16: MI_F16}
 
 # C ABI entry points and their argument types.
 _V, _I64, _SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t
@@ -127,7 +127,7 @@ def _dt(t: torch.Tensor) -> int:
     try:
         return _DTYPES[t.dtype]
     except KeyError:
-        raise TypeError("unsupported dtype %s (float32 or bfloat16)" % t.dtype) from None
+        raise TypeError("unsupported dtype %s (float32, bfloat16 or float16)" % t.dtype) from None
 
 
 def _dev_tensor(t: torch.Tensor, name: str) -> torch.Tensor:

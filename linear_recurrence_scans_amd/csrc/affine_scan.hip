@@ -426,15 +426,28 @@ __device__ __forceinline__ void stage_payloads(float *s_stage, const WsPtrs &ws,
                                                const LbPos &lq, int b0, int nb, int slot_sz) {
     const int tid = threadIdx.x, nt = blockDim.x;
     const int n_wait = lq.n_wait;
-    const int64_t lo = dir < 0 ? slot - n_wait + b0 : slot + n_wait - (b0 + nb - 1);  // lowest slot
-    const rsrc_t ra = make_rows(ws.agg + lo * slot_sz, (int64_t)nb * slot_sz * 4);
-    const rsrc_t ri = make_rows(ws.inc + lo * slot_sz, (int64_t)nb * slot_sz * 4);
-    for (int e = tid * 4; e < nb * slot_sz; e += nt * 4) {
-        const int a = e / slot_sz, off = e - a * slot_sz;  // slot lo + a
-        const int q = dir < 0 ? b0 + a : b0 + nb - 1 - a;   // its fold index
-        float v[4];
-        carry_load_vec<4>(v, (q == 0 && lq.has_inc) ? ri : ra, 4u * (uint32_t)e);
-        *reinterpret_cast<f32x4 *>(s_stage + (q - b0) * slot_sz + off) = f32x4{v[0], v[1], v[2], v[3]};
+    int first = b0;
+    if (b0 == 0 && lq.has_inc) {  // fold index 0: the inclusive state of slot + n_wait dir
+        const rsrc_t r = make_rows(ws.inc + (slot + (int64_t)dir * n_wait) * slot_sz, (int64_t)slot_sz * 4);
+        for (int e = tid * 4; e < slot_sz; e += nt * 4) {
+            float v[4];
+            carry_load_vec<4>(v, r, 4u * (uint32_t)e);
+            *reinterpret_cast<f32x4 *>(s_stage + e) = f32x4{v[0], v[1], v[2], v[3]};
+        }
+        first = 1;
+    }
+    const int last = b0 + nb - 1;
+    const int na = last - first + 1;  // aggregates in this batch
+    if (na > 0) {
+        const int64_t lo = dir < 0 ? slot - n_wait + first : slot + n_wait - last;  // lowest slot
+        const rsrc_t r = make_rows(ws.agg + lo * slot_sz, (int64_t)na * slot_sz * 4);
+        for (int e = tid * 4; e < na * slot_sz; e += nt * 4) {
+            const int a = e / slot_sz, off = e - a * slot_sz;  // slot lo + a
+            const int q = dir < 0 ? first + a : last - a;       // its fold index
+            float v[4];
+            carry_load_vec<4>(v, r, 4u * (uint32_t)e);
+            *reinterpret_cast<f32x4 *>(s_stage + (q - b0) * slot_sz + off) = f32x4{v[0], v[1], v[2], v[3]};
+        }
     }
 }
 
@@ -511,6 +524,11 @@ __global__ __launch_bounds__(512) void affine_fwd_kernel(FwdArgs p) {
     const int64_t t_w = sm.t(t_c, hsc, wave * L);  // first step of the lane's rows
     const int64_t m0 = bidx * p.T * p.n + hn;  // matrix index of (b, t = 0, h); + t n per step
 
+    float x[KP][CPL];
+#pragma unroll
+    for (int i = 0; i < KP; ++i)
+#pragma unroll
+        for (int cc = 0; cc < CPL; ++cc) x[i][cc] = (cl.kind[cc] == C_ABAR && i == cl.col[cc]) ? 1.f : 0.f;
     // 1. B of the wave's steps (registers) and the A_t blocks (LDS).
     float rb[L][KP][CPL];
 #pragma unroll
@@ -519,11 +537,6 @@ __global__ __launch_bounds__(512) void affine_fwd_kernel(FwdArgs p) {
     lds_barrier();
 
     // 2. The wave's transform from [I | 0].
-    float x[KP][CPL];
-#pragma unroll
-    for (int i = 0; i < KP; ++i)
-#pragma unroll
-        for (int cc = 0; cc < CPL; ++cc) x[i][cc] = (cl.kind[cc] == C_ABAR && i == cl.col[cc]) ? 1.f : 0.f;
 #pragma unroll
     for (int r = 0; r < L; ++r) step_lds<KP, CPL>(x, s_A + ((wave * L + r) * HPW + hsc) * AS, rb[r]);
     // 3. Inclusive prefix (Hillis-Steele) over the chunk's SEG * NW pieces in
@@ -596,11 +609,12 @@ __global__ __launch_bounds__(512) void affine_fwd_kernel(FwdArgs p) {
             stage_payloads(s_stage, p.ws, slot, -1, lq, b0, nb, slot_sz);
             lds_barrier();
             if (wave == 0) {
-                for (int q = b0; q < b0 + nb; ++q) {
-                    const float *blk_q = s_stage + (q - b0) * slot_sz + hoff;
-                    if (q == 0 && lq.has_inc) get_cols<KP, CPL>(S, blk_q, NCP, c0);  // chunk - W's state
-                    else block_apply<KP, CPL>(S, blk_q, NCP, k, c0, is_h);
+                int q = b0;
+                if (q == 0 && lq.has_inc) {  // the inclusive state of chunk - W
+                    get_cols<KP, CPL>(S, s_stage + hoff, NCP, c0);
+                    q = 1;
                 }
+                for (; q < b0 + nb; ++q) block_apply<KP, CPL>(S, s_stage + (q - b0) * slot_sz + hoff, NCP, k, c0, is_h);
             }
             if (b0 + p.DB < lq.n_wait) lds_barrier();  // the next batch overwrites the stage
         }
@@ -928,18 +942,16 @@ __global__ __launch_bounds__(512) void affine_bwd_kernel(BwdArgs p) {
             stage_payloads(s_part, p.ws, slot, +1, lq, b0, nb, slot_sz);
             lds_barrier();
             if (wave == 0) {
-                for (int q = b0; q < b0 + nb; ++q) {
-                    const float *blk_q = s_part + (q - b0) * slot_sz + hoff;
-                    if (q == 0 && lq.has_inc) {  // the state of chunk + W (its Y columns)
-                        get_cols<KP, CPL>(S, blk_q, NCP, c0);
+                int q = b0;
+                if (q == 0 && lq.has_inc) {  // the state of chunk + W (its Y columns)
+                    get_cols<KP, CPL>(S, s_part + hoff, NCP, c0);
 #pragma unroll
-                        for (int i = 0; i < KP; ++i)
+                    for (int i = 0; i < KP; ++i)
 #pragma unroll
-                            for (int cc = 0; cc < CPL; ++cc) S[i][cc] = is_y[cc] ? S[i][cc] : 0.f;
-                    } else {
-                        block_apply<KP, CPL>(S, blk_q, NCP, k, c0, is_y);
-                    }
+                        for (int cc = 0; cc < CPL; ++cc) S[i][cc] = is_y[cc] ? S[i][cc] : 0.f;
+                    q = 1;
                 }
+                for (; q < b0 + nb; ++q) block_apply<KP, CPL>(S, s_part + (q - b0) * slot_sz + hoff, NCP, k, c0, is_y);
             }
             if (b0 + p.DB < lq.n_wait) lds_barrier();  // the next batch overwrites the stage
         }
@@ -1080,10 +1092,11 @@ struct AffPlan {
     int KP, CPL;
     bool VIO;
     bool h0;    // launch the initial-state (H0) kernels
-    bool bf16;  // bf16 storage (fp32 otherwise)
+    mi_dtype dt;  // storage type (arithmetic is fp32)
     int G, HPW, NCP, n_groups, n_chunks, LC, NW;
     int HH, SEG;  // heads per workgroup, time segments per chunk (HH * SEG = HPW)
     int DB;       // look-back payload blocks staged per round trip
+    int W;        // look-back window
     size_t n_slots, payload, lds_bytes;
     bool ok;  // the work-item count fits the int32 ticket space, the LDS the workgroup
 };
@@ -1112,6 +1125,13 @@ constexpr size_t LDS_DEVICE_MAX = 163840;
 #define MISCAN_AFF_STAGE_FLOATS 4096
 #endif
 
+// Work items that run at once, for the look-back window (lb_window): the k x k
+// fold costs a block product per payload on one wave, so its window is kept
+// short (2 to 4 chunks at the workloads' head counts).
+#ifndef MISCAN_AFF_RESIDENT
+#define MISCAN_AFF_RESIDENT 128
+#endif
+
 // Time segments per forward chunk: the largest divisor of HPW up to this
 // bound.  Segments shorten the look-back chain but add prefix rounds; with
 // the longer per-wave runs above, two segments at most measured fastest.
@@ -1131,12 +1151,12 @@ inline AffPlan make_plan(int64_t B, int64_t T, int64_t n, int k, int v, bool bwd
     pl.CPL = CPL;
     pl.VIO = VIO;
     pl.h0 = false;
-    pl.bf16 = false;
+    pl.dt = MI_F32;
     const int ncols = bwd ? 2 * k + v : k + v;
     pl.G = (ncols + CPL - 1) / CPL;
     if (pl.G > 64) {  // a head must fit one wave: this tiling is not usable
         pl.HPW = 0; pl.NCP = 0; pl.n_groups = 0; pl.n_chunks = 0; pl.LC = 0; pl.NW = 0;
-        pl.HH = 0; pl.SEG = 0; pl.DB = 0;
+        pl.HH = 0; pl.SEG = 0; pl.DB = 0; pl.W = 2;
         pl.n_slots = 0; pl.payload = 0; pl.lds_bytes = 0; pl.ok = false;
         return pl;
     }
@@ -1154,8 +1174,14 @@ inline AffPlan make_plan(int64_t B, int64_t T, int64_t n, int k, int v, bool bwd
     const size_t part = round_up((size_t)pl.HPW * pl.G * aff_part_stride(rb * pl.KP), 4);
     const size_t limit = bwd ? BWD_LDS_MAX : FWD_LDS_MAX;
     const size_t payload = (size_t)pl.HH * pl.KP * pl.NCP;  // floats of one look-back slot
+    // Look-back window (payloads a chunk folds) and staged payloads per round
+    // trip: no more than the window, so the forward's stage takes no more LDS
+    // than one round needs.
+    const int64_t heads = B * n;
+    pl.W = lb_window((heads + pl.HH - 1) / pl.HH, MISCAN_AFF_RESIDENT);
     const size_t fwd_db = MISCAN_AFF_STAGE_FLOATS / payload;
-    const int fdb = fwd_db < 1 ? 1 : fwd_db > MISCAN_AFF_DBMAX ? MISCAN_AFF_DBMAX : (int)fwd_db;
+    const int fdb_cap = pl.W < MISCAN_AFF_DBMAX ? pl.W : MISCAN_AFF_DBMAX;
+    const int fdb = fwd_db < 1 ? 1 : fwd_db > (size_t)fdb_cap ? fdb_cap : (int)fwd_db;
     auto lds_floats = [&](int nw) {
         const size_t common = round_up((size_t)nw * L * pl.HPW * a_ld, 4) + (size_t)nw * pl.HPW * x_ld;
         // the backward's dA buffer also holds at least one staged payload
@@ -1168,7 +1194,6 @@ inline AffPlan make_plan(int64_t B, int64_t T, int64_t n, int k, int v, bool bwd
         if (lds_floats(nw) * sizeof(float) <= limit) { pl.NW = nw; break; }
     pl.LC = pl.SEG * pl.NW * L;
     pl.lds_bytes = lds_floats(pl.NW) * sizeof(float);
-    const int64_t heads = B * n;
     const int64_t ng = (heads + pl.HH - 1) / pl.HH;
     const int64_t nc = (T + pl.LC - 1) / pl.LC;
     pl.ok = ng <= INT32_MAX && nc <= INT32_MAX && ng * nc <= (int64_t)INT32_MAX &&
@@ -1179,7 +1204,7 @@ inline AffPlan make_plan(int64_t B, int64_t T, int64_t n, int k, int v, bool bwd
     pl.payload = payload;
     if (bwd) {
         const size_t db = ((size_t)pl.NW * part > payload ? (size_t)pl.NW * part : payload) / payload;
-        pl.DB = db > MISCAN_AFF_DBMAX ? MISCAN_AFF_DBMAX : (int)db;
+        pl.DB = db > (size_t)fdb_cap ? fdb_cap : (int)db;
     } else {
         pl.DB = fdb;
     }
@@ -1230,9 +1255,12 @@ mi_status fwd_launch_h(const AffPlan &pl, FwdArgs &a, hipStream_t s) {
 // Storage type and initial-state kernels from the plan.
 template <int KP, int CPL, bool VIO>
 mi_status fwd_launch(const AffPlan &pl, FwdArgs &a, hipStream_t s) {
-    if (pl.bf16)
+    if (pl.dt == MI_BF16)
         return pl.h0 ? fwd_launch_h<bf16_t, KP, CPL, VIO, true>(pl, a, s)
                      : fwd_launch_h<bf16_t, KP, CPL, VIO, false>(pl, a, s);
+    if (pl.dt == MI_F16)
+        return pl.h0 ? fwd_launch_h<f16_t, KP, CPL, VIO, true>(pl, a, s)
+                     : fwd_launch_h<f16_t, KP, CPL, VIO, false>(pl, a, s);
     return pl.h0 ? fwd_launch_h<float, KP, CPL, VIO, true>(pl, a, s) : fwd_launch_h<float, KP, CPL, VIO, false>(pl, a, s);
 }
 template <typename TS, int KP, int CPL, bool VIO, bool H0>
@@ -1245,9 +1273,12 @@ mi_status bwd_launch_h(const AffPlan &pl, BwdArgs &a, hipStream_t s) {
 }
 template <int KP, int CPL, bool VIO>
 mi_status bwd_launch(const AffPlan &pl, BwdArgs &a, hipStream_t s) {
-    if (pl.bf16)
+    if (pl.dt == MI_BF16)
         return pl.h0 ? bwd_launch_h<bf16_t, KP, CPL, VIO, true>(pl, a, s)
                      : bwd_launch_h<bf16_t, KP, CPL, VIO, false>(pl, a, s);
+    if (pl.dt == MI_F16)
+        return pl.h0 ? bwd_launch_h<f16_t, KP, CPL, VIO, true>(pl, a, s)
+                     : bwd_launch_h<f16_t, KP, CPL, VIO, false>(pl, a, s);
     return pl.h0 ? bwd_launch_h<float, KP, CPL, VIO, true>(pl, a, s) : bwd_launch_h<float, KP, CPL, VIO, false>(pl, a, s);
 }
 
@@ -1300,7 +1331,7 @@ mi_status launch_affine_fwd(const void *A, const void *Bm, void *Abar, void *Bba
     AffPlan pl = choose_plan(B, T, n, (int)k, (int)v, false, p16);
     if (!pl.ok) return MI_ERR_UNSUPPORTED;
     pl.h0 = h0_kernels;
-    pl.bf16 = dt == MI_BF16;
+    pl.dt = dt;
     WsLayout lay(pl.n_slots, pl.payload);
     if (ws == nullptr || ws_bytes < lay.total) return MI_ERR_WORKSPACE;
     FwdArgs a;
@@ -1308,7 +1339,7 @@ mi_status launch_affine_fwd(const void *A, const void *Bm, void *Abar, void *Bba
     a.T = T; a.heads = B * n; a.n = (int)n; a.k = (int)k; a.v = (int)v;
     a.G = pl.G; a.HPW = pl.HPW; a.NCP = pl.NCP; a.n_groups = pl.n_groups;
     a.n_chunks = pl.n_chunks; a.NW = pl.NW; a.HH = pl.HH; a.DB = pl.DB;
-    a.lb_window = lb_window(pl.n_groups);
+    a.lb_window = pl.W;
     a.ws = ws_ptrs(ws, lay);
     mi_status st = clear_workspace(a.ws, pl.n_slots, s);
     if (st != MI_OK) return st;
@@ -1325,7 +1356,7 @@ mi_status launch_affine_bwd(const void *A, const void *Abar, const void *Bbar,
     AffPlan pl = choose_plan(B, T, n, (int)k, (int)v, true, p16);
     if (!pl.ok) return MI_ERR_UNSUPPORTED;
     pl.h0 = h0_kernels;
-    pl.bf16 = dt == MI_BF16;
+    pl.dt = dt;
     WsLayout lay(pl.n_slots, pl.payload);
     if (ws == nullptr || ws_bytes < lay.total) return MI_ERR_WORKSPACE;
     BwdArgs a;
@@ -1334,7 +1365,7 @@ mi_status launch_affine_bwd(const void *A, const void *Abar, const void *Bbar,
     a.T = T; a.heads = B * n; a.n = (int)n; a.k = (int)k; a.v = (int)v;
     a.G = pl.G; a.HPW = pl.HPW; a.NCP = pl.NCP; a.n_groups = pl.n_groups;
     a.n_chunks = pl.n_chunks; a.NW = pl.NW; a.HH = pl.HH; a.DB = pl.DB;
-    a.lb_window = lb_window(pl.n_groups);
+    a.lb_window = pl.W;
     a.ws = ws_ptrs(ws, lay);
     mi_status st = clear_workspace(a.ws, pl.n_slots, s);
     if (st != MI_OK) return st;

@@ -44,8 +44,8 @@ mi_status zero_async(void *p, size_t bytes, hipStream_t s) {
 
 namespace {
 
-size_t elem_size(mi_dtype dt) { return dt == MI_BF16 ? 2 : 4; }
-bool dtype_known(mi_dtype dt) { return dt == MI_F32 || dt == MI_BF16; }
+size_t elem_size(mi_dtype dt) { return dt == MI_F32 ? 4 : 2; }
+bool dtype_known(mi_dtype dt) { return dt == MI_F32 || dt == MI_BF16 || dt == MI_F16; }
 
 // a*b*c*d into *out without int64 overflow; all factors non-negative.
 bool mul_ok(int64_t a, int64_t b, int64_t c, int64_t d, int64_t *out) {

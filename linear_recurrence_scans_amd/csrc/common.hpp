@@ -14,6 +14,7 @@
 namespace miscan {
 
 typedef uint16_t bf16_t;  // raw bfloat16 bits
+typedef _Float16 f16_t;   // IEEE binary16 (storage only; arithmetic stays fp32)
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -30,6 +31,18 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
     f32x2 f = {lo, hi};
     bf16x2 r = __builtin_convertvector(f, bf16x2);
     return __builtin_bit_cast(uint32_t, r);
+}
+
+// fp16 <-> fp32: widening is exact (v_cvt_f32_f16); narrowing rounds to
+// nearest even (v_cvt_f16_f32 under the default rounding mode), with fp16
+// subnormals kept.
+__device__ __forceinline__ float f16_lo(uint32_t w) {
+    return (float)__builtin_bit_cast(f16_t, (uint16_t)(w & 0xffffu));
+}
+__device__ __forceinline__ float f16_hi(uint32_t w) { return (float)__builtin_bit_cast(f16_t, (uint16_t)(w >> 16)); }
+__device__ __forceinline__ uint16_t f16_bits(float x) { return __builtin_bit_cast(uint16_t, (f16_t)x); }
+__device__ __forceinline__ uint32_t pack_f16x2(float lo, float hi) {
+    return (uint32_t)f16_bits(lo) | ((uint32_t)f16_bits(hi) << 16);
 }
 
 // ---------------------------------------------------------------------------
@@ -84,6 +97,39 @@ template <> struct Pack<bf16_t, 1> {
     typedef uint16_t raw_t;
     static __device__ __forceinline__ void unpack(raw_t r, float *f) { f[0] = __uint_as_float((uint32_t)r << 16); }
     static __device__ __forceinline__ raw_t pack(const float *f) { return (uint16_t)(pack_bf16x2(f[0], 0.f) & 0xffffu); }
+};
+
+template <> struct Pack<f16_t, 8> {
+    typedef u32x4 raw_t;
+    static __device__ __forceinline__ void unpack(raw_t r, float *f) {
+        f[0] = f16_lo(r.x); f[1] = f16_hi(r.x); f[2] = f16_lo(r.y); f[3] = f16_hi(r.y);
+        f[4] = f16_lo(r.z); f[5] = f16_hi(r.z); f[6] = f16_lo(r.w); f[7] = f16_hi(r.w);
+    }
+    static __device__ __forceinline__ raw_t pack(const float *f) {
+        raw_t r = {pack_f16x2(f[0], f[1]), pack_f16x2(f[2], f[3]),
+                   pack_f16x2(f[4], f[5]), pack_f16x2(f[6], f[7])};
+        return r;
+    }
+};
+template <> struct Pack<f16_t, 4> {
+    typedef u32x2 raw_t;
+    static __device__ __forceinline__ void unpack(raw_t r, float *f) {
+        f[0] = f16_lo(r.x); f[1] = f16_hi(r.x); f[2] = f16_lo(r.y); f[3] = f16_hi(r.y);
+    }
+    static __device__ __forceinline__ raw_t pack(const float *f) {
+        raw_t r = {pack_f16x2(f[0], f[1]), pack_f16x2(f[2], f[3])};
+        return r;
+    }
+};
+template <> struct Pack<f16_t, 2> {
+    typedef uint32_t raw_t;
+    static __device__ __forceinline__ void unpack(raw_t r, float *f) { f[0] = f16_lo(r); f[1] = f16_hi(r); }
+    static __device__ __forceinline__ raw_t pack(const float *f) { return pack_f16x2(f[0], f[1]); }
+};
+template <> struct Pack<f16_t, 1> {
+    typedef uint16_t raw_t;
+    static __device__ __forceinline__ void unpack(raw_t r, float *f) { f[0] = (float)__builtin_bit_cast(f16_t, r); }
+    static __device__ __forceinline__ raw_t pack(const float *f) { return f16_bits(f[0]); }
 };
 
 template <typename T, int VEC>
@@ -244,18 +290,18 @@ __host__ __device__ inline LbPos lb_pos(int ord, int W) {
 
 // Window from the shape: about RESIDENT work items run at once, i.e.
 // RESIDENT / tiles consecutive chunks of every tile.  A power of two in
-// [2, 16].  It depends on the shape only, so equal shapes always fold in the
-// same order.
+// [2, wmax] (wmax <= 64: a wait polls one flag a lane).  It depends on the
+// shape only, so equal shapes always fold in the same order.
 #ifndef MISCAN_LB_RESIDENT
 #define MISCAN_LB_RESIDENT 256
 #endif
 #ifndef MISCAN_LB_WMAX
 #define MISCAN_LB_WMAX 16
 #endif
-inline int lb_window(int64_t tiles, int64_t resident = MISCAN_LB_RESIDENT) {
+inline int lb_window(int64_t tiles, int64_t resident = MISCAN_LB_RESIDENT, int wmax = MISCAN_LB_WMAX) {
     const int64_t want = tiles > 0 ? (resident + tiles - 1) / tiles : 1;
     int W = 2;
-    while (W < want && W < MISCAN_LB_WMAX) W *= 2;
+    while (W < want && W < wmax) W *= 2;
     return W;
 }
 
@@ -283,6 +329,9 @@ __device__ __forceinline__ float carry_load(const float *p) {
 // relaxed device-scope atomic loads, so it observes payload words published
 // under the flag protocol.
 constexpr int CPOL_SC1 = 16;
+// The same for a poll that a loop repeats: the volatile bit keeps the
+// compiler from treating the repeated load as invariant.
+constexpr int CPOL_SC1_VOLATILE = (int)(16u | 0x80000000u);
 template <int N>
 __device__ __forceinline__ void carry_load_vec(float *dst, __amdgpu_buffer_rsrc_t r, uint32_t voff) {
     if constexpr (N == 4) {
@@ -321,11 +370,15 @@ __device__ __forceinline__ void wait_window(const uint32_t *flags, int64_t slot,
     const int lane = threadIdx.x & 63;
     const bool valid = lane < q.n_wait;
     const uint32_t need = (q.has_inc && lane == q.n_wait - 1) ? FLAG_INC : FLAG_AGG;
-    const uint32_t *f_lane = flags + slot + (int64_t)dir * (lane + 1);
+    // the window's flags through one descriptor based at its lowest slot: a
+    // 32-bit offset per lane (device-coherent loads, as carry_load)
+    const int64_t lo = dir < 0 ? slot - q.n_wait : slot + 1;
+    const rsrc_t r = make_rows(flags + lo, (int64_t)q.n_wait * 4);
+    const uint32_t voff = valid ? 4u * (uint32_t)(dir < 0 ? q.n_wait - 1 - lane : lane) : 0u;
     uint32_t spins = 0;
     while (true) {
         uint32_t f = FLAG_INC;
-        if (valid) f = __hip_atomic_load(f_lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (valid) f = __builtin_amdgcn_raw_buffer_load_b32(r, voff, 0, CPOL_SC1_VOLATILE);
         const uint64_t empty = __ballot(f < need);
         if (own) {
             publish_flag(own, FLAG_AGG);

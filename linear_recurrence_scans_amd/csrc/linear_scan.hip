@@ -595,7 +595,8 @@ mi_status run_bwd(const void *a, const void *A, const void *Bc, const void *gA,
 }  // namespace
 
 // Workspace of the forward alone at one vector width (the width the call
-// picks from D and the pointer alignment).
+// picks from D and the pointer alignment).  The 2-byte storage types (bf16,
+// fp16) share their tilings.
 size_t linear_fwd_workspace_bytes(int64_t B, int64_t T, int64_t D, mi_dtype dt, int vec) {
     if (dt == MI_F32) {
         switch (vec) {
@@ -621,7 +622,7 @@ size_t linear_workspace_bytes(int64_t B, int64_t T, int64_t D, mi_dtype dt) {
     if (dt == MI_F32) {
         upd(fwd_ws<float, 4>(B, T, D)); upd(fwd_ws<float, 2>(B, T, D)); upd(fwd_ws<float, 1>(B, T, D));
         upd(bwd_ws<float, 4>(B, T, D)); upd(bwd_ws<float, 2>(B, T, D)); upd(bwd_ws<float, 1>(B, T, D));
-    } else {
+    } else {  // bf16 and fp16
         upd(fwd_ws<bf16_t, 8>(B, T, D)); upd(fwd_ws<bf16_t, 4>(B, T, D));
         upd(fwd_ws<bf16_t, 2>(B, T, D)); upd(fwd_ws<bf16_t, 1>(B, T, D));
         upd(bwd_ws<bf16_t, 8>(B, T, D)); upd(bwd_ws<bf16_t, 4>(B, T, D));
@@ -630,27 +631,58 @@ size_t linear_workspace_bytes(int64_t B, int64_t T, int64_t D, mi_dtype dt) {
     return m;
 }
 
+namespace {
+
+// 2-byte storage (bf16 or fp16): the widest vector each direction uses.
+template <typename E>
+mi_status fwd_2byte(const void *a, const void *b, void *A, void *Bc, int64_t B, int64_t T, int64_t D, int vec,
+                    void *ws, size_t ws_bytes, hipStream_t s, bool h0_kernels, const void *h0) {
+#define MISCAN_LIN_FWD(V)                                                                        \
+    (h0_kernels ? run_fwd<E, V, true>(a, b, A, Bc, B, T, D, ws, ws_bytes, s, h0)                 \
+                : run_fwd<E, V, false>(a, b, A, Bc, B, T, D, ws, ws_bytes, s))
+    if (vec > MISCAN_LIN_FWD_BF16_VMAX) vec = MISCAN_LIN_FWD_BF16_VMAX;
+    switch (vec) {
+        case 8: return MISCAN_LIN_FWD(8);
+        case 4: return MISCAN_LIN_FWD(4);
+        case 2: return MISCAN_LIN_FWD(2);
+        default: return MISCAN_LIN_FWD(1);
+    }
+#undef MISCAN_LIN_FWD
+}
+
+template <typename E>
+mi_status bwd_2byte(const void *a, const void *A, const void *Bc, const void *gA, const void *gBc, void *da,
+                    void *db, int64_t B, int64_t T, int64_t D, int vec, void *ws, size_t ws_bytes, hipStream_t s,
+                    bool h0_kernels, const void *h0, void *dh0) {
+#define MISCAN_LIN_BWD(V)                                                                                  \
+    (h0_kernels ? run_bwd<E, V, true>(a, A, Bc, gA, gBc, da, db, B, T, D, ws, ws_bytes, s, h0, dh0)        \
+                : run_bwd<E, V, false>(a, A, Bc, gA, gBc, da, db, B, T, D, ws, ws_bytes, s))
+    if (vec > MISCAN_LIN_BWD_BF16_VMAX) vec = MISCAN_LIN_BWD_BF16_VMAX;
+    switch (vec) {
+        case 8: return MISCAN_LIN_BWD(8);
+        case 4: return MISCAN_LIN_BWD(4);
+        case 2: return MISCAN_LIN_BWD(2);
+        default: return MISCAN_LIN_BWD(1);
+    }
+#undef MISCAN_LIN_BWD
+}
+
+}  // namespace
+
 // h0_kernels: the H0 instantiations (initial state in, dh0 out); h0 may be
 // NULL (zero) there.
 mi_status launch_linear_fwd(const void *a, const void *b, void *A, void *Bc, int64_t B,
                             int64_t T, int64_t D, mi_dtype dt, int vec, void *ws,
                             size_t ws_bytes, hipStream_t s, bool h0_kernels, const void *h0) {
-#define MISCAN_LIN_FWD(E, V)                                                                     \
-    (h0_kernels ? run_fwd<E, V, true>(a, b, A, Bc, B, T, D, ws, ws_bytes, s, h0)                 \
-                : run_fwd<E, V, false>(a, b, A, Bc, B, T, D, ws, ws_bytes, s))
-    if (dt == MI_F32) {
-        switch (vec) {
-            case 4: return MISCAN_LIN_FWD(float, 4);
-            case 2: return MISCAN_LIN_FWD(float, 2);
-            default: return MISCAN_LIN_FWD(float, 1);
-        }
-    }
-    if (vec > MISCAN_LIN_FWD_BF16_VMAX) vec = MISCAN_LIN_FWD_BF16_VMAX;
+    if (dt == MI_BF16) return fwd_2byte<bf16_t>(a, b, A, Bc, B, T, D, vec, ws, ws_bytes, s, h0_kernels, h0);
+    if (dt == MI_F16) return fwd_2byte<f16_t>(a, b, A, Bc, B, T, D, vec, ws, ws_bytes, s, h0_kernels, h0);
+#define MISCAN_LIN_FWD(V)                                                                        \
+    (h0_kernels ? run_fwd<float, V, true>(a, b, A, Bc, B, T, D, ws, ws_bytes, s, h0)             \
+                : run_fwd<float, V, false>(a, b, A, Bc, B, T, D, ws, ws_bytes, s))
     switch (vec) {
-        case 8: return MISCAN_LIN_FWD(bf16_t, 8);
-        case 4: return MISCAN_LIN_FWD(bf16_t, 4);
-        case 2: return MISCAN_LIN_FWD(bf16_t, 2);
-        default: return MISCAN_LIN_FWD(bf16_t, 1);
+        case 4: return MISCAN_LIN_FWD(4);
+        case 2: return MISCAN_LIN_FWD(2);
+        default: return MISCAN_LIN_FWD(1);
     }
 #undef MISCAN_LIN_FWD
 }
@@ -659,22 +691,17 @@ mi_status launch_linear_bwd(const void *a, const void *A, const void *Bc, const 
                             const void *gBc, void *da, void *db, int64_t B, int64_t T,
                             int64_t D, mi_dtype dt, int vec, void *ws, size_t ws_bytes,
                             hipStream_t s, bool h0_kernels, const void *h0, void *dh0) {
-#define MISCAN_LIN_BWD(E, V)                                                                               \
-    (h0_kernels ? run_bwd<E, V, true>(a, A, Bc, gA, gBc, da, db, B, T, D, ws, ws_bytes, s, h0, dh0)        \
-                : run_bwd<E, V, false>(a, A, Bc, gA, gBc, da, db, B, T, D, ws, ws_bytes, s))
-    if (dt == MI_F32) {
-        switch (vec) {
-            case 4: return MISCAN_LIN_BWD(float, 4);
-            case 2: return MISCAN_LIN_BWD(float, 2);
-            default: return MISCAN_LIN_BWD(float, 1);
-        }
-    }
-    if (vec > MISCAN_LIN_BWD_BF16_VMAX) vec = MISCAN_LIN_BWD_BF16_VMAX;
+    if (dt == MI_BF16)
+        return bwd_2byte<bf16_t>(a, A, Bc, gA, gBc, da, db, B, T, D, vec, ws, ws_bytes, s, h0_kernels, h0, dh0);
+    if (dt == MI_F16)
+        return bwd_2byte<f16_t>(a, A, Bc, gA, gBc, da, db, B, T, D, vec, ws, ws_bytes, s, h0_kernels, h0, dh0);
+#define MISCAN_LIN_BWD(V)                                                                                  \
+    (h0_kernels ? run_bwd<float, V, true>(a, A, Bc, gA, gBc, da, db, B, T, D, ws, ws_bytes, s, h0, dh0)    \
+                : run_bwd<float, V, false>(a, A, Bc, gA, gBc, da, db, B, T, D, ws, ws_bytes, s))
     switch (vec) {
-        case 8: return MISCAN_LIN_BWD(bf16_t, 8);
-        case 4: return MISCAN_LIN_BWD(bf16_t, 4);
-        case 2: return MISCAN_LIN_BWD(bf16_t, 2);
-        default: return MISCAN_LIN_BWD(bf16_t, 1);
+        case 4: return MISCAN_LIN_BWD(4);
+        case 2: return MISCAN_LIN_BWD(2);
+        default: return MISCAN_LIN_BWD(1);
     }
 #undef MISCAN_LIN_BWD
 }

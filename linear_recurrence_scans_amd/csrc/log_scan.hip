@@ -57,9 +57,16 @@ struct LogOp {
     }
 };
 
-// Predecessors whose payload loads one look-back round trip issues.
+// Predecessors whose payload loads one look-back round trip issues, and the
+// largest look-back window.  The log scans' workloads have few channel tiles
+// and few chunks, all running at once: a window that reaches the first chunk
+// lets every chunk fold straight from the initial state, with no chain of
+// inclusive states to wait for.
 #ifndef MISCAN_LOG_BATCH
-#define MISCAN_LOG_BATCH 8
+#define MISCAN_LOG_BATCH 16
+#endif
+#ifndef MISCAN_LOG_WMAX
+#define MISCAN_LOG_WMAX 32
 #endif
 
 template <typename T, int VEC, int L, int NW>
@@ -466,7 +473,7 @@ mi_status run_log_bwd(const void *lc, const void *lv, const void *h, const void 
     WsLayout lay(n_slots, 64 * 2 * VEC);
     if (ws == nullptr || ws_bytes < lay.total) return MI_ERR_WORKSPACE;
     p.lc = lc; p.lv = lv; p.h = h; p.g = g; p.dlc = dlc; p.dlv = dlv; p.T = T; p.D = D;
-    p.lb_window = lb_window(p.n_tiles);
+    p.lb_window = lb_window(p.n_tiles, MISCAN_LB_RESIDENT, MISCAN_LOG_WMAX);
     p.ws = ws_ptrs(ws, lay);
     mi_status st = clear_workspace(p.ws, n_slots, s);
     if (st != MI_OK) return st;
@@ -498,7 +505,7 @@ mi_status run_log(const void *lc, const void *lv, void *h, int64_t B, int64_t T,
     WsLayout lay(n_slots, 64 * 2 * VEC);
     if (ws == nullptr || ws_bytes < lay.total) return MI_ERR_WORKSPACE;
     p.lc = lc; p.lv = lv; p.h = h; p.T = T; p.D = D;
-    p.lb_window = lb_window(p.n_tiles);
+    p.lb_window = lb_window(p.n_tiles, MISCAN_LB_RESIDENT, MISCAN_LOG_WMAX);
     p.ws = ws_ptrs(ws, lay);
     mi_status st = clear_workspace(p.ws, n_slots, s);
     if (st != MI_OK) return st;
@@ -516,7 +523,7 @@ size_t log_workspace_bytes(int64_t B, int64_t T, int64_t D, mi_dtype dt) {
     if (dt == MI_F32) {
         upd(log_ws<float, 4>(B, T, D)); upd(log_ws<float, 2>(B, T, D)); upd(log_ws<float, 1>(B, T, D));
         upd(log_bwd_ws<float, 4>(B, T, D)); upd(log_bwd_ws<float, 2>(B, T, D)); upd(log_bwd_ws<float, 1>(B, T, D));
-    } else {
+    } else {  // bf16 and fp16 share their tilings
         upd(log_ws<bf16_t, 8>(B, T, D)); upd(log_ws<bf16_t, 4>(B, T, D));
         upd(log_ws<bf16_t, 2>(B, T, D)); upd(log_ws<bf16_t, 1>(B, T, D));
         upd(log_bwd_ws<bf16_t, 8>(B, T, D)); upd(log_bwd_ws<bf16_t, 4>(B, T, D));
@@ -525,41 +532,55 @@ size_t log_workspace_bytes(int64_t B, int64_t T, int64_t D, mi_dtype dt) {
     return m;
 }
 
+namespace {
+
+template <typename E>
+mi_status log_fwd_2byte(const void *lc, const void *lv, void *h, int64_t B, int64_t T, int64_t D, int vec,
+                        void *ws, size_t ws_bytes, hipStream_t s) {
+    switch (vec) {
+        case 8: return run_log<E, 8>(lc, lv, h, B, T, D, ws, ws_bytes, s);
+        case 4: return run_log<E, 4>(lc, lv, h, B, T, D, ws, ws_bytes, s);
+        case 2: return run_log<E, 2>(lc, lv, h, B, T, D, ws, ws_bytes, s);
+        default: return run_log<E, 1>(lc, lv, h, B, T, D, ws, ws_bytes, s);
+    }
+}
+
+template <typename E>
+mi_status log_bwd_2byte(const void *lc, const void *lv, const void *h, const void *g, void *dlc, void *dlv,
+                        int64_t B, int64_t T, int64_t D, int vec, void *ws, size_t ws_bytes, hipStream_t s) {
+    switch (vec) {
+        case 8: return run_log_bwd<E, 8>(lc, lv, h, g, dlc, dlv, B, T, D, ws, ws_bytes, s);
+        case 4: return run_log_bwd<E, 4>(lc, lv, h, g, dlc, dlv, B, T, D, ws, ws_bytes, s);
+        case 2: return run_log_bwd<E, 2>(lc, lv, h, g, dlc, dlv, B, T, D, ws, ws_bytes, s);
+        default: return run_log_bwd<E, 1>(lc, lv, h, g, dlc, dlv, B, T, D, ws, ws_bytes, s);
+    }
+}
+
+}  // namespace
+
 mi_status launch_log_fwd(const void *lc, const void *lv, void *h, int64_t B, int64_t T,
                          int64_t D, mi_dtype dt, int vec, void *ws, size_t ws_bytes,
                          hipStream_t s) {
-    if (dt == MI_F32) {
-        if (vec > MISCAN_LOG_F32_VMAX) vec = MISCAN_LOG_F32_VMAX;
-        switch (vec) {
-            case 4: return run_log<float, 4>(lc, lv, h, B, T, D, ws, ws_bytes, s);
-            case 2: return run_log<float, 2>(lc, lv, h, B, T, D, ws, ws_bytes, s);
-            default: return run_log<float, 1>(lc, lv, h, B, T, D, ws, ws_bytes, s);
-        }
-    }
+    if (dt == MI_BF16) return log_fwd_2byte<bf16_t>(lc, lv, h, B, T, D, vec, ws, ws_bytes, s);
+    if (dt == MI_F16) return log_fwd_2byte<f16_t>(lc, lv, h, B, T, D, vec, ws, ws_bytes, s);
+    if (vec > MISCAN_LOG_F32_VMAX) vec = MISCAN_LOG_F32_VMAX;
     switch (vec) {
-        case 8: return run_log<bf16_t, 8>(lc, lv, h, B, T, D, ws, ws_bytes, s);
-        case 4: return run_log<bf16_t, 4>(lc, lv, h, B, T, D, ws, ws_bytes, s);
-        case 2: return run_log<bf16_t, 2>(lc, lv, h, B, T, D, ws, ws_bytes, s);
-        default: return run_log<bf16_t, 1>(lc, lv, h, B, T, D, ws, ws_bytes, s);
+        case 4: return run_log<float, 4>(lc, lv, h, B, T, D, ws, ws_bytes, s);
+        case 2: return run_log<float, 2>(lc, lv, h, B, T, D, ws, ws_bytes, s);
+        default: return run_log<float, 1>(lc, lv, h, B, T, D, ws, ws_bytes, s);
     }
 }
 
 mi_status launch_log_bwd(const void *lc, const void *lv, const void *h, const void *g, void *dlc, void *dlv,
                          int64_t B, int64_t T, int64_t D, mi_dtype dt, int vec, void *ws, size_t ws_bytes,
                          hipStream_t s) {
-    if (dt == MI_F32) {
-        if (vec > MISCAN_LOG_F32_VMAX) vec = MISCAN_LOG_F32_VMAX;
-        switch (vec) {
-            case 4: return run_log_bwd<float, 4>(lc, lv, h, g, dlc, dlv, B, T, D, ws, ws_bytes, s);
-            case 2: return run_log_bwd<float, 2>(lc, lv, h, g, dlc, dlv, B, T, D, ws, ws_bytes, s);
-            default: return run_log_bwd<float, 1>(lc, lv, h, g, dlc, dlv, B, T, D, ws, ws_bytes, s);
-        }
-    }
+    if (dt == MI_BF16) return log_bwd_2byte<bf16_t>(lc, lv, h, g, dlc, dlv, B, T, D, vec, ws, ws_bytes, s);
+    if (dt == MI_F16) return log_bwd_2byte<f16_t>(lc, lv, h, g, dlc, dlv, B, T, D, vec, ws, ws_bytes, s);
+    if (vec > MISCAN_LOG_F32_VMAX) vec = MISCAN_LOG_F32_VMAX;
     switch (vec) {
-        case 8: return run_log_bwd<bf16_t, 8>(lc, lv, h, g, dlc, dlv, B, T, D, ws, ws_bytes, s);
-        case 4: return run_log_bwd<bf16_t, 4>(lc, lv, h, g, dlc, dlv, B, T, D, ws, ws_bytes, s);
-        case 2: return run_log_bwd<bf16_t, 2>(lc, lv, h, g, dlc, dlv, B, T, D, ws, ws_bytes, s);
-        default: return run_log_bwd<bf16_t, 1>(lc, lv, h, g, dlc, dlv, B, T, D, ws, ws_bytes, s);
+        case 4: return run_log_bwd<float, 4>(lc, lv, h, g, dlc, dlv, B, T, D, ws, ws_bytes, s);
+        case 2: return run_log_bwd<float, 2>(lc, lv, h, g, dlc, dlv, B, T, D, ws, ws_bytes, s);
+        default: return run_log_bwd<float, 1>(lc, lv, h, g, dlc, dlv, B, T, D, ws, ws_bytes, s);
     }
 }
 

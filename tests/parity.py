@@ -13,13 +13,20 @@ Error readings (the pages give only "max relative error"):
   * any non-finite GPU value where the oracle is finite is an infinite error.
   * 2^-100 only matters where the true value underflows fp32 (running
     products of hundreds of factors below one).
-Tolerances: 1e-5 for fp32 storage, 2e-2 for bf16 storage with fp32 arithmetic.
+Tolerances: 1e-5 for fp32 storage, 2e-2 for bf16 storage with fp32 arithmetic,
+and 2.5e-3 for fp16 storage with fp32 arithmetic: the bf16 bar scaled by the
+ratio of the two formats' unit roundoffs (2^-11 / 2^-8).  With fp16 storage the
+denominator is at least 2^-14, fp16's smallest normal: below it the format
+keeps only an absolute precision of 2^-25 (its subnormal grid), so outputs
+there are compared to that grid rather than to their own magnitude.
 """
 import numpy as np
 import torch
 
-TOL = {torch.float32: 1e-5, torch.bfloat16: 2e-2}
+TOL = {torch.float32: 1e-5, torch.bfloat16: 2e-2, torch.float16: 2.5e-3}
 TINY = 2.0 ** -100
+# Smallest error denominator per storage type (see above).
+FLOOR = {torch.float32: TINY, torch.bfloat16: TINY, torch.float16: 2.0 ** -14}
 
 
 def quantise(x: np.ndarray, dtype):
@@ -32,11 +39,12 @@ def to_np(t: torch.Tensor) -> np.ndarray:
     return t.detach().double().cpu().numpy()
 
 
-def scaled_err(g: np.ndarray, r: np.ndarray, s: np.ndarray) -> float:
+def scaled_err(g: np.ndarray, r: np.ndarray, s: np.ndarray, floor: float = TINY) -> float:
     g = np.asarray(g, dtype=np.float64)
     if np.any(~np.isfinite(g) & np.isfinite(r)):
         return float("inf")
-    return float(np.max(np.abs(g - r) / (np.abs(s) + TINY))) if g.size else 0.0
+    den = np.maximum(np.abs(s) + TINY, floor)
+    return float(np.max(np.abs(g - r) / den)) if g.size else 0.0
 
 
 def block_err(G: np.ndarray, R: np.ndarray) -> float:

@@ -18,7 +18,7 @@ HEADER = os.path.join(ROOT, "include", "miscan.h")
 
 (MI_OK, MI_ERR_INVALID_ARG, MI_ERR_UNSUPPORTED, MI_ERR_WORKSPACE, MI_ERR_LAUNCH, MI_ERR_DEVICE,
  MI_ERR_CAPACITY) = range(7)
-F32, BF16 = 0, 1
+F32, BF16, F16 = 0, 1, 2
 P = 1 << 20        # fake, 256-byte aligned "device" addresses; never dereferenced
 STEP = 1 << 30     # far apart: no overlap unless a test wants one
 
@@ -89,6 +89,9 @@ def test_linear_fwd_validation():
     assert fwd(a, b, A, Bc, 1, 4, 4, dt=7) == MI_ERR_UNSUPPORTED            # unknown dtype
     assert fwd(a + 2, b, A, Bc, 1, 4, 4, ws=ws, wsb=big) == MI_ERR_INVALID_ARG  # misaligned f32
     assert fwd(a + 2, b, A, Bc, 1, 4, 4, dt=BF16, ws=None) == MI_ERR_WORKSPACE  # bf16 aligned ok
+    assert fwd(a + 2, b, A, Bc, 1, 4, 4, dt=F16, ws=None) == MI_ERR_WORKSPACE   # fp16 too
+    assert fwd(a + 1, b, A, Bc, 1, 4, 4, dt=F16, ws=ws, wsb=big) == MI_ERR_INVALID_ARG  # odd address
+    assert fwd(a, b, A, Bc, 1, 4, 4, dt=3) == MI_ERR_UNSUPPORTED
     assert fwd(a, b, a + 8, Bc, 1, 4, 4, ws=ws, wsb=big) == MI_ERR_INVALID_ARG  # output overlaps input
     assert fwd(a, b, A, A + 4, 1, 4, 4, ws=ws, wsb=big) == MI_ERR_INVALID_ARG  # outputs overlap
     assert fwd(a, b, A, Bc, 1, 4, 4, ws=None) == MI_ERR_WORKSPACE           # no workspace
@@ -191,6 +194,7 @@ def test_affine_envelope():
     assert call(4, 0) == MI_ERR_UNSUPPORTED
     assert call(4, 129) == MI_ERR_UNSUPPORTED
     assert call(4, 4, BF16) == MI_ERR_WORKSPACE      # bf16 storage is inside the envelope
+    assert call(4, 4, F16) == MI_ERR_WORKSPACE       # and fp16
     assert call(4, 4, 7) == MI_ERR_UNSUPPORTED       # unknown dtype
     assert call(16, 128) == MI_ERR_WORKSPACE        # inside the envelope
     assert call(1, 1) == MI_ERR_WORKSPACE
@@ -201,7 +205,7 @@ def test_affine_envelope():
 def test_workspace_sizes_cover_every_shape():
     L = lib()
     for Bn, T, D in ((1, 1, 1), (1, 1024, 64), (8, 8192, 4096), (3, 1000, 100)):
-        for dt in (F32, BF16):
+        for dt in (F32, BF16, F16):
             w = L.mi_linear_scan_workspace(Bn, T, D, dt)
             assert w >= 256 + 256
             assert L.mi_scan_log_workspace(Bn, T, D, dt) >= 512

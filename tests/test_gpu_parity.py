@@ -13,7 +13,7 @@ import torch
 
 import linear_recurrence_scans_amd as lrs
 import oracle
-from parity import TOL, block_err, quantise, scaled_err, timeouts, to_np
+from parity import FLOOR, TOL, block_err, quantise, scaled_err, timeouts, to_np
 from workloads import (affine_inputs_diag, affine_inputs_rotation, linear_inputs, log_inputs,
                        workload_inputs)
 
@@ -50,7 +50,7 @@ def run_linear(x, dtype, with_bwd=True, check_ws=True):
         assert timeouts(ws) == 0
     A_r, Bc_r = oracle.linear_scan_fwd(a, b)
     _, Bc_s = oracle.linear_scan_fwd(np.abs(a), np.abs(b))
-    errs = {"A": scaled_err(to_np(A_d), A_r, A_r), "Bc": scaled_err(to_np(Bc_d), Bc_r, Bc_s)}
+    errs = {"A": scaled_err(to_np(A_d), A_r, A_r, FLOOR[dtype]), "Bc": scaled_err(to_np(Bc_d), Bc_r, Bc_s, FLOOR[dtype])}
     if with_bwd:
         # backward inputs: the oracle's forward states, quantised like any input
         A_in_d, A_in = quantise(A_r, dtype)
@@ -64,8 +64,8 @@ def run_linear(x, dtype, with_bwd=True, check_ws=True):
         da_r, db_r = oracle.linear_scan_bwd(a, A_in, Bc_in, gA, gB)
         da_s, db_s = oracle.linear_scan_bwd(np.abs(a), np.abs(A_in), np.abs(Bc_in), np.abs(gA),
                                             np.abs(gB))
-        errs["da"] = scaled_err(to_np(da_d), da_r, da_s)
-        errs["db"] = scaled_err(to_np(db_d), db_r, db_s)
+        errs["da"] = scaled_err(to_np(da_d), da_r, da_s, FLOOR[dtype])
+        errs["db"] = scaled_err(to_np(db_d), db_r, db_s, FLOOR[dtype])
     return errs
 
 
@@ -297,7 +297,7 @@ def run_log(x, dtype):
     torch.cuda.synchronize()
     assert timeouts(ws) == 0
     h_r = oracle.scan_log_fwd_logspace(lc, lv)
-    return scaled_err(to_np(h_d), h_r, h_r)
+    return scaled_err(to_np(h_d), h_r, h_r, FLOOR[dtype])
 
 
 @pytest.mark.parametrize("seed", [2, 12])
@@ -348,7 +348,7 @@ def run_log_bwd(x, dtype, seed=0):
     assert timeouts(ws) == 0
     dlc_r, dlv_r = oracle.scan_log_bwd(lc, lv, h, g)
     dlc_s, dlv_s = oracle.scan_log_bwd(lc, lv, h, np.abs(g))  # every other factor is positive
-    return {"dlc": scaled_err(to_np(dlc_d), dlc_r, dlc_s), "dlv": scaled_err(to_np(dlv_d), dlv_r, dlv_s)}
+    return {"dlc": scaled_err(to_np(dlc_d), dlc_r, dlc_s, FLOOR[dtype]), "dlv": scaled_err(to_np(dlv_d), dlv_r, dlv_s, FLOOR[dtype])}
 
 
 @pytest.mark.parametrize("seed", [2, 12])
@@ -450,8 +450,8 @@ def run_affine(x, with_bwd, metric, dtype=torch.float32):
     else:
         Abar_s, Bbar_s = oracle.affine_scan_fwd(np.abs(A), np.abs(Bm))
         assert np.all(np.isfinite(Abar_s)) and np.all(np.isfinite(Bbar_s))
-        errs = {"Abar": scaled_err(to_np(Abar_d), Abar_r, Abar_s),
-                "Bbar": scaled_err(to_np(Bbar_d), Bbar_r, Bbar_s)}
+        errs = {"Abar": scaled_err(to_np(Abar_d), Abar_r, Abar_s, FLOOR[dtype]),
+                "Bbar": scaled_err(to_np(Bbar_d), Bbar_r, Bbar_s, FLOOR[dtype])}
     if with_bwd:
         assert metric == "abs"
         Ab_in_d, Ab_in = quantise(Abar_r, dtype)
@@ -465,8 +465,8 @@ def run_affine(x, with_bwd, metric, dtype=torch.float32):
         dA_s, dB_s = oracle.affine_scan_bwd(np.abs(A), np.abs(Ab_in), np.abs(Bb_in), np.abs(gA),
                                             np.abs(gB))
         assert np.all(np.isfinite(dA_s)) and np.all(np.isfinite(dB_s))
-        errs["dA"] = scaled_err(to_np(dA_d), dA_r, dA_s)
-        errs["dB"] = scaled_err(to_np(dB_d), dB_r, dB_s)
+        errs["dA"] = scaled_err(to_np(dA_d), dA_r, dA_s, FLOOR[dtype])
+        errs["dB"] = scaled_err(to_np(dB_d), dB_r, dB_s, FLOOR[dtype])
     return errs
 
 
@@ -633,3 +633,54 @@ def test_affine_repeated_runs():
         else:
             for f, o in zip(first, outs):
                 assert np.array_equal(f, o), run
+
+
+# ---------------------------------------------------------------------------
+# fp16 storage (fp32 arithmetic) for every op
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("shape", [(2, 1000, 4104), (1, 77, 37), (3, 33, 6), (2, 300, 512)])
+def test_linear_f16(shape):
+    """fp16 storage on the workload-3 distribution; D values pick the 8-, 1-
+    and 2-wide vector kernels and ragged tiles."""
+    say("linear fwd+bwd fp16 shape", shape)
+    errs = run_linear(lin_case(*shape, seed=29, a_lo=0.9, a_hi=0.9999), torch.float16)
+    assert max(errs.values()) <= TOL[torch.float16], (shape, errs)
+
+
+def test_linear_f16_workload3_size():
+    """fp16 storage at the workload-3 size (B=8, T=8192, D=4096)."""
+    say("linear fwd+bwd fp16 B=8 T=8192 D=4096 seed 3")
+    errs = run_linear(workload_inputs(3), torch.float16)
+    print("errors", errs, flush=True)
+    assert max(errs.values()) <= TOL[torch.float16], errs
+
+
+@pytest.mark.parametrize("shape", [(2, 500, 136), (1, 77, 37), (4, 4096, 512)])
+def test_log_f16(shape):
+    """Log-space forward and backward with fp16 storage (the last shape is the
+    workload-2 size)."""
+    say("log fwd+bwd fp16 shape", shape)
+    x = log_inputs(*shape, seed=31)
+    e = run_log(x, torch.float16)
+    assert e <= TOL[torch.float16], (shape, e)
+    errs = run_log_bwd(x, torch.float16, 31)
+    assert max(errs.values()) <= TOL[torch.float16], (shape, errs)
+
+
+@pytest.mark.parametrize("kv", [(4, 16), (8, 32), (3, 5), (2, 2), (16, 8)])
+def test_affine_f16(kv):
+    """k x k forward and backward with fp16 storage."""
+    k, v = kv
+    for (Bn, T, n) in ((1, 1, 1), (2, 300, 5)):
+        say("affine fwd+bwd fp16 B,T,n,k,v =", (Bn, T, n, k, v))
+        x = affine_inputs_diag(Bn, T, n, k, v, seed=k * 11 + v + T, grads=True)
+        errs = run_affine(x, with_bwd=True, metric="abs", dtype=torch.float16)
+        assert max(errs.values()) <= TOL[torch.float16], ((Bn, T, n, k, v), errs)
+
+
+def test_affine_f16_workload5_size():
+    say("affine fwd+bwd fp16 at workload-5 size")
+    errs = run_affine(workload_inputs(5), with_bwd=True, metric="abs", dtype=torch.float16)
+    print("errors", errs, flush=True)
+    assert max(errs.values()) <= TOL[torch.float16], errs
