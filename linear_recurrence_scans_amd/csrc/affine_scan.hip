@@ -1027,10 +1027,13 @@ __global__ __launch_bounds__(512) void affine_bwd_kernel(BwdArgs p) {
                         if (i < k && cl.kind[cc] == Z_L) st1(static_cast<TS *>(p.dB) + m * k * v + i * v + cl.col[cc], S[i][cc]);
             }
         }
-        // dA_t = Y_t X_{t-1}^T, RB rows a round
+        // dA_t = Y_t X_{t-1}^T, RB rows a round.  Lanes that hold only P
+        // columns (g < k / CPL) contribute zeros: they store no partial sums
+        // and the readers skip their slots.
+        const int g_first = k / CPL;
 #pragma unroll
         for (int ib = 0; ib < KP; ib += RB) {
-            if (slot_lane) {
+            if (slot_lane && g >= g_first) {
 #pragma unroll
                 for (int ii = 0; ii < RB; ++ii) {
                     float row[KP];
@@ -1054,7 +1057,7 @@ __global__ __launch_bounds__(512) void affine_bwd_kernel(BwdArgs p) {
                         const int ii = e / KP, j0 = e - (e / KP) * KP;
                         const int i = ib + ii;
                         float acc[4] = {0.f, 0.f, 0.f, 0.f};
-                        for (int gg = 0; gg < G; ++gg) {
+                        for (int gg = g_first; gg < G; ++gg) {
                             float q[4];
                             ldv<4>(q, part + (hs * G + gg) * PS + ii * KP + j0);
 #pragma unroll
@@ -1073,7 +1076,7 @@ __global__ __launch_bounds__(512) void affine_bwd_kernel(BwdArgs p) {
                         const int ii = e / KP, j = e - (e / KP) * KP;
                         const int i = ib + ii;
                         float acc = 0.f;
-                        for (int gg = 0; gg < G; ++gg) acc += part[(hs * G + gg) * PS + ii * KP + j];
+                        for (int gg = g_first; gg < G; ++gg) acc += part[(hs * G + gg) * PS + ii * KP + j];
                         if (i < k && j < k) st1(static_cast<TS *>(p.dA) + m * k * k + (int64_t)i * k + j, acc);
                     }
                 }
