@@ -274,58 +274,92 @@ struct SlotMap {
     __device__ __forceinline__ int64_t head(int grp, int s) const { return (int64_t)grp * HH + s % HH; }
 };
 
+// Loads a thread issues before its first LDS write when staging A: a batch
+// of loads in flight together instead of a round trip each.  Sized to what a
+// thread stages at padded k = 8 (six float4s on 3 heads x 32 steps) and half
+// that at k = 4; the backward's chunks are shorter (two float4s a thread on
+// 2 heads x 16 steps), and a batch of two keeps it at three waves per SIMD.  Other tiles keep one load at a
+// time: they stage little A per thread (k <= 2) or have no registers to
+// spare (k = 16).
+#ifndef MISCAN_AFF_STAGE_BATCH
+#define MISCAN_AFF_STAGE_BATCH 8
+#endif
+#ifndef MISCAN_AFF_BWD_STAGE_BATCH
+#define MISCAN_AFF_BWD_STAGE_BATCH 2
+#endif
+__host__ __device__ constexpr int aff_stage_batch(int KP, bool bwd) {
+    if (KP < 4 || KP > 8) return 1;
+    return bwd ? MISCAN_AFF_BWD_STAGE_BATCH : KP == 8 ? MISCAN_AFF_STAGE_BATCH : MISCAN_AFF_STAGE_BATCH / 2;
+}
+
 // A_t of every slot for the CHW rows of its segment into LDS, laid out
 // [row][slot][AS] with AS = pad_bank(KP * KP) (each block zero padded to
 // KP x KP; identity for steps past T and for heads past the last).
 // Cooperative, coalesced: consecutive threads take consecutive float4s (or
-// floats) of the source blocks.
+// floats) of the source blocks.  Each thread issues a batch of loads before
+// it writes any of them.
 template <typename TS, int KP, bool VIO>
 __device__ __forceinline__ void stage_a(float *s_A, const FwdArgs &p, const SlotMap &sm, int grp, int64_t t_c) {
     const TS *Ag = static_cast<const TS *>(p.A);
     constexpr int KK = KP * KP;
     constexpr int AS = pad_bank(KK);
+    constexpr int NB = aff_stage_batch(KP, false);
+    constexpr int EPT = (VIO && KK % 4 == 0) ? 4 : 1;  // elements a thread moves per access
+    using PK = Pack<TS, EPT>;
     const int per_row = p.HPW * KK;
     const int total = sm.CHW * per_row;
-    if constexpr (VIO && KK % 4 == 0) {
-        for (int e = (int)threadIdx.x * 4; e < total; e += (int)blockDim.x * 4) {
-            const int q = e / per_row;
-            const int rem = e - q * per_row;
+    const int step = (int)blockDim.x * EPT;
+    const int k = VIO ? KP : p.k;
+    // One batch: NB accesses starting at e0, every `step` elements.  Every
+    // access loads (elements outside the tensor from its first element) and
+    // the identity is selected at the write: no branch around a load, so the
+    // batch's loads are all in flight before the first write waits.  The
+    // first batch is straight-line code: in a loop the compiler waits for
+    // every load in flight (the caller's too) before the loop's first load.
+    auto batch = [&](int e0) {
+        typename PK::raw_t raw[NB];
+        int dst[NB], off[NB];
+        bool in[NB];
+#pragma unroll
+        for (int u = 0; u < NB; ++u) {
+            const int e = e0 + u * step;
+            const bool valid = e < total;
+            const int ec = valid ? e : 0;
+            const int q = ec / per_row;
+            const int rem = ec - q * per_row;
             const int hs = rem / KK;
             const int o = rem - hs * KK;
             const int64_t t = sm.t(t_c, hs, q);
             const int64_t gh = sm.head(grp, hs);
-            f32x4 val;
-            if (t < p.T && gh < p.heads) {
-                const int64_t b = gh / p.n, h = gh - b * p.n;
-                float w[4];
-                ld_g<TS, 4>(w, Ag + ((b * p.T + t) * p.n + h) * KK + o);
-                val.x = w[0]; val.y = w[1]; val.z = w[2]; val.w = w[3];
-            } else {
-                val.x = (o / KP == o % KP) ? 1.f : 0.f;
-                val.y = ((o + 1) / KP == (o + 1) % KP) ? 1.f : 0.f;
-                val.z = ((o + 2) / KP == (o + 2) % KP) ? 1.f : 0.f;
-                val.w = ((o + 3) / KP == (o + 3) % KP) ? 1.f : 0.f;
-            }
-            *reinterpret_cast<f32x4 *>(s_A + (q * p.HPW + hs) * AS + o) = val;
-        }
-    } else {
-        const int k = p.k;
-        for (int e = (int)threadIdx.x; e < total; e += (int)blockDim.x) {
-            const int q = e / per_row;
-            const int rem = e - q * per_row;
-            const int hs = rem / KK;
-            const int o = rem - hs * KK;
             const int i = o / KP, j = o - (o / KP) * KP;
-            const int64_t t = sm.t(t_c, hs, q);
-            const int64_t gh = sm.head(grp, hs);
-            float val = (i == j) ? 1.f : 0.f;
-            if (t < p.T && gh < p.heads && i < k && j < k) {
-                const int64_t b = gh / p.n, h = gh - b * p.n;
-                val = ld1(Ag + ((b * p.T + t) * p.n + h) * k * k + i * k + j);
-            }
-            s_A[(q * p.HPW + hs) * AS + o] = val;
+            in[u] = valid && t < p.T && gh < p.heads && (EPT == 4 || (i < k && j < k));
+            const int64_t b = in[u] ? gh / p.n : 0, h = in[u] ? gh - b * p.n : 0;
+            const TS *src = Ag;
+            if (in[u]) src = EPT == 4 ? Ag + ((b * p.T + t) * p.n + h) * KK + o
+                                      : Ag + ((b * p.T + t) * p.n + h) * k * k + i * k + j;
+            raw[u] = load_vec<TS, EPT>(src);
+            dst[u] = valid ? (q * p.HPW + hs) * AS + o : -1;
+            off[u] = o;
         }
-    }
+#pragma unroll
+        for (int u = 0; u < NB; ++u) {
+            if (dst[u] < 0) continue;
+            float w[EPT];
+            PK::unpack(raw[u], w);
+#pragma unroll
+            for (int c = 0; c < EPT; ++c) {
+                const int o = off[u] + c;
+                w[c] = in[u] ? w[c] : (o / KP == o % KP ? 1.f : 0.f);  // identity padding
+            }
+            if constexpr (EPT == 4)
+                *reinterpret_cast<f32x4 *>(s_A + dst[u]) = f32x4{w[0], w[1], w[2], w[3]};
+            else
+                s_A[dst[u]] = w[0];
+        }
+    };
+    const int e_first = (int)threadIdx.x * EPT;
+    batch(e_first);
+    for (int e0 = e_first + NB * step; e0 < total; e0 += NB * step) batch(e0);
 }
 
 // x <- A x + b for the lane's columns, A a KP x KP block in LDS.  b is zero
@@ -413,6 +447,20 @@ __device__ __forceinline__ void block_apply(float (&S)[KP][CPL], const float *bl
     }, k, is_h);
 }
 
+// Float4s of look-back payload a thread loads per round trip, from each of
+// the two arrays: the forward at padded k = 8 stages about three a thread
+// (3 heads x 8 x 40 floats, 3 aggregates); smaller k stage under one, and the
+// batch's registers would cost those kernels a wave per SIMD.
+#ifndef MISCAN_AFF_PAYLOAD_BATCH
+#define MISCAN_AFF_PAYLOAD_BATCH 4
+#endif
+#ifndef MISCAN_AFF_BWD_PAYLOAD_BATCH
+#define MISCAN_AFF_BWD_PAYLOAD_BATCH 1
+#endif
+__host__ __device__ constexpr int aff_payload_batch(int KP, bool bwd) {
+    return bwd ? MISCAN_AFF_BWD_PAYLOAD_BATCH : KP == 8 ? MISCAN_AFF_PAYLOAD_BATCH : 1;
+}
+
 // Look-back payloads into LDS, cooperatively: one round trip for a batch of
 // up to DB published blocks instead of one per block.  A chunk folds n_wait
 // predecessors; fold index q = 0 is the farthest (slot + n_wait dir) and, if
@@ -421,32 +469,44 @@ __device__ __forceinline__ void block_apply(float (&S)[KP][CPL], const float *bl
 // dir).  That is time order for the forward (dir = -1) and reverse time
 // order for the adjoint (dir = +1).  The batch holds fold indices b0 .. b0 +
 // nb - 1, index q at s_stage + (q - b0) * slot_sz.  Its slots are
-// consecutive, so each array is read through one descriptor.
+// consecutive, so each array is read through one descriptor; the loads from
+// both arrays go out together before any is written to LDS.
+template <int NB>
 __device__ __forceinline__ void stage_payloads(float *s_stage, const WsPtrs &ws, int64_t slot, int dir,
                                                const LbPos &lq, int b0, int nb, int slot_sz) {
     const int tid = threadIdx.x, nt = blockDim.x;
     const int n_wait = lq.n_wait;
-    int first = b0;
-    if (b0 == 0 && lq.has_inc) {  // fold index 0: the inclusive state of slot + n_wait dir
-        const rsrc_t r = make_rows(ws.inc + (slot + (int64_t)dir * n_wait) * slot_sz, (int64_t)slot_sz * 4);
-        for (int e = tid * 4; e < slot_sz; e += nt * 4) {
-            float v[4];
-            carry_load_vec<4>(v, r, 4u * (uint32_t)e);
-            *reinterpret_cast<f32x4 *>(s_stage + e) = f32x4{v[0], v[1], v[2], v[3]};
-        }
-        first = 1;
-    }
+    const bool inc = b0 == 0 && lq.has_inc;  // fold index 0: the inclusive state of slot + n_wait dir
+    const int first = inc ? 1 : b0;
     const int last = b0 + nb - 1;
     const int na = last - first + 1;  // aggregates in this batch
-    if (na > 0) {
-        const int64_t lo = dir < 0 ? slot - n_wait + first : slot + n_wait - last;  // lowest slot
-        const rsrc_t r = make_rows(ws.agg + lo * slot_sz, (int64_t)na * slot_sz * 4);
-        for (int e = tid * 4; e < na * slot_sz; e += nt * 4) {
-            const int a = e / slot_sz, off = e - a * slot_sz;  // slot lo + a
-            const int q = dir < 0 ? first + a : last - a;       // its fold index
-            float v[4];
-            carry_load_vec<4>(v, r, 4u * (uint32_t)e);
-            *reinterpret_cast<f32x4 *>(s_stage + (q - b0) * slot_sz + off) = f32x4{v[0], v[1], v[2], v[3]};
+    const int inc_len = inc ? slot_sz : 0;
+    const int agg_len = na > 0 ? na * slot_sz : 0;
+    const int64_t lo = dir < 0 ? slot - n_wait + first : slot + n_wait - last;  // lowest aggregate slot
+    const rsrc_t ri = make_rows(ws.inc + (slot + (int64_t)dir * n_wait) * slot_sz, (int64_t)inc_len * 4);
+    const rsrc_t ra = make_rows(ws.agg + (na > 0 ? lo : slot) * slot_sz, (int64_t)agg_len * 4);
+    for (int e0 = tid * 4; e0 < inc_len || e0 < agg_len; e0 += nt * 4 * NB) {
+        float vi[NB][4], va[NB][4];
+#pragma unroll
+        for (int u = 0; u < NB; ++u)
+            if (e0 + u * nt * 4 < inc_len) carry_load_vec<4>(vi[u], ri, 4u * (uint32_t)(e0 + u * nt * 4));
+#pragma unroll
+        for (int u = 0; u < NB; ++u)
+            if (e0 + u * nt * 4 < agg_len) carry_load_vec<4>(va[u], ra, 4u * (uint32_t)(e0 + u * nt * 4));
+#pragma unroll
+        for (int u = 0; u < NB; ++u) {
+            const int e = e0 + u * nt * 4;
+            if (e < inc_len) *reinterpret_cast<f32x4 *>(s_stage + e) = f32x4{vi[u][0], vi[u][1], vi[u][2], vi[u][3]};
+        }
+#pragma unroll
+        for (int u = 0; u < NB; ++u) {
+            const int e = e0 + u * nt * 4;
+            if (e < agg_len) {
+                const int a = e / slot_sz, off = e - a * slot_sz;  // slot lo + a
+                const int q = dir < 0 ? first + a : last - a;       // its fold index
+                *reinterpret_cast<f32x4 *>(s_stage + (q - b0) * slot_sz + off) =
+                    f32x4{va[u][0], va[u][1], va[u][2], va[u][3]};
+            }
         }
     }
 }
@@ -606,7 +666,7 @@ __global__ __launch_bounds__(512) void affine_fwd_kernel(FwdArgs p) {
         lds_barrier();
         for (int b0 = 0; b0 < lq.n_wait; b0 += p.DB) {
             const int nb = lq.n_wait - b0 < p.DB ? lq.n_wait - b0 : p.DB;
-            stage_payloads(s_stage, p.ws, slot, -1, lq, b0, nb, slot_sz);
+            stage_payloads<aff_payload_batch(KP, false)>(s_stage, p.ws, slot, -1, lq, b0, nb, slot_sz);
             lds_barrier();
             if (wave == 0) {
                 int q = b0;
@@ -750,56 +810,66 @@ __device__ __forceinline__ void load_xprev(float (&x)[KP][CPL], const BwdArgs &p
 // A_{t+1}^T for the CH steps t of the chunk into LDS, [step][head][AS] like
 // stage_a: zero for t = T - 1 (A_{T+1} = 0 in the page's 1-based time) and the
 // identity for steps past T or heads past the last.  Sources are read as
-// float4 rows and written transposed.
+// float4 rows and written transposed.  Batched like stage_a.
 template <typename TS, int KP, bool VIO>
 __device__ __forceinline__ void stage_at(float *s_A, const BwdArgs &p, int grp, int64_t t_c, int CH) {
     const TS *Ag = static_cast<const TS *>(p.A);
     constexpr int KK = KP * KP;
     constexpr int AS = pad_bank(KK);
+    constexpr int NB = aff_stage_batch(KP, true);
+    constexpr int EPT = (VIO && KP % 4 == 0) ? 4 : 1;  // elements a thread moves per access
+    using PK = Pack<TS, EPT>;
     const int per_step = p.HPW * KK;
     const int total = CH * per_step;
     const int k = VIO ? KP : p.k;
-    if constexpr (VIO && KP % 4 == 0) {
-        for (int e = (int)threadIdx.x * 4; e < total; e += (int)blockDim.x * 4) {
-            const int s = e / per_step;
-            const int rem = e - s * per_step;
+    const int step = (int)blockDim.x * EPT;
+    auto batch = [&](int e0) {  // as in stage_a
+        typename PK::raw_t raw[NB];
+        int dst[NB], jr[NB], i0[NB];
+        float d[NB];
+        bool in[NB];
+#pragma unroll
+        for (int u = 0; u < NB; ++u) {
+            const int e = e0 + u * step;
+            const bool valid = e < total;
+            const int ec = valid ? e : 0;
+            const int st = ec / per_step;
+            const int rem = ec - st * per_step;
             const int hs = rem / KK;
             const int q = rem - hs * KK;
-            const int jr = q / KP, i0 = q - jr * KP;  // source row jr, columns i0 .. i0 + 3
-            const int64_t t = t_c + s;
+            const int64_t t = t_c + st;
             const int64_t gh = (int64_t)grp * p.HPW + hs;
-            float val[4];
-            if (t + 1 < p.T && gh < p.heads) {
-                const int64_t b = gh / p.n, h = gh - b * p.n;
-                ld_g<TS, 4>(val, Ag + ((b * p.T + t + 1) * p.n + h) * KK + q);
-            } else {
-                const float d = (t < p.T && gh < p.heads) ? 0.f : 1.f;  // A_{T+1} = 0, identity elsewhere
-#pragma unroll
-                for (int u = 0; u < 4; ++u) val[u] = (i0 + u == jr) ? d : 0.f;
-            }
-            float *dst = s_A + (s * p.HPW + hs) * AS;
-#pragma unroll
-            for (int u = 0; u < 4; ++u) dst[(i0 + u) * KP + jr] = val[u];
+            // EPT == 4: source row jr, columns i0 .. i0 + 3, written transposed;
+            // EPT == 1: element (i0, jr) of A^T = A[jr][i0]
+            jr[u] = EPT == 4 ? q / KP : q - (q / KP) * KP;
+            i0[u] = EPT == 4 ? q - (q / KP) * KP : q / KP;
+            in[u] = valid && t + 1 < p.T && gh < p.heads && (EPT == 4 || (i0[u] < k && jr[u] < k));
+            // diagonal where nothing loads: 0 at a head's last step (A_{T+1} = 0),
+            // 1 elsewhere (steps past T, heads past the last, padding of k)
+            d[u] = (gh < p.heads && t == p.T - 1) ? 0.f : 1.f;
+            const int64_t b = in[u] ? gh / p.n : 0, h = in[u] ? gh - b * p.n : 0;
+            const TS *src = Ag;
+            if (in[u]) src = EPT == 4 ? Ag + ((b * p.T + t + 1) * p.n + h) * KK + q
+                                      : Ag + ((b * p.T + t + 1) * p.n + h) * k * k + jr[u] * k + i0[u];
+            raw[u] = load_vec<TS, EPT>(src);
+            dst[u] = valid ? (st * p.HPW + hs) * AS + (EPT == 4 ? i0[u] * KP + jr[u] : q) : -1;
         }
-    } else {
-        for (int e = (int)threadIdx.x; e < total; e += (int)blockDim.x) {
-            const int s = e / per_step;
-            const int rem = e - s * per_step;
-            const int hs = rem / KK;
-            const int q = rem - hs * KK;
-            const int i = q / KP, j = q - (q / KP) * KP;  // element (i, j) of A^T = A[j][i]
-            const int64_t t = t_c + s;
-            const int64_t gh = (int64_t)grp * p.HPW + hs;
-            float val;
-            if (t + 1 < p.T && gh < p.heads) {
-                const int64_t b = gh / p.n, h = gh - b * p.n;
-                val = (i < k && j < k) ? ld1(Ag + ((b * p.T + t + 1) * p.n + h) * k * k + j * k + i) : (i == j ? 1.f : 0.f);
-            } else {
-                val = (i == j) ? ((t < p.T && gh < p.heads) ? 0.f : 1.f) : 0.f;
+#pragma unroll
+        for (int u = 0; u < NB; ++u) {
+            if (dst[u] < 0) continue;
+            float w[EPT];
+            PK::unpack(raw[u], w);
+#pragma unroll
+            for (int c = 0; c < EPT; ++c) {
+                const bool diag = EPT == 4 ? i0[u] + c == jr[u] : i0[u] == jr[u];
+                w[c] = in[u] ? w[c] : (diag ? d[u] : 0.f);
+                s_A[dst[u] + c * KP] = w[c];
             }
-            s_A[(s * p.HPW + hs) * AS + q] = val;
         }
-    }
+    };
+    const int e_first = (int)threadIdx.x * EPT;
+    batch(e_first);
+    for (int e0 = e_first + NB * step; e0 < total; e0 += NB * step) batch(e0);
 }
 
 // Reverse time.  Y_t = [M_t | Lam_t] = G_t + A_{t+1}^T Y_{t+1}; a chunk's
@@ -939,7 +1009,7 @@ __global__ __launch_bounds__(512) void affine_bwd_kernel(BwdArgs p) {
         lds_barrier();
         for (int b0 = 0; b0 < lq.n_wait; b0 += p.DB) {
             const int nb = lq.n_wait - b0 < p.DB ? lq.n_wait - b0 : p.DB;
-            stage_payloads(s_part, p.ws, slot, +1, lq, b0, nb, slot_sz);
+            stage_payloads<aff_payload_batch(KP, true)>(s_part, p.ws, slot, +1, lq, b0, nb, slot_sz);
             lds_barrier();
             if (wave == 0) {
                 int q = b0;
