@@ -716,6 +716,18 @@ template <int KP> struct AffRB {
 // lanes over all 32.
 __host__ __device__ constexpr int aff_part_stride(int rbkp) { return rbkp >= 8 ? rbkp + 4 : rbkp; }
 
+// dA_t with vector IO and k a multiple of 4 goes through rows instead: each
+// head's Y_t and X_{t-1} rows in LDS (2 KP rows of the NCP columns), row
+// stride an odd number of float4s so that the KP rows a wave reads at once
+// fall in different banks.
+__host__ __device__ constexpr bool aff_da_rows(int KP, bool VIO) { return VIO && KP % 4 == 0; }
+__host__ __device__ constexpr int aff_row_stride(int NCP) { return (NCP / 4) % 2 == 0 ? NCP + 4 : NCP; }
+// Floats of one wave's dA buffer (HPW heads).
+__host__ __device__ constexpr int aff_da_wave_floats(int KP, int CPL, bool VIO, int HPW, int G, int NCP) {
+    return aff_da_rows(KP, VIO) ? (HPW * 2 * KP * aff_row_stride(NCP) + 3) / 4 * 4
+                                : (HPW * G * aff_part_stride((KP < MISCAN_AFF_RBMAX ? KP : MISCAN_AFF_RBMAX) * KP) + 3) / 4 * 4;
+}
+
 // Source of the lane's columns of one of two (k x k | k x v) tensor pairs at
 // matrix index m: the k x k tensor for Z_M columns, the k x v tensor for Z_L
 // columns.  Lanes of other kinds (and !ok) point at a valid element and are
@@ -902,7 +914,8 @@ __global__ __launch_bounds__(512) void affine_bwd_kernel(BwdArgs p) {
     const int blk = KP * NCP;
     const int bs = pad_bank(blk);
     constexpr int PS = aff_part_stride(RB * KP);      // floats per lane in it
-    const int pw = (HPW * G * PS + 3) / 4 * 4;        // one wave's dA partial-sum buffer
+    const int pw = aff_da_wave_floats(KP, CPL, VIO, HPW, G, NCP);  // one wave's dA buffer
+    const int YS = aff_row_stride(NCP);               // its row stride (row path)
     float *s_A = s_dyn;                                 // [CH][HPW][AS]: A_{t+1}^T
     float *s_X = s_A + (CH * HPW * AS + 3) / 4 * 4;     // [NW][HPW][bs]: wave transforms / suffixes
     float *s_S = s_X + NW * HPW * bs;                   // [HPW][bs]: Y entering the chunk from later
@@ -1038,6 +1051,16 @@ __global__ __launch_bounds__(512) void affine_bwd_kernel(BwdArgs p) {
     get_cols<KP, CPL>(S, s_S + hsc * bs, NCP, c0);
     if (wave + 1 < NW) block_apply<KP, CPL>(S, s_X + ((wave + 1) * HPW + hsc) * bs, NCP, k, c0, is_y);
     float *part = s_part + wave * pw;
+    if constexpr (aff_da_rows(KP, VIO)) {
+        // the last group of four columns reads past 2k + v when it is not a
+        // multiple of 4: those columns are never written, so zero them once
+        // (the buffer held the look-back's stage until the barrier above)
+        if (slot_lane && g == G - 1) {
+            float *hb = part + hsc * 2 * KP * YS;
+            for (int r2 = 0; r2 < 2 * KP; ++r2)
+                for (int c = c0 + CPL; c < NCP; ++c) hb[r2 * YS + c] = 0.f;
+        }
+    }
     // X_{t-1} columns for dA, loaded one step ahead of their use: holding all
     // L steps would cost L * KP * CPL registers and a workgroup per CU, while
     // loading each in the step that uses it exposes the load latency.
@@ -1097,63 +1120,103 @@ __global__ __launch_bounds__(512) void affine_bwd_kernel(BwdArgs p) {
                         if (i < k && cl.kind[cc] == Z_L) st1(static_cast<TS *>(p.dB) + m * k * v + i * v + cl.col[cc], S[i][cc]);
             }
         }
-        // dA_t = Y_t X_{t-1}^T, RB rows a round.  Lanes that hold only P
-        // columns (g < k / CPL) contribute zeros: they store no partial sums
-        // and the readers skip their slots.
-        const int g_first = k / CPL;
+        if constexpr (aff_da_rows(KP, VIO)) {
+            // dA_t = Y_t X_{t-1}^T as dot products over the k + v Y columns:
+            // every lane writes its columns of Y_t and X_{t-1} into the head's
+            // rows (no cross-lane sums), then lanes g < KP^2 / 4 of the head
+            // each form four entries of one row of dA_t.  P columns (c < k)
+            // are written but not read.
+            float *hb = part + hsc * 2 * KP * YS;
+            if (slot_lane) {
 #pragma unroll
-        for (int ib = 0; ib < KP; ib += RB) {
-            if (slot_lane && g >= g_first) {
+                for (int i = 0; i < KP; ++i) stv<CPL, false>(hb + i * YS + c0, S[i]);
 #pragma unroll
-                for (int ii = 0; ii < RB; ++ii) {
-                    float row[KP];
-#pragma unroll
-                    for (int j = 0; j < KP; ++j) row[j] = 0.f;
-#pragma unroll
-                    for (int cc = 0; cc < CPL; ++cc) {
-                        const float y = is_y[cc] ? S[ib + ii][cc] : 0.f;
-#pragma unroll
-                        for (int j = 0; j < KP; ++j) row[j] = fmaf(y, rxr[j][cc], row[j]);
-                    }
-                    stv<KP, false>(part + (hs * G + g) * PS + ii * KP, row);
-                }
+                for (int j = 0; j < KP; ++j) stv<CPL, false>(hb + (KP + j) * YS + c0, rxr[j]);
             }
-            // the wave's own partial sums are in LDS before any lane reads them
+            // the wave's own rows are in LDS before any lane reads them
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
             if (active) {
-                if constexpr (KP % 4 == 0) {
-                    // groups of 4 consecutive entries of a row: vector LDS reads
-                    for (int e = 4 * g; e < RB * KP; e += 4 * G) {
-                        const int ii = e / KP, j0 = e - (e / KP) * KP;
-                        const int i = ib + ii;
-                        float acc[4] = {0.f, 0.f, 0.f, 0.f};
-                        for (int gg = g_first; gg < G; ++gg) {
-                            float q[4];
-                            ldv<4>(q, part + (hs * G + gg) * PS + ii * KP + j0);
+                for (int e = g; e < KP * KP / 4; e += G) {
+                    const int i = e / (KP / 4), j0 = (e - i * (KP / 4)) * 4;
+                    const float *yr = hb + i * YS;
+                    const float *xr = hb + (KP + j0) * YS;
+                    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+                    for (int c = k; c < 2 * k + v; c += 4) {
+                        float y[4];
+                        ldv<4>(y, yr + c);
 #pragma unroll
-                            for (int u = 0; u < 4; ++u) acc[u] += q[u];
-                        }
-                        if constexpr (VIO) {
-                            if (i < k) st_g<TS, 4, true>(static_cast<TS *>(p.dA) + m * k * k + (int64_t)i * k + j0, acc);
-                        } else {
+                        for (int u = 0; u < 4; ++u) {
+                            float x[4];
+                            ldv<4>(x, xr + u * YS + c);
 #pragma unroll
-                            for (int u = 0; u < 4; ++u)
-                                if (i < k && j0 + u < k) st1(static_cast<TS *>(p.dA) + m * k * k + (int64_t)i * k + j0 + u, acc[u]);
+                            for (int w = 0; w < 4; ++w) acc[u] = fmaf(y[w], x[w], acc[u]);
                         }
                     }
-                } else {
-                    for (int e = g; e < RB * KP; e += G) {
-                        const int ii = e / KP, j = e - (e / KP) * KP;
-                        const int i = ib + ii;
-                        float acc = 0.f;
-                        for (int gg = g_first; gg < G; ++gg) acc += part[(hs * G + gg) * PS + ii * KP + j];
-                        if (i < k && j < k) st1(static_cast<TS *>(p.dA) + m * k * k + (int64_t)i * k + j, acc);
-                    }
+                    st_g<TS, 4, true>(static_cast<TS *>(p.dA) + m * k * k + (int64_t)i * k + j0, acc);
                 }
             }
-            // LDS operations of one wave complete in order: the next round's
+            // LDS operations of one wave complete in order: the next step's
             // writes land after these reads; this keeps the compiler's order too.
             asm volatile("" ::: "memory");
+        } else {
+            // dA_t = Y_t X_{t-1}^T, RB rows a round.  Lanes that hold only P
+            // columns (g < k / CPL) contribute zeros: they store no partial sums
+            // and the readers skip their slots.
+            const int g_first = k / CPL;
+#pragma unroll
+            for (int ib = 0; ib < KP; ib += RB) {
+                if (slot_lane && g >= g_first) {
+#pragma unroll
+                    for (int ii = 0; ii < RB; ++ii) {
+                        float row[KP];
+#pragma unroll
+                        for (int j = 0; j < KP; ++j) row[j] = 0.f;
+#pragma unroll
+                        for (int cc = 0; cc < CPL; ++cc) {
+                            const float y = is_y[cc] ? S[ib + ii][cc] : 0.f;
+#pragma unroll
+                            for (int j = 0; j < KP; ++j) row[j] = fmaf(y, rxr[j][cc], row[j]);
+                        }
+                        stv<KP, false>(part + (hs * G + g) * PS + ii * KP, row);
+                    }
+                }
+                // the wave's own partial sums are in LDS before any lane reads them
+                asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+                if (active) {
+                    if constexpr (KP % 4 == 0) {
+                        // groups of 4 consecutive entries of a row: vector LDS reads
+                        for (int e = 4 * g; e < RB * KP; e += 4 * G) {
+                            const int ii = e / KP, j0 = e - (e / KP) * KP;
+                            const int i = ib + ii;
+                            float acc[4] = {0.f, 0.f, 0.f, 0.f};
+                            for (int gg = g_first; gg < G; ++gg) {
+                                float q[4];
+                                ldv<4>(q, part + (hs * G + gg) * PS + ii * KP + j0);
+#pragma unroll
+                                for (int u = 0; u < 4; ++u) acc[u] += q[u];
+                            }
+                            if constexpr (VIO) {
+                                if (i < k) st_g<TS, 4, true>(static_cast<TS *>(p.dA) + m * k * k + (int64_t)i * k + j0, acc);
+                            } else {
+#pragma unroll
+                                for (int u = 0; u < 4; ++u)
+                                    if (i < k && j0 + u < k) st1(static_cast<TS *>(p.dA) + m * k * k + (int64_t)i * k + j0 + u, acc[u]);
+                            }
+                        }
+                    } else {
+                        for (int e = g; e < RB * KP; e += G) {
+                            const int ii = e / KP, j = e - (e / KP) * KP;
+                            const int i = ib + ii;
+                            float acc = 0.f;
+                            for (int gg = g_first; gg < G; ++gg) acc += part[(hs * G + gg) * PS + ii * KP + j];
+                            if (i < k && j < k) st1(static_cast<TS *>(p.dA) + m * k * k + (int64_t)i * k + j, acc);
+                        }
+                    }
+                }
+                // LDS operations of one wave complete in order: the next round's
+                // writes land after these reads; this keeps the compiler's order too.
+                asm volatile("" ::: "memory");
+            }
         }
     }
 }
@@ -1243,8 +1306,7 @@ inline AffPlan make_plan(int64_t B, int64_t T, int64_t n, int k, int v, bool bwd
     const int L = aff_L(pl.KP, CPL, bwd);
     const size_t a_ld = (size_t)pad_bank(pl.KP * pl.KP);  // LDS strides (see pad_bank)
     const size_t x_ld = (size_t)pad_bank(pl.KP * pl.NCP);
-    const int rb = pl.KP < MISCAN_AFF_RBMAX ? pl.KP : MISCAN_AFF_RBMAX;  // AffRB
-    const size_t part = round_up((size_t)pl.HPW * pl.G * aff_part_stride(rb * pl.KP), 4);
+    const size_t part = (size_t)aff_da_wave_floats(pl.KP, CPL, VIO, pl.HPW, pl.G, pl.NCP);
     const size_t limit = bwd ? BWD_LDS_MAX : FWD_LDS_MAX;
     const size_t payload = (size_t)pl.HH * pl.KP * pl.NCP;  // floats of one look-back slot
     // Look-back window (payloads a chunk folds) and staged payloads per round
