@@ -155,6 +155,26 @@ struct BwdArgs {
     WsPtrs ws;
 };
 
+// Wave 0's look-back (publish, wait, fold, publish) is a link of the chain
+// of inclusive states that later chunks wait on.  In the backward (three
+// workgroups a CU, a window of two, the chain sets the pace) the wave issues
+// ahead of the other waves on its SIMD while it runs: measured 664 -> 650 us
+// (fp32) and 549 -> 535 us (bf16) on B=4, T=4096, n=32, k=8, v=32.  The
+// forward gains nothing from it (bf16 runs 3% slower).
+#ifndef MISCAN_AFF_LB_PRIO
+#define MISCAN_AFF_LB_PRIO 0
+#endif
+#ifndef MISCAN_AFF_BWD_LB_PRIO
+#define MISCAN_AFF_BWD_LB_PRIO 3
+#endif
+template <int PRIO>
+__device__ __forceinline__ void lb_prio(bool on) {
+    if constexpr (PRIO > 0) {
+        if (on) __builtin_amdgcn_s_setprio(PRIO);
+        else __builtin_amdgcn_s_setprio(0);
+    }
+}
+
 // Column kinds of a lane.  With VIO all CPL columns share one kind (k and v
 // are multiples of CPL).
 template <int CPL>
@@ -654,6 +674,7 @@ __global__ __launch_bounds__(512) void affine_fwd_kernel(FwdArgs p) {
     }
     // Every segment's lanes of a head hold the same look-back values (same
     // loads, same operations) and store them to the same addresses.
+    if (wave == 0) lb_prio<MISCAN_AFF_LB_PRIO>(true);
     if (wave == 0) {
         if (slot_lane) {
             float C[KP][CPL];
@@ -684,6 +705,7 @@ __global__ __launch_bounds__(512) void affine_fwd_kernel(FwdArgs p) {
         block_apply<KP, CPL>(S, s_C, NCP, k, c0, is_h);  // S becomes the inclusive state
         if (slot_lane) payload_store<KP, CPL>(p.ws.inc + slot * slot_sz + hoff, NCP, c0, S);
         publish_flag(p.ws.flags + slot, FLAG_INC);
+        lb_prio<MISCAN_AFF_LB_PRIO>(false);
     }
     lds_barrier();
 
@@ -815,6 +837,48 @@ __device__ __forceinline__ void load_xprev(float (&x)[KP][CPL], const BwdArgs &p
                 for (int cc = 0; cc < CPL; ++cc)
                     if (i < k && cl.kind[cc] == Z_L)
                         x[i][cc] = ld1(static_cast<const TS *>(p.H0) + gh * k * v + i * v + cl.col[cc]);
+        }
+    }
+}
+
+// load_xprev in two parts for vector IO: xprev_issue only loads (raw, from a
+// valid element in every lane) and xprev_finish widens and selects what the
+// loads cannot give, when the step uses the columns.  A select right after
+// the loads would wait for them, so a load issued a step ahead would not stay
+// in flight.
+template <typename TS, int KP, int CPL>
+struct XRaw {
+    typename Pack<TS, CPL>::raw_t r[KP];
+};
+template <typename TS, int KP, int CPL>
+__device__ __forceinline__ void xprev_issue(XRaw<TS, KP, CPL> &xr, const BwdArgs &p, const Cols<CPL> &cl,
+                                            int64_t m, int64_t t, bool ok) {
+    int ld;
+    const TS *src = y_src<TS, CPL>(p.Abar, p.Bbar, cl, m - p.n, KP, p.v, ok && t > 0, ld);
+#pragma unroll
+    for (int i = 0; i < KP; ++i) xr.r[i] = load_vec<TS, CPL>(src + i * ld);
+}
+template <typename TS, int KP, int CPL, bool H0>
+__device__ __forceinline__ void xprev_finish(float (&x)[KP][CPL], const XRaw<TS, KP, CPL> &xr, const BwdArgs &p,
+                                             const Cols<CPL> &cl, int64_t t, bool ok, int64_t gh) {
+    const bool use = ok && t > 0 && (cl.kind[0] == Z_M || cl.kind[0] == Z_L);
+#pragma unroll
+    for (int i = 0; i < KP; ++i) {
+        float f[CPL];
+        Pack<TS, CPL>::unpack(xr.r[i], f);
+#pragma unroll
+        for (int cc = 0; cc < CPL; ++cc) {
+            const float id = (ok && t == 0 && cl.kind[cc] == Z_M && i == cl.col[cc]) ? 1.f : 0.f;
+            x[i][cc] = use ? f[cc] : id;
+        }
+    }
+    if constexpr (H0) {  // X_{-1} = [I | H0]: its H columns at t = 0
+        if (ok && t == 0 && p.H0 != nullptr) {
+#pragma unroll
+            for (int i = 0; i < KP; ++i)
+#pragma unroll
+                for (int cc = 0; cc < CPL; ++cc)
+                    if (cl.kind[cc] == Z_L) x[i][cc] = ld1(static_cast<const TS *>(p.H0) + gh * KP * p.v + i * p.v + cl.col[cc]);
         }
     }
 }
@@ -1010,6 +1074,7 @@ __global__ __launch_bounds__(512) void affine_bwd_kernel(BwdArgs p) {
     for (int i = 0; i < KP; ++i)
 #pragma unroll
         for (int cc = 0; cc < CPL; ++cc) S[i][cc] = 0.f;
+    if (wave == 0) lb_prio<MISCAN_AFF_BWD_LB_PRIO>(true);
     if (wave == 0) {
         if (slot_lane) {
             float Z[KP][CPL];
@@ -1044,6 +1109,7 @@ __global__ __launch_bounds__(512) void affine_bwd_kernel(BwdArgs p) {
         block_apply<KP, CPL>(S, s_X + hsc * bs, NCP, k, c0, is_y);  // through the whole chunk
         if (slot_lane) payload_store<KP, CPL>(p.ws.inc + slot * slot_sz + hoff, NCP, c0, S);
         publish_flag(p.ws.flags + slot, FLAG_INC);
+        lb_prio<MISCAN_AFF_BWD_LB_PRIO>(false);
     }
     lds_barrier();
 
@@ -1064,19 +1130,30 @@ __global__ __launch_bounds__(512) void affine_bwd_kernel(BwdArgs p) {
     // X_{t-1} columns for dA, loaded one step ahead of their use: holding all
     // L steps would cost L * KP * CPL registers and a workgroup per CU, while
     // loading each in the step that uses it exposes the load latency.
-    float rxn[KP][CPL];
-    load_xprev<TS, KP, CPL, VIO, H0>(rxn, p, cl, m0 + (t_w + L - 1) * p.n, t_w + L - 1, active && t_w + L - 1 < p.T, gh);
+    float rxn[KP][CPL];   // element-wise IO: the next step's columns
+    XRaw<TS, KP, CPL> xn;  // vector IO: the next step's loads, still in flight
+    if constexpr (VIO)
+        xprev_issue<TS, KP, CPL>(xn, p, cl, m0 + (t_w + L - 1) * p.n, t_w + L - 1, active && t_w + L - 1 < p.T);
+    else
+        load_xprev<TS, KP, CPL, VIO, H0>(rxn, p, cl, m0 + (t_w + L - 1) * p.n, t_w + L - 1,
+                                         active && t_w + L - 1 < p.T, gh);
 #pragma unroll
     for (int r = L - 1; r >= 0; --r) {
         const int64_t t = t_w + r;
         float rxr[KP][CPL];
+        if constexpr (VIO) {
+            xprev_finish<TS, KP, CPL, H0>(rxr, xn, p, cl, t, active && t < p.T, gh);
+            if (r > 0)
+                xprev_issue<TS, KP, CPL>(xn, p, cl, m0 + (t_w + r - 1) * p.n, t_w + r - 1, active && t_w + r - 1 < p.T);
+        } else {
 #pragma unroll
-        for (int i = 0; i < KP; ++i)
+            for (int i = 0; i < KP; ++i)
 #pragma unroll
-            for (int cc = 0; cc < CPL; ++cc) rxr[i][cc] = rxn[i][cc];
-        if (r > 0)
-            load_xprev<TS, KP, CPL, VIO, H0>(rxn, p, cl, m0 + (t_w + r - 1) * p.n, t_w + r - 1,
-                                             active && t_w + r - 1 < p.T, gh);
+                for (int cc = 0; cc < CPL; ++cc) rxr[i][cc] = rxn[i][cc];
+            if (r > 0)
+                load_xprev<TS, KP, CPL, VIO, H0>(rxn, p, cl, m0 + (t_w + r - 1) * p.n, t_w + r - 1,
+                                                 active && t_w + r - 1 < p.T, gh);
+        }
         step_lds<KP, CPL>(S, s_A + ((wave * L + r) * HPW + hsc) * AS, rg[r]);  // S = Y_t
         if (t >= p.T) continue;  // wave-uniform
         const int64_t m = m0 + t * p.n;
@@ -1135,8 +1212,17 @@ __global__ __launch_bounds__(512) void affine_bwd_kernel(BwdArgs p) {
             }
             // the wave's own rows are in LDS before any lane reads them
             asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-            if (active) {
-                for (int e = g; e < KP * KP / 4; e += G) {
+            // groups e = g, g + G, ...: at most MAXIT a lane (a head has at
+            // least GMIN lanes, v >= CPL).  The loop over groups is unrolled:
+            // with a global store in a loop of run-time length the compiler
+            // waits for every load in flight, the next step's X_{t-1} too.
+            constexpr int NG = KP * KP / 4;
+            constexpr int GMIN = (2 * KP + CPL) / CPL;
+            constexpr int MAXIT = (NG + GMIN - 1) / GMIN;
+#pragma unroll
+            for (int it = 0; it < MAXIT; ++it) {
+                const int e = g + it * G;
+                if (active && e < NG) {
                     const int i = e / (KP / 4), j0 = (e - i * (KP / 4)) * 4;
                     const float *yr = hb + i * YS;
                     const float *xr = hb + (KP + j0) * YS;
@@ -1267,6 +1353,9 @@ constexpr size_t LDS_DEVICE_MAX = 163840;
 #ifndef MISCAN_AFF_RESIDENT
 #define MISCAN_AFF_RESIDENT 128
 #endif
+#ifndef MISCAN_AFF_BWD_RESIDENT
+#define MISCAN_AFF_BWD_RESIDENT MISCAN_AFF_RESIDENT
+#endif
 
 // Time segments per forward chunk: the largest divisor of HPW up to this
 // bound.  Segments shorten the look-back chain but add prefix rounds; with
@@ -1313,7 +1402,7 @@ inline AffPlan make_plan(int64_t B, int64_t T, int64_t n, int k, int v, bool bwd
     // trip: no more than the window, so the forward's stage takes no more LDS
     // than one round needs.
     const int64_t heads = B * n;
-    pl.W = lb_window((heads + pl.HH - 1) / pl.HH, MISCAN_AFF_RESIDENT);
+    pl.W = lb_window((heads + pl.HH - 1) / pl.HH, bwd ? MISCAN_AFF_BWD_RESIDENT : MISCAN_AFF_RESIDENT);
     const size_t fwd_db = MISCAN_AFF_STAGE_FLOATS / payload;
     const int fdb_cap = pl.W < MISCAN_AFF_DBMAX ? pl.W : MISCAN_AFF_DBMAX;
     const int fdb = fwd_db < 1 ? 1 : fwd_db > (size_t)fdb_cap ? fdb_cap : (int)fwd_db;
