@@ -447,6 +447,13 @@ def run_affine(x, with_bwd, metric, dtype=torch.float32):
     Abar_r, Bbar_r = oracle.affine_scan_fwd(A, Bm)
     if metric == "block":
         errs = {"Abar": block_err(to_np(Abar_d), Abar_r), "Bbar": block_err(to_np(Bbar_d), Bbar_r)}
+        # reported, not asserted: element-wise relative error over entries at least a
+        # tenth of their block's largest (the tolerance is read per block)
+        for name, G, R in (("Abar", to_np(Abar_d), Abar_r), ("Bbar", to_np(Bbar_d), Bbar_r)):
+            big = np.abs(R) >= 0.1 * np.max(np.abs(R), axis=(-2, -1), keepdims=True)
+            rel = np.abs(G - R)[big] / np.abs(R)[big]
+            print("element-wise relative error of %s over entries >= 0.1 x block max: %.3g"
+                  % (name, float(rel.max()) if rel.size else 0.0), flush=True)
     else:
         Abar_s, Bbar_s = oracle.affine_scan_fwd(np.abs(A), np.abs(Bm))
         assert np.all(np.isfinite(Abar_s)) and np.all(np.isfinite(Bbar_s))
