@@ -493,8 +493,10 @@ def test_affine_workload5_full(seed):
     assert max(errs.values()) <= TOL[torch.float32], errs
 
 
+# (4, 6), (8, 6) and (16, 6) leave 2k + v = 2 (mod 4): the backward's dA rows
+# then read two zeroed pad columns; at k = 16 a lane forms up to four groups.
 @pytest.mark.parametrize("kv", [(1, 1), (2, 2), (3, 5), (4, 16), (8, 32), (16, 1), (2, 128),
-                                (16, 128), (5, 3), (4, 6)])
+                                (16, 128), (5, 3), (4, 6), (8, 6), (16, 6)])
 def test_affine_edge_shapes(kv):
     k, v = kv
     for (Bn, T, n) in ((1, 1, 1), (2, 33, 3), (1, 130, 5)):
