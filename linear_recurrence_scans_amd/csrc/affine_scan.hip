@@ -127,6 +127,15 @@ __device__ __forceinline__ void st1(TS *dst, float v) {
     st_g<TS, 1, false>(dst, f);
 }
 
+// Sixteen zero bytes in device memory, never written: lanes with nothing to
+// load (padding and P columns, steps past T) read their CPL values here with a
+// row stride of 0, so the loads need no select afterwards.
+__device__ __align__(16) uint32_t g_aff_zeros[4];
+template <typename TS>
+__device__ __forceinline__ const TS *aff_zeros() {
+    return reinterpret_cast<const TS *>(g_aff_zeros);
+}
+
 // Tensor pointers are untyped here; the kernels read them as TS.
 struct FwdArgs {
     const void *A, *Bm;
@@ -236,17 +245,13 @@ __device__ __forceinline__ void load_b(float (&b)[KP][CPL], const FwdArgs &p, co
     const int k = VIO ? KP : p.k, v = p.v;
     const TS *Bm = static_cast<const TS *>(p.Bm);
     if constexpr (VIO) {
-        // every lane loads (other kinds from a valid element) and selects: no
-        // branch around the loads
+        // every lane loads, other kinds (and steps past T) zeros: no branch
+        // around the loads and no select after them
         const bool use = ok && cl.kind[0] == C_H;
-        const TS *src = use ? Bm + m * k * v + cl.col[0] : Bm;
+        const TS *src = use ? Bm + m * k * v + cl.col[0] : aff_zeros<TS>();
         const int ld = use ? v : 0;
 #pragma unroll
-        for (int i = 0; i < KP; ++i) {
-            ld_g<TS, CPL>(b[i], src + i * ld);
-#pragma unroll
-            for (int cc = 0; cc < CPL; ++cc) b[i][cc] = use ? b[i][cc] : 0.f;
-        }
+        for (int i = 0; i < KP; ++i) ld_g<TS, CPL>(b[i], src + i * ld);
     } else {
 #pragma unroll
         for (int i = 0; i < KP; ++i)
@@ -752,15 +757,15 @@ __host__ __device__ constexpr int aff_da_wave_floats(int KP, int CPL, bool VIO, 
 
 // Source of the lane's columns of one of two (k x k | k x v) tensor pairs at
 // matrix index m: the k x k tensor for Z_M columns, the k x v tensor for Z_L
-// columns.  Lanes of other kinds (and !ok) point at a valid element and are
-// zeroed by the caller: every lane loads, so no branch sits around the loads.
+// columns.  Lanes of other kinds (and !ok) read zeros (row stride 0): every
+// lane loads, so no branch sits around the loads and no select follows them.
 template <typename TS, int CPL>
 __device__ __forceinline__ const TS *y_src(const void *kk_, const void *kv_, const Cols<CPL> &cl, int64_t m,
                                            int k, int v, bool ok, int &ld) {
     const TS *kk = static_cast<const TS *>(kk_), *kv = static_cast<const TS *>(kv_);
     const bool is_m = ok && cl.kind[0] == Z_M, is_l = ok && cl.kind[0] == Z_L;
-    ld = is_l ? v : k;
-    return is_m ? kk + m * k * k + cl.col[0] : is_l ? kv + m * k * v + cl.col[0] : kk;
+    ld = is_l ? v : is_m ? k : 0;
+    return is_m ? kk + m * k * k + cl.col[0] : is_l ? kv + m * k * v + cl.col[0] : aff_zeros<TS>();
 }
 
 // The lane's columns of G_t = [gAbar_t | gBbar_t] (zero for P and padding
@@ -772,13 +777,8 @@ __device__ __forceinline__ void load_g(float (&g)[KP][CPL], const BwdArgs &p, co
     if constexpr (VIO) {
         int ld;
         const TS *src = y_src<TS, CPL>(p.gAbar, p.gBbar, cl, m, k, v, ok, ld);
-        const bool use = ok && (cl.kind[0] == Z_M || cl.kind[0] == Z_L);
 #pragma unroll
-        for (int i = 0; i < KP; ++i) {
-            ld_g<TS, CPL>(g[i], src + i * ld);
-#pragma unroll
-            for (int cc = 0; cc < CPL; ++cc) g[i][cc] = use ? g[i][cc] : 0.f;
-        }
+        for (int i = 0; i < KP; ++i) ld_g<TS, CPL>(g[i], src + i * ld);
     } else {
 #pragma unroll
         for (int i = 0; i < KP; ++i)
@@ -795,40 +795,26 @@ __device__ __forceinline__ void load_g(float (&g)[KP][CPL], const BwdArgs &p, co
 }
 
 // The lane's columns of X_{t-1} = [Abar_{t-1} | Bbar_{t-1}] matching its Y
-// columns ([I | 0] at t = 0; zero when !ok).
-template <typename TS, int KP, int CPL, bool VIO, bool H0 = false>
+// columns ([I | 0] at t = 0; zero when !ok), element-wise IO (vector IO uses
+// xprev_issue / xprev_finish below).
+template <typename TS, int KP, int CPL, bool H0 = false>
 __device__ __forceinline__ void load_xprev(float (&x)[KP][CPL], const BwdArgs &p, const Cols<CPL> &cl, int64_t m,
                                            int64_t t, bool ok, int64_t gh = 0) {
-    const int k = VIO ? KP : p.k, v = p.v;
-    if constexpr (VIO) {
-        int ld;
-        const TS *src = y_src<TS, CPL>(p.Abar, p.Bbar, cl, m - p.n, k, v, ok && t > 0, ld);
-        const bool use = ok && t > 0 && (cl.kind[0] == Z_M || cl.kind[0] == Z_L);
+    const int k = p.k, v = p.v;
 #pragma unroll
-        for (int i = 0; i < KP; ++i) {
-            ld_g<TS, CPL>(x[i], src + i * ld);
+    for (int i = 0; i < KP; ++i)
 #pragma unroll
-            for (int cc = 0; cc < CPL; ++cc) {
-                const float id = (ok && t == 0 && cl.kind[cc] == Z_M && i == cl.col[cc]) ? 1.f : 0.f;
-                x[i][cc] = use ? x[i][cc] : id;
+        for (int cc = 0; cc < CPL; ++cc) {
+            float xv = 0.f;
+            if (ok && i < k) {
+                if (cl.kind[cc] == Z_M)
+                    xv = (t > 0) ? ld1(static_cast<const TS *>(p.Abar) + (m - p.n) * k * k + i * k + cl.col[cc])
+                                 : (i == cl.col[cc] ? 1.f : 0.f);
+                else if (cl.kind[cc] == Z_L && t > 0)
+                    xv = ld1(static_cast<const TS *>(p.Bbar) + (m - p.n) * k * v + i * v + cl.col[cc]);
             }
+            x[i][cc] = xv;
         }
-    } else {
-#pragma unroll
-        for (int i = 0; i < KP; ++i)
-#pragma unroll
-            for (int cc = 0; cc < CPL; ++cc) {
-                float xv = 0.f;
-                if (ok && i < k) {
-                    if (cl.kind[cc] == Z_M)
-                        xv = (t > 0) ? ld1(static_cast<const TS *>(p.Abar) + (m - p.n) * k * k + i * k + cl.col[cc])
-                                     : (i == cl.col[cc] ? 1.f : 0.f);
-                    else if (cl.kind[cc] == Z_L && t > 0)
-                        xv = ld1(static_cast<const TS *>(p.Bbar) + (m - p.n) * k * v + i * v + cl.col[cc]);
-                }
-                x[i][cc] = xv;
-            }
-    }
     if constexpr (H0) {  // X_{-1} = [I | H0]: its H columns at t = 0
         if (ok && t == 0 && p.H0 != nullptr) {
 #pragma unroll
@@ -841,11 +827,11 @@ __device__ __forceinline__ void load_xprev(float (&x)[KP][CPL], const BwdArgs &p
     }
 }
 
-// load_xprev in two parts for vector IO: xprev_issue only loads (raw, from a
-// valid element in every lane) and xprev_finish widens and selects what the
-// loads cannot give, when the step uses the columns.  A select right after
-// the loads would wait for them, so a load issued a step ahead would not stay
-// in flight.
+// load_xprev in two parts for vector IO: xprev_issue only loads (raw; lanes
+// without X columns, and t = 0, read zeros) and xprev_finish widens, when the
+// step uses the columns, and sets the identity at t = 0.  Work on the loaded
+// values right after the loads would wait for them, so a load issued a step
+// ahead would not stay in flight.
 template <typename TS, int KP, int CPL>
 struct XRaw {
     typename Pack<TS, CPL>::raw_t r[KP];
@@ -861,16 +847,14 @@ __device__ __forceinline__ void xprev_issue(XRaw<TS, KP, CPL> &xr, const BwdArgs
 template <typename TS, int KP, int CPL, bool H0>
 __device__ __forceinline__ void xprev_finish(float (&x)[KP][CPL], const XRaw<TS, KP, CPL> &xr, const BwdArgs &p,
                                              const Cols<CPL> &cl, int64_t t, bool ok, int64_t gh) {
-    const bool use = ok && t > 0 && (cl.kind[0] == Z_M || cl.kind[0] == Z_L);
 #pragma unroll
-    for (int i = 0; i < KP; ++i) {
-        float f[CPL];
-        Pack<TS, CPL>::unpack(xr.r[i], f);
+    for (int i = 0; i < KP; ++i) Pack<TS, CPL>::unpack(xr.r[i], x[i]);
+    if (t == 0) {  // wave-uniform: X_0 = [I | 0] on the lane's M columns (zeros were loaded)
 #pragma unroll
-        for (int cc = 0; cc < CPL; ++cc) {
-            const float id = (ok && t == 0 && cl.kind[cc] == Z_M && i == cl.col[cc]) ? 1.f : 0.f;
-            x[i][cc] = use ? f[cc] : id;
-        }
+        for (int i = 0; i < KP; ++i)
+#pragma unroll
+            for (int cc = 0; cc < CPL; ++cc)
+                x[i][cc] = (ok && cl.kind[cc] == Z_M && i == cl.col[cc]) ? 1.f : 0.f;
     }
     if constexpr (H0) {  // X_{-1} = [I | H0]: its H columns at t = 0
         if (ok && t == 0 && p.H0 != nullptr) {
@@ -1135,7 +1119,7 @@ __global__ __launch_bounds__(512) void affine_bwd_kernel(BwdArgs p) {
     if constexpr (VIO)
         xprev_issue<TS, KP, CPL>(xn, p, cl, m0 + (t_w + L - 1) * p.n, t_w + L - 1, active && t_w + L - 1 < p.T);
     else
-        load_xprev<TS, KP, CPL, VIO, H0>(rxn, p, cl, m0 + (t_w + L - 1) * p.n, t_w + L - 1,
+        load_xprev<TS, KP, CPL, H0>(rxn, p, cl, m0 + (t_w + L - 1) * p.n, t_w + L - 1,
                                          active && t_w + L - 1 < p.T, gh);
 #pragma unroll
     for (int r = L - 1; r >= 0; --r) {
@@ -1151,7 +1135,7 @@ __global__ __launch_bounds__(512) void affine_bwd_kernel(BwdArgs p) {
 #pragma unroll
                 for (int cc = 0; cc < CPL; ++cc) rxr[i][cc] = rxn[i][cc];
             if (r > 0)
-                load_xprev<TS, KP, CPL, VIO, H0>(rxn, p, cl, m0 + (t_w + r - 1) * p.n, t_w + r - 1,
+                load_xprev<TS, KP, CPL, H0>(rxn, p, cl, m0 + (t_w + r - 1) * p.n, t_w + r - 1,
                                                  active && t_w + r - 1 < p.T, gh);
         }
         step_lds<KP, CPL>(S, s_A + ((wave * L + r) * HPW + hsc) * AS, rg[r]);  // S = Y_t
