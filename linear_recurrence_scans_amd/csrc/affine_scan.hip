@@ -293,6 +293,15 @@ __host__ __device__ constexpr int pad_bank(int f) { return f < 4 ? f : f + ((4 -
 // Slot s of a wave holds head s % HH of the workgroup's group and segment
 // s / HH of its chunk; row q (0 <= q < CHW = NW * L) of a segment is time step
 // t_c + (s / HH) * CHW + q.
+// Batch index and head of a global head index (b * n + h).  The plan admits
+// fewer than 2^31 heads, so the division runs in 32 bits: a 64-bit division
+// is a long instruction sequence, and the A staging divides once per element.
+__device__ __forceinline__ void split_head(int64_t gh, int n, int64_t &b, int64_t &h) {
+    const uint32_t g32 = (uint32_t)gh, q = g32 / (uint32_t)n;
+    b = (int64_t)q;
+    h = (int64_t)(g32 - q * (uint32_t)n);
+}
+
 struct SlotMap {
     int HH, CHW;
     __device__ __forceinline__ int64_t t(int64_t t_c, int s, int q) const { return t_c + (int64_t)(s / HH) * CHW + q; }
@@ -358,7 +367,8 @@ __device__ __forceinline__ void stage_a(float *s_A, const FwdArgs &p, const Slot
             const int64_t gh = sm.head(grp, hs);
             const int i = o / KP, j = o - (o / KP) * KP;
             in[u] = valid && t < p.T && gh < p.heads && (EPT == 4 || (i < k && j < k));
-            const int64_t b = in[u] ? gh / p.n : 0, h = in[u] ? gh - b * p.n : 0;
+            int64_t b, h;
+            split_head(in[u] ? gh : 0, p.n, b, h);
             const TS *src = Ag;
             if (in[u]) src = EPT == 4 ? Ag + ((b * p.T + t) * p.n + h) * KK + o
                                       : Ag + ((b * p.T + t) * p.n + h) * k * k + i * k + j;
@@ -586,8 +596,8 @@ __global__ __launch_bounds__(512) void affine_fwd_kernel(FwdArgs p) {
     const int hh = hsc - sg * HH;     // and head within the group
     const int64_t gh = sm.head(grp, hsc);
     const bool active = slot_lane && gh < p.heads;
-    const int64_t bidx = active ? gh / p.n : 0;
-    const int64_t hn = active ? gh % p.n : 0;
+    int64_t bidx, hn;
+    split_head(active ? gh : 0, p.n, bidx, hn);
     // With vector IO k equals KP: a compile-time k removes every bounds test
     // (and the branches around the loads) from the block products.
     const int k = VIO ? KP : p.k;
@@ -907,7 +917,8 @@ __device__ __forceinline__ void stage_at(float *s_A, const BwdArgs &p, int grp, 
             // diagonal where nothing loads: 0 at a head's last step (A_{T+1} = 0),
             // 1 elsewhere (steps past T, heads past the last, padding of k)
             d[u] = (gh < p.heads && t == p.T - 1) ? 0.f : 1.f;
-            const int64_t b = in[u] ? gh / p.n : 0, h = in[u] ? gh - b * p.n : 0;
+            int64_t b, h;
+            split_head(in[u] ? gh : 0, p.n, b, h);
             const TS *src = Ag;
             if (in[u]) src = EPT == 4 ? Ag + ((b * p.T + t + 1) * p.n + h) * KK + q
                                       : Ag + ((b * p.T + t + 1) * p.n + h) * k * k + jr[u] * k + i0[u];
@@ -984,8 +995,8 @@ __global__ __launch_bounds__(512) void affine_bwd_kernel(BwdArgs p) {
     const int hsc = slot_lane ? hs : 0;
     const int64_t gh = (int64_t)grp * HPW + hs;
     const bool active = slot_lane && gh < p.heads;
-    const int64_t bidx = active ? gh / p.n : 0;
-    const int64_t hh = active ? gh % p.n : 0;
+    int64_t bidx, hh;
+    split_head(active ? gh : 0, p.n, bidx, hh);
     const int k = VIO ? KP : p.k;
     const int v = p.v;
     const int c0 = g * CPL;
@@ -1404,7 +1415,7 @@ inline AffPlan make_plan(int64_t B, int64_t T, int64_t n, int k, int v, bool bwd
     pl.lds_bytes = lds_floats(pl.NW) * sizeof(float);
     const int64_t ng = (heads + pl.HH - 1) / pl.HH;
     const int64_t nc = (T + pl.LC - 1) / pl.LC;
-    pl.ok = ng <= INT32_MAX && nc <= INT32_MAX && ng * nc <= (int64_t)INT32_MAX &&
+    pl.ok = ng <= INT32_MAX && nc <= INT32_MAX && ng * nc <= (int64_t)INT32_MAX && heads <= INT32_MAX &&
             pl.lds_bytes <= LDS_DEVICE_MAX;
     pl.n_groups = (int)ng;
     pl.n_chunks = (int)nc;

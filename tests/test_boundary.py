@@ -200,6 +200,15 @@ def test_affine_envelope():
     assert call(1, 1) == MI_ERR_WORKSPACE
     assert L.mi_affine_scan_workspace(1, 4, 2, 17, 4, F32) == 0
     assert L.mi_affine_scan_bwd(A, Ab, Bb, Bm, Bm, ws, ws, 1, 4, 2, 4, 4, F32, P, 1 << 40, None) == MI_ERR_INVALID_ARG
+    # head indices (B * n) run in 32 bits in the kernels: 2^31 heads or more are
+    # refused by the plan, before anything is launched
+    # (tensors of 128 GiB: fake pointers 1 TiB apart)
+    G = [P + i * (1 << 40) for i in range(8)]
+    wsz = L.mi_affine_scan_workspace(1 << 16, 1, 1 << 15, 4, 4, F32)
+    assert L.mi_affine_scan_fwd(G[0], G[1], G[2], G[3], 1 << 16, 1, 1 << 15, 4, 4, F32, G[7], wsz,
+                                None) == MI_ERR_UNSUPPORTED
+    assert L.mi_affine_scan_bwd(G[0], G[2], G[3], G[4], G[5], G[1], G[6], 1 << 16, 1, 1 << 15, 4, 4, F32, G[7],
+                                wsz, None) == MI_ERR_UNSUPPORTED
 
 
 def test_workspace_sizes_cover_every_shape():
