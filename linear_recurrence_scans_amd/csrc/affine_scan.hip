@@ -625,9 +625,38 @@ __global__ __launch_bounds__(512) void affine_fwd_kernel(FwdArgs p) {
 #pragma unroll
         for (int cc = 0; cc < CPL; ++cc) x[i][cc] = (cl.kind[cc] == C_ABAR && i == cl.col[cc]) ? 1.f : 0.f;
     // 1. B of the wave's steps (registers) and the A_t blocks (LDS).
+    //    With vector IO a lane's B columns and X_t destination are a base at
+    //    the wave's first step plus one stride a step (n matrices): a step
+    //    costs a 64-bit add, not a recomputed matrix index.
     float rb[L][KP][CPL];
+    const TS *bsrc = nullptr;
+    TS *xdst = nullptr;
+    int64_t bstep = 0, xstep = 0;
+    int xld = 0;
+    if constexpr (VIO) {
+        const int64_t mw = m0 + t_w * p.n;  // matrix index at the wave's first step
+        const bool bh = active && cl.kind[0] == C_H;
+        bsrc = bh ? static_cast<const TS *>(p.Bm) + mw * k * p.v + cl.col[0] : aff_zeros<TS>();
+        bstep = bh ? p.n * (int64_t)k * p.v : 0;
+        const bool xa = cl.kind[0] == C_ABAR;
+        xdst = xa ? static_cast<TS *>(p.Abar) + mw * k * k + cl.col[0] : static_cast<TS *>(p.Bbar) + mw * k * p.v + cl.col[0];
+        xstep = p.n * (int64_t)k * (xa ? k : p.v);
+        xld = xa ? k : p.v;
+        const int bld = bh ? p.v : 0;
+        const TS *src = bsrc;
 #pragma unroll
-    for (int r = 0; r < L; ++r) load_b<TS, KP, CPL, VIO>(rb[r], p, cl, m0 + (t_w + r) * p.n, active && t_w + r < p.T);
+        for (int r = 0; r < L; ++r) {
+            const TS *sr = (t_w + r < p.T) ? src : aff_zeros<TS>();
+            const int ldr = (t_w + r < p.T) ? bld : 0;
+#pragma unroll
+            for (int i = 0; i < KP; ++i) ld_g<TS, CPL>(rb[r][i], sr + i * ldr);
+            src += bstep;
+        }
+    } else {
+#pragma unroll
+        for (int r = 0; r < L; ++r)
+            load_b<TS, KP, CPL, VIO>(rb[r], p, cl, m0 + (t_w + r) * p.n, active && t_w + r < p.T);
+    }
     stage_a<TS, KP, VIO>(s_A, p, sm, grp, t_c);
     lds_barrier();
 
@@ -728,10 +757,19 @@ __global__ __launch_bounds__(512) void affine_fwd_kernel(FwdArgs p) {
     //    before it), rescan, store.
     get_cols<KP, CPL>(S, s_S + hh * bs, NCP, c0);
     if (e > 0) block_apply<KP, CPL>(S, piece(e - 1), NCP, k, c0, is_h);
+    const bool xst = active && cl.kind[0] != C_PAD;  // vector IO: the lane stores
 #pragma unroll
     for (int r = 0; r < L; ++r) {
         step_lds<KP, CPL>(S, s_A + ((wave * L + r) * HPW + hsc) * AS, rb[r]);
-        if (active && t_w + r < p.T) store_x<TS, KP, CPL, VIO>(p, cl, m0 + (t_w + r) * p.n, S);
+        if constexpr (VIO) {
+            if (xst && t_w + r < p.T) {
+#pragma unroll
+                for (int i = 0; i < KP; ++i) st_g<TS, CPL, true>(xdst + i * xld, S[i]);
+            }
+            xdst += xstep;
+        } else {
+            if (active && t_w + r < p.T) store_x<TS, KP, CPL, VIO>(p, cl, m0 + (t_w + r) * p.n, S);
+        }
     }
 }
 
