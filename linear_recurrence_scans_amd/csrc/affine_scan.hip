@@ -885,10 +885,7 @@ struct XRaw {
     typename Pack<TS, CPL>::raw_t r[KP];
 };
 template <typename TS, int KP, int CPL>
-__device__ __forceinline__ void xprev_issue(XRaw<TS, KP, CPL> &xr, const BwdArgs &p, const Cols<CPL> &cl,
-                                            int64_t m, int64_t t, bool ok) {
-    int ld;
-    const TS *src = y_src<TS, CPL>(p.Abar, p.Bbar, cl, m - p.n, KP, p.v, ok && t > 0, ld);
+__device__ __forceinline__ void xprev_issue(XRaw<TS, KP, CPL> &xr, const TS *src, int ld) {
 #pragma unroll
     for (int i = 0; i < KP; ++i) xr.r[i] = load_vec<TS, CPL>(src + i * ld);
 }
@@ -1057,9 +1054,29 @@ __global__ __launch_bounds__(512) void affine_bwd_kernel(BwdArgs p) {
     const int64_t m0 = bidx * p.T * p.n + hh;
 
     // 1. G columns (registers), A_{t+1}^T (LDS).
+    //    With vector IO a lane's G and X_{t-1} sources and dB, dA destinations
+    //    are a base at the wave's first step plus one stride a step.
     float rg[L][KP][CPL];
+    const int64_t mw = m0 + t_w * p.n;  // matrix index at the wave's first step
+    const bool yl = active && (cl.kind[0] == Z_M || cl.kind[0] == Z_L);  // vector IO: Y columns
+    const int64_t ystep = yl ? p.n * (int64_t)k * (cl.kind[0] == Z_M ? k : v) : 0;
+    const int yld = yl ? (cl.kind[0] == Z_M ? k : v) : 0;
+    if constexpr (VIO) {
+        int ld0;
+        const TS *src = y_src<TS, CPL>(p.gAbar, p.gBbar, cl, mw, k, v, active, ld0);
 #pragma unroll
-    for (int r = 0; r < L; ++r) load_g<TS, KP, CPL, VIO>(rg[r], p, cl, m0 + (t_w + r) * p.n, active && t_w + r < p.T);
+        for (int r = 0; r < L; ++r) {
+            const bool ok = t_w + r < p.T;
+            const TS *sr = ok ? src : aff_zeros<TS>();
+            const int ldr = ok ? yld : 0;
+#pragma unroll
+            for (int i = 0; i < KP; ++i) ld_g<TS, CPL>(rg[r][i], sr + i * ldr);
+            src += ystep;
+        }
+    } else {
+#pragma unroll
+        for (int r = 0; r < L; ++r) load_g<TS, KP, CPL, VIO>(rg[r], p, cl, m0 + (t_w + r) * p.n, active && t_w + r < p.T);
+    }
     stage_at<TS, KP, VIO>(s_A, p, grp, t_c, CH);
     lds_barrier();
 
@@ -1165,9 +1182,20 @@ __global__ __launch_bounds__(512) void affine_bwd_kernel(BwdArgs p) {
     // loading each in the step that uses it exposes the load latency.
     float rxn[KP][CPL];   // element-wise IO: the next step's columns
     XRaw<TS, KP, CPL> xn;  // vector IO: the next step's loads, still in flight
-    if constexpr (VIO)
-        xprev_issue<TS, KP, CPL>(xn, p, cl, m0 + (t_w + L - 1) * p.n, t_w + L - 1, active && t_w + L - 1 < p.T);
-    else
+    // vector IO: X_{t-1} of step r (t = t_w + r) sits at matrix index t_w + r - 1
+    int ldx0;
+    const TS *xb = y_src<TS, CPL>(p.Abar, p.Bbar, cl, mw, k, v, active, ldx0);
+    auto x_src = [&](int r, int &ldr) -> const TS * {
+        const int64_t tr = t_w + r;
+        const bool ok = yl && tr > 0 && tr < p.T;
+        ldr = ok ? yld : 0;
+        return ok ? xb + (int64_t)(r - 1) * ystep : aff_zeros<TS>();
+    };
+    if constexpr (VIO) {
+        int ldr;
+        const TS *sr = x_src(L - 1, ldr);
+        xprev_issue<TS, KP, CPL>(xn, sr, ldr);
+    } else
         load_xprev<TS, KP, CPL, H0>(rxn, p, cl, m0 + (t_w + L - 1) * p.n, t_w + L - 1,
                                          active && t_w + L - 1 < p.T, gh);
 #pragma unroll
@@ -1176,8 +1204,11 @@ __global__ __launch_bounds__(512) void affine_bwd_kernel(BwdArgs p) {
         float rxr[KP][CPL];
         if constexpr (VIO) {
             xprev_finish<TS, KP, CPL, H0>(rxr, xn, p, cl, t, active && t < p.T, gh);
-            if (r > 0)
-                xprev_issue<TS, KP, CPL>(xn, p, cl, m0 + (t_w + r - 1) * p.n, t_w + r - 1, active && t_w + r - 1 < p.T);
+            if (r > 0) {
+                int ldr;
+                const TS *sr = x_src(r - 1, ldr);
+                xprev_issue<TS, KP, CPL>(xn, sr, ldr);
+            }
         } else {
 #pragma unroll
             for (int i = 0; i < KP; ++i)
@@ -1219,8 +1250,9 @@ __global__ __launch_bounds__(512) void affine_bwd_kernel(BwdArgs p) {
         if (active) {
             if constexpr (VIO) {
                 if (cl.kind[0] == Z_L) {
+                    TS *db = static_cast<TS *>(p.dB) + (mw * k * v + cl.col[0]) + (int64_t)r * ystep;
 #pragma unroll
-                    for (int i = 0; i < KP; ++i) st_g<TS, CPL, true>(static_cast<TS *>(p.dB) + m * k * v + i * v + cl.col[0], S[i]);
+                    for (int i = 0; i < KP; ++i) st_g<TS, CPL, true>(db + i * v, S[i]);
                 }
             } else {
 #pragma unroll
@@ -1249,6 +1281,8 @@ __global__ __launch_bounds__(512) void affine_bwd_kernel(BwdArgs p) {
             // least GMIN lanes, v >= CPL).  The loop over groups is unrolled:
             // with a global store in a loop of run-time length the compiler
             // waits for every load in flight, the next step's X_{t-1} too.
+            TS *const dA_w = static_cast<TS *>(p.dA) + mw * k * k;  // dA at the wave's first step
+            const int64_t dastep = p.n * (int64_t)k * k;
             constexpr int NG = KP * KP / 4;
             constexpr int GMIN = (2 * KP + CPL) / CPL;
             constexpr int MAXIT = (NG + GMIN - 1) / GMIN;
@@ -1271,7 +1305,7 @@ __global__ __launch_bounds__(512) void affine_bwd_kernel(BwdArgs p) {
                             for (int w = 0; w < 4; ++w) acc[u] = fmaf(y[w], x[w], acc[u]);
                         }
                     }
-                    st_g<TS, 4, true>(static_cast<TS *>(p.dA) + m * k * k + (int64_t)i * k + j0, acc);
+                    st_g<TS, 4, true>(dA_w + (int64_t)r * dastep + i * k + j0, acc);
                 }
             }
             // LDS operations of one wave complete in order: the next step's
