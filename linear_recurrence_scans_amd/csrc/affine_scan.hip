@@ -798,8 +798,12 @@ __host__ __device__ constexpr int aff_part_stride(int rbkp) { return rbkp >= 8 ?
 __host__ __device__ constexpr bool aff_da_rows(int KP, bool VIO) { return VIO && KP % 4 == 0; }
 __host__ __device__ constexpr int aff_row_stride(int NCP) { return (NCP / 4) % 2 == 0 ? NCP + 4 : NCP; }
 // Floats of one wave's dA buffer (HPW heads).
+// Floats between two heads' rows: 16 past the 2 KP rows, so that where one
+// pass of a row write covers lanes of two heads (24 lanes a head at k = 8,
+// v = 32) their words fall in opposite halves of the 32 banks.
+__host__ __device__ constexpr int aff_row_head(int KP, int NCP) { return 2 * KP * aff_row_stride(NCP) + 16; }
 __host__ __device__ constexpr int aff_da_wave_floats(int KP, int CPL, bool VIO, int HPW, int G, int NCP) {
-    return aff_da_rows(KP, VIO) ? (HPW * 2 * KP * aff_row_stride(NCP) + 3) / 4 * 4
+    return aff_da_rows(KP, VIO) ? (HPW * aff_row_head(KP, NCP) + 3) / 4 * 4
                                 : (HPW * G * aff_part_stride((KP < MISCAN_AFF_RBMAX ? KP : MISCAN_AFF_RBMAX) * KP) + 3) / 4 * 4;
 }
 
@@ -1172,7 +1176,7 @@ __global__ __launch_bounds__(512) void affine_bwd_kernel(BwdArgs p) {
         // multiple of 4: those columns are never written, so zero them once
         // (the buffer held the look-back's stage until the barrier above)
         if (slot_lane && g == G - 1) {
-            float *hb = part + hsc * 2 * KP * YS;
+            float *hb = part + hsc * aff_row_head(KP, NCP);
             for (int r2 = 0; r2 < 2 * KP; ++r2)
                 for (int c = c0 + CPL; c < NCP; ++c) hb[r2 * YS + c] = 0.f;
         }
@@ -1266,9 +1270,10 @@ __global__ __launch_bounds__(512) void affine_bwd_kernel(BwdArgs p) {
             // dA_t = Y_t X_{t-1}^T as dot products over the k + v Y columns:
             // every lane writes its columns of Y_t and X_{t-1} into the head's
             // rows (no cross-lane sums), then lanes g < KP^2 / 4 of the head
-            // each form four entries of one row of dA_t.  P columns (c < k)
+            // each form a 2 x 2 block of dA_t (two Y rows and two X rows a
+            // column group: four LDS reads for 16 FMA).  P columns (c < k)
             // are written but not read.
-            float *hb = part + hsc * 2 * KP * YS;
+            float *hb = part + hsc * aff_row_head(KP, NCP);
             if (slot_lane) {
 #pragma unroll
                 for (int i = 0; i < KP; ++i) stv<CPL, false>(hb + i * YS + c0, S[i]);
@@ -1290,22 +1295,25 @@ __global__ __launch_bounds__(512) void affine_bwd_kernel(BwdArgs p) {
             for (int it = 0; it < MAXIT; ++it) {
                 const int e = g + it * G;
                 if (active && e < NG) {
-                    const int i = e / (KP / 4), j0 = (e - i * (KP / 4)) * 4;
-                    const float *yr = hb + i * YS;
+                    const int i0 = e / (KP / 2) * 2, j0 = (e - e / (KP / 2) * (KP / 2)) * 2;
+                    const float *yr = hb + i0 * YS;
                     const float *xr = hb + (KP + j0) * YS;
-                    float acc[4] = {0.f, 0.f, 0.f, 0.f};
+                    float acc[2][2] = {{0.f, 0.f}, {0.f, 0.f}};
                     for (int c = k; c < 2 * k + v; c += 4) {
-                        float y[4];
-                        ldv<4>(y, yr + c);
+                        float y[2][4], x[2][4];
 #pragma unroll
-                        for (int u = 0; u < 4; ++u) {
-                            float x[4];
-                            ldv<4>(x, xr + u * YS + c);
+                        for (int u = 0; u < 2; ++u) ldv<4>(y[u], yr + u * YS + c);
 #pragma unroll
-                            for (int w = 0; w < 4; ++w) acc[u] = fmaf(y[w], x[w], acc[u]);
-                        }
+                        for (int u = 0; u < 2; ++u) ldv<4>(x[u], xr + u * YS + c);
+#pragma unroll
+                        for (int a = 0; a < 2; ++a)
+#pragma unroll
+                            for (int b = 0; b < 2; ++b)
+#pragma unroll
+                                for (int w = 0; w < 4; ++w) acc[a][b] = fmaf(y[a][w], x[b][w], acc[a][b]);
                     }
-                    st_g<TS, 4, true>(dA_w + (int64_t)r * dastep + i * k + j0, acc);
+#pragma unroll
+                    for (int a = 0; a < 2; ++a) st_g<TS, 2, true>(dA_w + (int64_t)r * dastep + (i0 + a) * k + j0, acc[a]);
                 }
             }
             // LDS operations of one wave complete in order: the next step's
